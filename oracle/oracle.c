@@ -1,0 +1,366 @@
+/*
+ * CPU oracle for the QAD hot path (NVFP4 simulated quantization + KL loss).
+ * TEST INFRASTRUCTURE ONLY -- see oracle.h for the page legend, the
+ * precision rules and who may use this file.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared (no fast-math).
+ * On x86-64 every `float` operation below is one IEEE binary32 operation
+ * rounded to nearest-even; nothing is fused or reassociated.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float    u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* ------------------------------------------------------------------------
+ * E2M1 ("4-bit floating point", [Nano] section "NVFP4-Format und warum es
+ * wichtig ist?").  The pages name the format but not its grid; the reading
+ * taken is the standard E2M1 layout: 1 sign bit, 2 exponent bits (bias 1),
+ * 1 mantissa bit, exponent 0 subnormal -> magnitudes
+ *     idx : 0    1    2    3    4    5    6    7
+ *     val : 0   0.5   1   1.5   2    3    4    6
+ * Rounding: nearest grid value, ties to the even index, magnitudes beyond 6
+ * saturate to 6.  Written as the midpoints between neighbouring grid values:
+ * at a midpoint the even index wins, so the comparison is "<=" when the lower
+ * neighbour is even and "<" when it is odd.
+ * ---------------------------------------------------------------------- */
+static const float E2M1_VAL[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static unsigned e2m1_index(float a) /* a = |r|, finite */
+{
+    if (a <= 0.25f) return 0; /* midpoint 0|0.5,   lower idx 0 even */
+    if (a <  0.75f) return 1; /* midpoint 0.5|1,   lower idx 1 odd  */
+    if (a <= 1.25f) return 2; /* midpoint 1|1.5,   lower idx 2 even */
+    if (a <  1.75f) return 3; /* midpoint 1.5|2,   lower idx 3 odd  */
+    if (a <= 2.5f)  return 4; /* midpoint 2|3,     lower idx 4 even */
+    if (a <  3.5f)  return 5; /* midpoint 3|4,     lower idx 5 odd  */
+    if (a <= 5.0f)  return 6; /* midpoint 4|6,     lower idx 6 even */
+    return 7;                 /* (5, inf): 6, saturating            */
+}
+
+uint8_t orc_e2m1_encode(float r)
+{
+    unsigned sign = f2u(r) >> 31;   /* signbit: -0 gives a negative code */
+    float a = fabsf(r);
+    if (isnan(a)) a = INFINITY;     /* not expected; saturate deterministically */
+    return (uint8_t)((sign << 3) | e2m1_index(a));
+}
+
+float orc_e2m1_decode(uint8_t code)
+{
+    float v = E2M1_VAL[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+void orc_e2m1_encode_array(const float* r, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_encode(r[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * E4M3 block scale ("E4M3-FP8" per block, [Nano] section "NVFP4-Format und
+ * warum es wichtig ist?").  Reading: the OCP "E4M3FN" encoding -- bias 7,
+ * largest finite 448 (code 0x7E), no infinities, 0x7F is NaN (never
+ * produced), subnormals m * 2^-9.  Encoding rounds to nearest-even and
+ * saturates at 448.  Scales are non-negative, so only the positive half is
+ * encoded.
+ * ---------------------------------------------------------------------- */
+float orc_e4m3_decode(uint8_t code)
+{
+    unsigned e = (code >> 3) & 15, m = code & 7;
+    float v;
+    if ((code & 0x7F) == 0x7F) return NAN;
+    if (e == 0) v = ldexpf((float)m, -9);                 /* m * 2^-9          */
+    else        v = ldexpf(1.0f + (float)m / 8.0f, (int)e - 7);
+    return (code & 0x80) ? -v : v;
+}
+
+uint8_t orc_e4m3_encode(float v)
+{
+    /* v >= 0 and finite */
+    if (!(v > 0.0f)) return 0;                            /* 0 (and -0)        */
+    if (v > 448.0f) return 0x7E;                          /* saturate (also +inf) */
+    if (v >= 0.015625f) {                                 /* normal: v >= 2^-6 */
+        int E;
+        float f = frexpf(v, &E);                          /* v = f * 2^E, f in [0.5,1) */
+        E -= 1;                                           /* v = (2f) * 2^E, 2f in [1,2) */
+        float frac = ldexpf(f, 1) - 1.0f;                 /* exact, in [0,1)   */
+        float m = nearbyintf(frac * 8.0f);                /* RNE, exact scaling */
+        if (m == 8.0f) { m = 0.0f; E += 1; }              /* mantissa carry    */
+        int biased = E + 7;
+        if (biased > 15) return 0x7E;                     /* beyond the format: saturate */
+        unsigned code = ((unsigned)biased << 3) | (unsigned)m;
+        if (code > 0x7E) code = 0x7E;                     /* 480 would be NaN: saturate */
+        return (uint8_t)code;
+    } else {                                              /* subnormal range   */
+        float m = nearbyintf(ldexpf(v, 9));               /* v*2^9 exact, RNE  */
+        return (uint8_t)m;                                /* m == 8 is code 0x08 = 2^-6 */
+    }
+}
+
+void orc_e4m3_encode_array(const float* v, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * bfloat16: top 16 bits of binary32, rounded to nearest-even.
+ * ---------------------------------------------------------------------- */
+uint16_t orc_bf16_from_f32(float f)
+{
+    uint32_t u = f2u(f);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x40);    /* quiet NaN         */
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+float orc_f32_from_bf16(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+void orc_bf16_from_f32_array(const float* f, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_f32(f[i]);
+}
+
+/* element i of an input tensor as binary32 (bf16 -> fp32 is exact) */
+static float load_x(const void* x, int dtype, int64_t i)
+{
+    if (dtype == 1) return orc_f32_from_bf16(((const uint16_t*)x)[i]);
+    return ((const float*)x)[i];
+}
+
+/* ------------------------------------------------------------------------
+ * Tensor amax: the largest magnitude over the whole tensor.  Max calibration
+ * is what the dynamic-scale variant starts from ([Lightning] section
+ * "量化尺度处理策略", dynamic-scale QAD recomputes it every step).
+ * ---------------------------------------------------------------------- */
+float orc_amax(const void* x, int dtype, int64_t n)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(load_x(x, dtype, i));
+        if (a > m || isnan(a)) m = a;
+    }
+    return m;
+}
+
+/* Two-level scaling ([Nano]: FP32 scale per tensor, E4M3 scale per block).
+ * Reading: the tensor scale maps the tensor amax onto the product of the
+ * largest E2M1 value (6) and the largest E4M3 value (448), so that the block
+ * holding the tensor amax gets the largest block scale.  An all-zero tensor
+ * gets tensor scale 1. */
+float orc_tensor_scale(float amax)
+{
+    return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+/* E4M3 block scale of a block with amax amax_b under tensor scale s_g:
+ * the block amax is mapped onto 6 (the top of the E2M1 grid), expressed in
+ * units of the tensor scale, then rounded to E4M3. */
+static uint8_t block_scale_code(float amax_b, float s_g)
+{
+    float per_block = amax_b / 6.0f;
+    float raw = per_block / s_g;
+    return orc_e4m3_encode(raw);
+}
+
+/* Quantize one 16-element block with effective scale s_eff = dec(s_b) * s_g.
+ * code = E2M1(x / s_eff) with the quotient correctly rounded to binary32;
+ * a zero effective scale gives signed-zero codes (no division).  The
+ * dequantized value is the binary32 product dec(code) * s_eff rounded once
+ * more to bf16. */
+static void quantize_block(const float* xb, float s_eff, uint8_t* code16, uint16_t* y16)
+{
+    for (int j = 0; j < 16; ++j) {
+        uint8_t c;
+        if (s_eff == 0.0f) {
+            c = (uint8_t)((f2u(xb[j]) >> 31) << 3);
+        } else {
+            float r = xb[j] / s_eff;
+            c = orc_e2m1_encode(r);
+        }
+        code16[j] = c;
+        float deq = orc_e2m1_decode(c) * s_eff;   /* +-0 stays +-0 */
+        y16[j] = orc_bf16_from_f32(deq);
+    }
+}
+
+void orc_nvfp4_quantize(const void* x, int dtype, int64_t R, int64_t C,
+                        const uint8_t* scales_in, const float* tscale_in,
+                        uint8_t* codes, uint8_t* scales, float* tscale,
+                        uint16_t* y)
+{
+    const int64_t n = R * C, nb = n / 16;
+    float s_g;
+    if (scales_in) {
+        s_g = *tscale_in;                       /* frozen: stored tensor scale */
+    } else {
+        s_g = orc_tensor_scale(orc_amax(x, dtype, n)); /* dynamic: recomputed   */
+    }
+    if (tscale) *tscale = s_g;
+
+    float xb[16];
+    uint8_t c16[16];
+    uint16_t y16[16];
+    for (int64_t b = 0; b < nb; ++b) {
+        float amax_b = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+            xb[j] = load_x(x, dtype, b * 16 + j);
+            float a = fabsf(xb[j]);
+            if (a > amax_b) amax_b = a;
+        }
+        uint8_t sb = scales_in ? scales_in[b] : block_scale_code(amax_b, s_g);
+        float s_eff = orc_e4m3_decode(sb) * s_g;
+        quantize_block(xb, s_eff, c16, y16);
+        if (scales) scales[b] = sb;
+        if (codes)
+            for (int j = 0; j < 16; j += 2)
+                codes[b * 8 + j / 2] = (uint8_t)((c16[j] & 15) | ((c16[j + 1] & 15) << 4));
+        if (y) memcpy(y + b * 16, y16, sizeof y16);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * MSE calibration (frozen-scale variant, [Lightning] section "量化尺度处理策略":
+ * the MSE search is too expensive to redo every step, so its scales are
+ * calibrated once and then kept fixed while only the weights train).
+ * Candidates: block scale amax_b * k / 6 for n values of k spread evenly over
+ * [k_min, k_max] (each k the binary32 value nearest the exact grid point).
+ * Each candidate is rounded to E4M3 like a dynamic scale; its error is the
+ * sum over the block, in element order, of the binary32 squares of
+ * (x - dequantized fp32 value).  The first candidate with strictly smaller
+ * error wins.  The tensor scale is the dynamic one and is frozen with them.
+ * ---------------------------------------------------------------------- */
+void orc_mse_kgrid(int n, float k_min, float k_max, float* k_out)
+{
+    for (int i = 0; i < n; ++i) {
+        if (n == 1) { k_out[i] = k_min; continue; }
+        double num = (double)k_min * (double)(n - 1 - i) + (double)k_max * (double)i;
+        k_out[i] = (float)(num / (double)(n - 1));
+    }
+}
+
+static float block_sq_error(const float* xb, float s_eff)
+{
+    uint8_t c16[16];
+    float err = 0.0f;
+    for (int j = 0; j < 16; ++j) {
+        if (s_eff == 0.0f) c16[j] = 0;
+        else c16[j] = orc_e2m1_encode(xb[j] / s_eff);
+        float deq = orc_e2m1_decode(c16[j]) * s_eff;
+        float d = xb[j] - deq;
+        float sq = d * d;
+        err = err + sq;
+    }
+    return err;
+}
+
+static uint8_t calibrate_one_block(const float* xb, float s_g, int n_cand,
+                                   const float* k, float* best_err,
+                                   uint8_t* cand_codes, float* cand_err)
+{
+    float amax_b = 0.0f;
+    for (int j = 0; j < 16; ++j) { float a = fabsf(xb[j]); if (a > amax_b) amax_b = a; }
+    uint8_t best = 0;
+    float best_e = INFINITY;
+    for (int i = 0; i < n_cand; ++i) {
+        float scaled = amax_b * k[i];
+        uint8_t sb = block_scale_code(scaled, s_g);
+        float s_eff = orc_e4m3_decode(sb) * s_g;
+        float e = block_sq_error(xb, s_eff);
+        if (cand_codes) cand_codes[i] = sb;
+        if (cand_err) cand_err[i] = e;
+        if (e < best_e) { best_e = e; best = sb; }
+    }
+    if (best_err) *best_err = best_e;
+    return best;
+}
+
+void orc_mse_calibrate_blocks(const float* blocks, int64_t nblocks, float s_g,
+                              int n_cand, float k_min, float k_max,
+                              uint8_t* scales, float* err_out,
+                              uint8_t* cand_codes, float* cand_err)
+{
+    float k[4096];
+    if (n_cand > 4096) n_cand = 4096;
+    orc_mse_kgrid(n_cand, k_min, k_max, k);
+    for (int64_t b = 0; b < nblocks; ++b) {
+        float e;
+        uint8_t sb = calibrate_one_block(blocks + b * 16, s_g, n_cand, k, &e,
+                                         cand_codes ? cand_codes + b * n_cand : NULL,
+                                         cand_err ? cand_err + b * n_cand : NULL);
+        if (scales) scales[b] = sb;
+        if (err_out) err_out[b] = e;
+    }
+}
+
+void orc_mse_calibrate(const void* x, int dtype, int64_t R, int64_t C,
+                       int n_cand, float k_min, float k_max,
+                       uint8_t* scales, float* tscale)
+{
+    const int64_t n = R * C, nb = n / 16;
+    float s_g = orc_tensor_scale(orc_amax(x, dtype, n));
+    if (tscale) *tscale = s_g;
+    float k[4096];
+    if (n_cand > 4096) n_cand = 4096;
+    orc_mse_kgrid(n_cand, k_min, k_max, k);
+    float xb[16];
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int j = 0; j < 16; ++j) xb[j] = load_x(x, dtype, b * 16 + j);
+        scales[b] = calibrate_one_block(xb, s_g, n_cand, k, NULL, NULL, NULL);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * KL distillation loss ([Nano] section "Von QAT zu QAD": the student is
+ * trained to minimise the KL divergence to the frozen teacher's output token
+ * distribution; [Qwen] section "3. QAD": the loss compares the two logit
+ * vectors element by element over the vocabulary).
+ * Readings: p = softmax(teacher/T), q = softmax(student/T),
+ *   KL_row = sum_v p_v (log p_v - log q_v)   (forward KL, teacher first),
+ *   loss   = mean over rows,
+ *   dloss/ds_v scaled by grad_scale: (q_v - p_v) * grad_scale / T.
+ * Straight definition in binary64 with the usual max subtraction.
+ * ---------------------------------------------------------------------- */
+static double load_d(const void* p, int dtype, int64_t i)
+{
+    return (double)load_x(p, dtype, i);
+}
+
+double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
+                      int64_t rows, int64_t V, double T, double grad_scale,
+                      double* row_kl, double* grad)
+{
+    double total = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t o = r * V;
+        double mt = -INFINITY, ms = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            double t = load_d(teacher, dtype, o + v) / T;
+            double s = load_d(student, dtype, o + v) / T;
+            if (t > mt) mt = t;
+            if (s > ms) ms = s;
+        }
+        double zt = 0.0, zs = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            zt += exp(load_d(teacher, dtype, o + v) / T - mt);
+            zs += exp(load_d(student, dtype, o + v) / T - ms);
+        }
+        const double lse_t = mt + log(zt), lse_s = ms + log(zs);
+        double kl = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double t = load_d(teacher, dtype, o + v) / T;
+            double s = load_d(student, dtype, o + v) / T;
+            double logp = t - lse_t, logq = s - lse_s;
+            double p = exp(logp);
+            kl += p * (logp - logq);
+            if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
+        }
+        if (row_kl) row_kl[r] = kl;
+        total += kl;
+    }
+    return rows > 0 ? total / (double)rows : 0.0;
+}

@@ -1,0 +1,226 @@
+"""ctypes front-end of the C oracle (test infrastructure only).
+
+Every function takes and returns numpy arrays; bf16 tensors travel as their
+raw uint16 bit patterns.  No arithmetic of the method happens in this file:
+it only builds ``liboracle.so`` from ``oracle.c`` and calls into it.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (strict IEEE binary32/binary64, no fusion)."""
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = C.CDLL(_LIB_PATH)
+        vp, i64, f32, f64, i32 = C.c_void_p, C.c_int64, C.c_float, C.c_double, C.c_int
+        sig = {
+            "orc_e2m1_encode": (C.c_uint8, [f32]),
+            "orc_e2m1_decode": (f32, [C.c_uint8]),
+            "orc_e4m3_encode": (C.c_uint8, [f32]),
+            "orc_e4m3_decode": (f32, [C.c_uint8]),
+            "orc_bf16_from_f32": (C.c_uint16, [f32]),
+            "orc_f32_from_bf16": (f32, [C.c_uint16]),
+            "orc_e2m1_encode_array": (None, [vp, i64, vp]),
+            "orc_e4m3_encode_array": (None, [vp, i64, vp]),
+            "orc_bf16_from_f32_array": (None, [vp, i64, vp]),
+            "orc_amax": (f32, [vp, i32, i64]),
+            "orc_nvfp4_quantize": (None, [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]),
+            "orc_tensor_scale": (f32, [f32]),
+            "orc_mse_kgrid": (None, [i32, f32, f32, vp]),
+            "orc_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
+            "orc_mse_calibrate_blocks": (None, [vp, i64, f32, i32, f32, f32, vp, vp, vp, vp]),
+            "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 or raw-bf16 uint16 arrays, got %s" % x.dtype)
+
+
+# ---- scalar / array codecs ------------------------------------------------
+def e2m1_encode(r: np.ndarray) -> np.ndarray:
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    out = np.empty(r.shape, np.uint8)
+    _load().orc_e2m1_encode_array(_ptr(r), r.size, _ptr(out))
+    return out
+
+
+def e2m1_decode(code: int) -> float:
+    return float(_load().orc_e2m1_decode(int(code)))
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().orc_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().orc_e4m3_decode(int(code)))
+
+
+def e4m3_decode_table() -> np.ndarray:
+    lib = _load()
+    return np.array([lib.orc_e4m3_decode(c) for c in range(256)], np.float32)
+
+
+def bf16_from_f32(f: np.ndarray) -> np.ndarray:
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().orc_bf16_from_f32_array(_ptr(f), f.size, _ptr(out))
+    return out
+
+
+def f32_from_bf16(h: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits to float32 (exact; a bit shift, not arithmetic)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- NVFP4 tensor operations ----------------------------------------------
+def amax(x: np.ndarray) -> float:
+    x = np.ascontiguousarray(x)
+    return float(_load().orc_amax(_ptr(x), _dtype_code(x), x.size))
+
+
+def tensor_scale(a: float) -> float:
+    return float(_load().orc_tensor_scale(float(a)))
+
+
+def nvfp4_quantize(x: np.ndarray, scales_in: np.ndarray | None = None,
+                   tscale_in: float | None = None):
+    """Quantize one tensor [..., C] (C % 16 == 0); leading dims are rows.
+
+    Returns (codes u8[R, C/2], scales u8[R, C/16], tscale float, y bf16-bits
+    u16[R, C]).  Pass scales_in / tscale_in for the frozen variant.
+    """
+    x = np.ascontiguousarray(x)
+    Cc = x.shape[-1]
+    R = x.size // Cc if Cc else 0
+    assert Cc % 16 == 0
+    codes = np.empty((R, Cc // 2), np.uint8)
+    scales = np.empty((R, Cc // 16), np.uint8)
+    ts = np.zeros(1, np.float32)
+    y = np.empty((R, Cc), np.uint16)
+    sin = None
+    tin = None
+    if scales_in is not None:
+        sin = np.ascontiguousarray(scales_in, dtype=np.uint8).reshape(-1)
+        assert sin.size == R * Cc // 16
+        tin = np.array([tscale_in], np.float32)
+    _load().orc_nvfp4_quantize(_ptr(x), _dtype_code(x), R, Cc, _ptr(sin), _ptr(tin),
+                               _ptr(codes), _ptr(scales), _ptr(ts), _ptr(y))
+    return codes, scales, float(ts[0]), y
+
+
+def mse_kgrid(n: int = 64, k_min: float = 0.5, k_max: float = 1.0) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    _load().orc_mse_kgrid(n, k_min, k_max, _ptr(out))
+    return out
+
+
+def mse_calibrate(x: np.ndarray, n_cand: int = 64, k_min: float = 0.5, k_max: float = 1.0):
+    """MSE-calibrate one tensor: returns (E4M3 scales u8[R, C/16], tscale)."""
+    x = np.ascontiguousarray(x)
+    Cc = x.shape[-1]
+    R = x.size // Cc if Cc else 0
+    scales = np.empty((R, Cc // 16), np.uint8)
+    ts = np.zeros(1, np.float32)
+    _load().orc_mse_calibrate(_ptr(x), _dtype_code(x), R, Cc, n_cand, k_min, k_max,
+                              _ptr(scales), _ptr(ts))
+    return scales, float(ts[0])
+
+
+def mse_calibrate_blocks(blocks: np.ndarray, s_g: float, n_cand: int = 64,
+                         k_min: float = 0.5, k_max: float = 1.0, detail: bool = False):
+    """Calibrate independent 16-element fp32 blocks under tensor scale s_g.
+
+    Returns scales u8[nb] and best errors f32[nb]; with detail=True also every
+    candidate's E4M3 code u8[nb, n_cand] and error f32[nb, n_cand].
+    """
+    blocks = np.ascontiguousarray(blocks, dtype=np.float32).reshape(-1, 16)
+    nb = blocks.shape[0]
+    scales = np.empty(nb, np.uint8)
+    err = np.empty(nb, np.float32)
+    cc = np.empty((nb, n_cand), np.uint8) if detail else None
+    ce = np.empty((nb, n_cand), np.float32) if detail else None
+    _load().orc_mse_calibrate_blocks(_ptr(blocks), nb, float(s_g), n_cand, k_min, k_max,
+                                     _ptr(scales), _ptr(err), _ptr(cc), _ptr(ce))
+    if detail:
+        return scales, err, cc, ce
+    return scales, err
+
+
+# ---- KL ---------------------------------------------------------------------
+def kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0,
+               grad_scale: float | None = None, want_grad: bool = True):
+    """Binary64 KL(teacher || student) over the last dim.
+
+    Returns (mean loss, row losses f64[rows], gradient f64[rows, V] or None).
+    grad_scale defaults to 1/rows (gradient of the mean).
+    """
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    assert t.shape == s.shape and t.dtype == s.dtype
+    V = t.shape[-1]
+    rows = t.size // V if V else 0
+    if grad_scale is None:
+        grad_scale = 1.0 / rows if rows else 0.0
+    row = np.empty(rows, np.float64)
+    g = np.empty((rows, V), np.float64) if want_grad else None
+    loss = _load().orc_kl_fwd_bwd(_ptr(t), _ptr(s), _dtype_code(t), rows, V, float(T),
+                                  float(grad_scale), _ptr(row), _ptr(g))
+    return float(loss), row, g
+
+
+__all__ = [
+    "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
+    "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
+    "nvfp4_quantize", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
+]

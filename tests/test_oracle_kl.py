@@ -1,0 +1,107 @@
+"""Pins of the oracle's KL(teacher || student) loss and gradient.
+
+Page 'NVIDIA AI bringt Nemotron-3-Nano-30B auf NVFP4 ...' (chatgpz.de),
+section 'Von QAT zu QAD': training minimises the KL divergence between the
+output token distributions of a frozen BF16 teacher and the NVFP4 student.
+Page 'Model-Optimizer 实战 ... W4A4 NVFP4 精度' (nlpx.cn), section '3. QAD': the
+loss compares the two logit vectors element-wise over the vocabulary.
+
+Pins: torch's float64 kl_div + autograd (an independent library routine),
+closed forms (two-way vocabulary, uniform teacher), KL(p||p) = 0, KL >= 0,
+shift invariance, central finite differences, gradient rows summing to 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_quantization_aware_amd import synth
+
+
+def _grid_logits(rng, rows, V, scale=4.0):
+    # values on a 2^-10 grid: exact in fp32, and exact after +-2^-10 steps
+    return (np.round(rng.normal(0, scale, (rows, V)) * 1024) / 1024).astype(np.float32)
+
+
+def test_zero_for_identical(orc):
+    t, _ = synth.logits_bf16(tokens=4, vocab=1000, seed=5)
+    b = synth.bf16_bits(t)
+    loss, row, g = orc.kl_fwd_bwd(b, b)
+    assert loss == 0.0 and np.all(row == 0.0) and np.all(g == 0.0)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0, 0.5])
+def test_against_torch_float64(orc, T):
+    t, s = synth.logits_bf16(tokens=6, vocab=3000, seed=9)
+    tb, sb = synth.bf16_bits(t), synth.bf16_bits(s)
+    loss, row, g = orc.kl_fwd_bwd(tb, sb, T=T)
+    td = t.double() / T
+    sd = s.double().requires_grad_(True)
+    ref = torch.nn.functional.kl_div(torch.log_softmax(sd / T, -1), torch.log_softmax(td, -1),
+                                     log_target=True, reduction="batchmean")
+    ref.backward()
+    assert abs(loss - ref.item()) <= 1e-12 * abs(ref.item())
+    assert np.allclose(g, sd.grad.numpy(), rtol=1e-9, atol=1e-15)
+    assert np.all(row >= 0)
+
+
+def test_two_way_vocabulary_closed_form(orc):
+    rng = np.random.default_rng(1)
+    x = _grid_logits(rng, 50, 2)
+    y = _grid_logits(rng, 50, 2)
+    _, row, g = orc.kl_fwd_bwd(x, y, grad_scale=1.0)
+    p = 1.0 / (1.0 + np.exp(-(x[:, 1].astype(np.float64) - x[:, 0])))
+    q = 1.0 / (1.0 + np.exp(-(y[:, 1].astype(np.float64) - y[:, 0])))
+    kl = p * np.log(p / q) + (1 - p) * np.log((1 - p) / (1 - q))
+    assert np.allclose(row, kl, rtol=1e-10, atol=1e-14)
+    assert np.allclose(g[:, 1], q - p, rtol=1e-10, atol=1e-15)
+
+
+def test_uniform_teacher_closed_form(orc):
+    rng = np.random.default_rng(2)
+    V = 257
+    t = np.full((3, V), 1.5, np.float32)
+    s = _grid_logits(rng, 3, V)
+    _, row, _ = orc.kl_fwd_bwd(t, s)
+    sd = s.astype(np.float64)
+    logq = sd - (sd.max(1, keepdims=True) + np.log(np.exp(sd - sd.max(1, keepdims=True)).sum(1, keepdims=True)))
+    expect = -math.log(V) - logq.mean(1)
+    assert np.allclose(row, expect, rtol=1e-12)
+
+
+def test_nonnegative_and_shift_invariant(orc):
+    rng = np.random.default_rng(3)
+    t = _grid_logits(rng, 8, 500)
+    s = _grid_logits(rng, 8, 500)
+    l0, r0, g0 = orc.kl_fwd_bwd(t, s)
+    l1, r1, g1 = orc.kl_fwd_bwd(t + np.float32(3.0), s - np.float32(5.0))
+    assert np.all(r0 > 0)
+    assert abs(l0 - l1) <= 1e-12 * l0
+    assert np.allclose(g0, g1, rtol=1e-9, atol=1e-16)
+    assert np.all(np.abs(g0.sum(1)) <= 1e-15)
+
+
+def test_finite_differences(orc):
+    rng = np.random.default_rng(4)
+    t = _grid_logits(rng, 3, 7, 1.0)
+    s = _grid_logits(rng, 3, 7, 1.0)
+    _, _, g = orc.kl_fwd_bwd(t, s)
+    h = np.float32(2.0**-10)
+    for r in range(3):
+        for v in range(7):
+            sp, sm = s.copy(), s.copy()
+            sp[r, v] += h
+            sm[r, v] -= h
+            lp, _, _ = orc.kl_fwd_bwd(t, sp, want_grad=False)
+            lm, _, _ = orc.kl_fwd_bwd(t, sm, want_grad=False)
+            fd = (lp - lm) / (2 * float(h))
+            assert abs(fd - g[r, v]) <= 1e-6 * np.abs(g).max()
+
+
+def test_config_like_magnitude(orc):
+    # teacher N(0,9), student = teacher + N(0,0.25): KL per row is about
+    # Var(delta)/2 = 0.125 nats for small perturbations (second-order expansion)
+    t, s = synth.logits_bf16(tokens=4, vocab=131072, seed=5)
+    loss, row, _ = orc.kl_fwd_bwd(synth.bf16_bits(t), synth.bf16_bits(s), want_grad=False)
+    assert 0.08 < loss < 0.16
