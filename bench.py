@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the QAD hot path on one MI355X.
+
+One step runs every step of the hot path once over synthetic inputs resident
+in HBM, in the launch configuration the parity tests check:
+  moe   : dynamic NVFP4 QDQ forward of 128 expert matrices 2048 x 4096 bf16
+          (N(0,0.02^2), 16 outlier input columns x20 per expert) + the
+          straight-through backward of a bf16 N(0,(1e-3)^2) gradient;
+  act   : W4A4 activation QDQ forward of 32768 x 4096 bf16 (Student-t nu=3,
+          8 outlier channels x30; amax recomputed each call) + STE backward;
+  mse   : MSE calibration of an 8192 x 8192 bf16 N(0,0.02^2) weight (64
+          candidates amax*k/6, k in [0.5, 1]) + QDQ with the frozen scales;
+  kl    : KL(teacher || student) loss (mean, fp32) + bf16 gradient over 8192
+          tokens x 131072 vocabulary, teacher N(0,3^2), student = teacher +
+          N(0,0.5^2), T = 1.
+`value` is the step's algorithmic HBM bytes (every input read once, every
+output written once) divided by the step time.  Per-part times come from HIP
+events recorded on the stream the kernels run on.  The CPU baseline times the
+CPU oracle, single-threaded, on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 QDQ GB/s and KL fwd+bwd tokens/s, % of HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+GiB = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-scale", type=float, default=1.0,
+                    help="multiplies the size of the CPU-baseline sample")
+    return ap.parse_args()
+
+
+def ensure_built():
+    from nvfp4_quantization_aware_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from nvfp4_quantization_aware_amd import build
+        build.build()
+
+
+class Workload:
+    """Inputs, outputs and workspaces of one step, allocated once."""
+
+    def __init__(self, dev):
+        import torch
+        import nvfp4_quantization_aware_amd as q
+        from nvfp4_quantization_aware_amd import synth
+        self.q = q
+        E, R2, C2 = 128, 2048, 4096
+        T3, H3 = 32768, 4096
+        R4 = C4 = 8192
+        N5, V5 = 8192, 131072
+        self.shapes = dict(moe=(E, R2, C2), act=(T3, H3), mse=(R4, C4), kl=(N5, V5))
+        self.w2, self.g2 = synth.moe_weights_bf16(E, R2, C2, seed=2, device=dev)
+        x3, self.g3 = synth.student_t_activations_bf16(T3, H3, seed=3, device=dev)
+        self.x3 = x3.unsqueeze(0)
+        self.w4 = synth.gaussian_weight_bf16(R4, C4, seed=4, device=dev).unsqueeze(0)
+        self.t5, self.s5 = synth.logits_bf16(N5, V5, seed=5, device=dev)
+        bf = torch.bfloat16
+        self.y2 = torch.empty_like(self.w2)
+        self.gx2 = torch.empty_like(self.g2)
+        self.y3 = torch.empty_like(self.x3)
+        self.gx3 = torch.empty_like(self.g3)
+        self.sc4 = torch.empty((1, R4, C4 // 16), dtype=torch.uint8, device=dev)
+        self.ts4 = torch.empty(1, dtype=torch.float32, device=dev)
+        self.y4 = torch.empty_like(self.w4)
+        self.l5 = torch.empty(1, dtype=torch.float32, device=dev)
+        self.gr5 = torch.empty((N5, V5), dtype=bf, device=dev)
+        self.ws2 = q.workspace(q.QAD_OP_QUANTIZE, E, R2, C2, dev)
+        self.ws3 = q.workspace(q.QAD_OP_QUANTIZE, 1, T3, H3, dev)
+        self.ws4 = q.workspace(q.QAD_OP_MSE_CALIBRATE, 1, R4, C4, dev)
+        self.ws5 = q.workspace(q.QAD_OP_KL, 1, N5, V5, dev)
+        n2, n3, n4, n5 = E * R2 * C2, T3 * H3, R4 * C4, N5 * V5
+        # algorithmic bytes: each input read once, each output written once
+        self.bytes = {
+            "moe_qdq_fwd": 2 * n2 + 2 * n2,
+            "moe_ste_bwd": 2 * n2 + 2 * n2,
+            "act_qdq_fwd": 2 * n3 + 2 * n3,
+            "act_ste_bwd": 2 * n3 + 2 * n3,
+            "mse_calibrate": 2 * n4 + n4 // 16,
+            "mse_frozen_qdq": 2 * n4 + n4 // 16 + 2 * n4,
+            "kl_fwd_bwd": 2 * n5 + 2 * n5 + 2 * n5,
+        }
+        self.parts = list(self.bytes)
+
+    def step(self, ev=None):
+        q = self.q
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        q.nvfp4_qdq_fwd(self.w2, y=self.y2, ws=self.ws2)
+        rec(1)
+        q.nvfp4_qdq_bwd(self.g2, self.gx2)
+        rec(2)
+        q.nvfp4_qdq_fwd(self.x3, y=self.y3, ws=self.ws3)
+        rec(3)
+        q.nvfp4_qdq_bwd(self.g3, self.gx3)
+        rec(4)
+        q.nvfp4_mse_calibrate(self.w4, scales_out=self.sc4, tscale_out=self.ts4, ws=self.ws4)
+        rec(5)
+        q.nvfp4_qdq_fwd(self.w4, self.sc4, self.ts4, y=self.y4)
+        rec(6)
+        q.qad_kl_fwd_bwd(self.t5, self.s5, loss_out=self.l5, grad=self.gr5, ws=self.ws5)
+        rec(7)
+
+
+def cpu_baseline(scale: float):
+    """The CPU oracle (single-threaded C) on a bounded sample of each part."""
+    import numpy as np
+    import torch
+    import oracle
+    from nvfp4_quantization_aware_amd import synth
+    oracle.build(force=False)
+    bits = synth.bf16_bits
+    rows2 = max(16, int(2048 * scale))
+    rows3 = max(16, int(512 * scale))
+    rows4 = max(16, int(64 * scale))
+    rows5 = max(2, int(24 * scale))
+    w, g = synth.moe_weights_bf16(1, rows2, 4096, seed=2)
+    x, g3 = synth.student_t_activations_bf16(rows3, 4096, seed=3)
+    w4 = synth.gaussian_weight_bf16(rows4, 8192, seed=4)
+    t5, s5 = synth.logits_bf16(rows5, 131072, seed=5)
+    w, g, x, g3, w4, t5, s5 = (bits(a) for a in (w, g, x, g3, w4, t5, s5))
+    timings = []
+
+    def timed(fn, nbytes):
+        t0 = time.perf_counter()
+        fn()
+        timings.append((time.perf_counter() - t0, nbytes))
+
+    timed(lambda: oracle.nvfp4_quantize(w[0]), 4 * w.size)
+    timed(lambda: np.copy(g), 4 * g.size)
+    timed(lambda: oracle.nvfp4_quantize(x), 4 * x.size)
+    timed(lambda: np.copy(g3), 4 * g3.size)
+
+    def mse_then_frozen():
+        sc, ts = oracle.mse_calibrate(w4)
+        oracle.nvfp4_quantize(w4, sc, ts)
+
+    timed(mse_then_frozen, 2 * w4.size + w4.size // 16 + 2 * w4.size + w4.size // 16 + 2 * w4.size)
+    timed(lambda: oracle.kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
+    secs = sum(t for t, _ in timings)
+    nbytes = sum(b for _, b in timings)
+    return {
+        "value": round(nbytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "seconds": round(secs, 2),
+        "sample": ("one step's parts on a slice: 1 expert x %d x 4096 QDQ + its STE copy; %d x 4096 "
+                   "activation QDQ + STE copy; MSE calibration + frozen QDQ of %d x 8192; KL fwd+bwd "
+                   "of %d x 131072 rows (binary64); same generators and seeds as the GPU workload"
+                   % (rows2, rows3, rows4, rows5)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every part of this hot path runs on a single MI355X "
+              "(per-expert tensors and token rows are independent; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    ensure_built()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    wl = Workload(dev)
+    torch.cuda.synchronize()
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(K):
+        wl.step(evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    part_ms = {}
+    for i, name in enumerate(wl.parts):
+        part_ms[name] = sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)) / K
+    total_bytes = sum(wl.bytes.values())
+    parts = {}
+    for name in wl.parts:
+        gbs = wl.bytes[name] / (part_ms[name] * 1e-3) / 1e9
+        parts[name] = {"ms": round(part_ms[name], 4), "bytes": wl.bytes[name], "GB/s": round(gbs, 1),
+                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(wl.parts, key=lambda n: part_ms[n])
+    dom_gbs = wl.bytes[dom] / (part_ms[dom] * 1e-3) / 1e9
+    kl_tokens_s = wl.shapes["kl"][0] / (part_ms["kl_fwd_bwd"] * 1e-3)
+    qdq_bytes = sum(wl.bytes[n] for n in wl.parts if n != "kl_fwd_bwd")
+    qdq_ms = sum(part_ms[n] for n in wl.parts if n != "kl_fwd_bwd")
+    out = {
+        "metric": METRIC,
+        "value": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "qad_hot_path_step: moe 128x2048x4096 bf16 dynamic QDQ fwd + STE bwd; "
+                        "act 32768x4096 bf16 dynamic QDQ fwd + STE bwd; mse 8192x8192 bf16 "
+                        "64-candidate calibration + frozen QDQ; kl 8192x131072 bf16 fwd+bwd T=1",
+            "storage": "bf16 in/out, e2m1+e4m3 scales, fp32 tensor scales",
+            "bytes_per_step": total_bytes,
+            "parallelism": "single GPU",
+        },
+        "frac_hbm_step": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "nvfp4_qdq_GBps": round(qdq_bytes / (qdq_ms * 1e-3) / 1e9, 1),
+        "kl_tokens_per_s": round(kl_tokens_s, 1),
+        "parts": parts,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_scale)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

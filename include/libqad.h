@@ -1,0 +1,197 @@
+/*
+ * libqad -- the data-parallel hot path of quantization-aware distillation
+ * (QAD) for AMD Instinct MI355X (gfx950): NVFP4 simulated quantization of
+ * weights and activations in the student's forward pass (dynamic or frozen
+ * MSE-calibrated scales) with a straight-through backward, and the
+ * KL(teacher || student) distillation loss with its gradient over the
+ * vocabulary.
+ *
+ * Pages the operations follow (cited by title and section):
+ *  [Nano]      "NVIDIA AI bringt Nemotron-3-Nano-30B auf NVFP4 mit Quantization
+ *              Conscious Distillation (QAD) ..." (chatgpz.de):
+ *              "NVFP4-Format und warum es wichtig ist?" -- 4-bit floating-point
+ *              values in blocks of 16, one E4M3 scale per block, one FP32
+ *              scale per tensor; "Von QAT zu QAD" -- the student minimises the
+ *              KL divergence to a frozen BF16 teacher's token distribution.
+ *  [Lightning] "使用量化感知蒸馏技术构建Nemotron 3.5 Lightning NVFP4模型"
+ *              (163.com): "QAD的工作原理" -- every student forward runs
+ *              simulated quantization; "量化尺度处理策略" -- dynamic scales are
+ *              recomputed each step, frozen scales come from an MSE search
+ *              done once and stay fixed while only the weights train.
+ *  [Qwen]      "Model-Optimizer 实战：用量化感知蒸馏（QAD）恢复 Qwen3.6-35B-A3B 的
+ *              W4A4 NVFP4 精度" (nlpx.cn): "3. QAD" -- the KD loss compares
+ *              teacher and student logits element-wise over the vocabulary;
+ *              dense fp32 [seq, vocab] logits do not fit, so the loss must
+ *              stream the logits.
+ *
+ * Numerics (what the pages leave open is fixed as follows, identically in the
+ * CPU reference the library is tested against):
+ *  - E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}; nearest value, ties to the even
+ *    code index, magnitudes above 6 saturate; the code's sign is the sign bit
+ *    of x (so -0 gives code 0x8).
+ *  - E4M3 is the OCP "E4M3FN" encoding (bias 7, max 448, subnormals), round to
+ *    nearest even, saturating at 448.
+ *  - tensor scale s_g = amax/2688 (2688 = 6 * 448), or 1 for an all-zero
+ *    tensor; block scale s_b = E4M3((amax_b/6)/s_g); effective scale
+ *    s_eff = dec(s_b) * s_g; code = E2M1(x/s_eff) with the quotient correctly
+ *    rounded to binary32 (a zero effective scale gives signed-zero codes);
+ *    dequantized value y = bf16(dec(code) * s_eff).  Every operation is one
+ *    IEEE binary32 operation rounded to nearest even, in that order.
+ *  - Codes are packed two per byte, the even element in the low nibble,
+ *    row-major [R][C/2]; block scales row-major [R][C/16]; blocks run along
+ *    the contiguous last dimension.
+ *  - KL: p = softmax(t/T), q = softmax(s/T), loss = mean over token rows of
+ *    sum_v p_v (log p_v - log q_v) in nats; gradient w.r.t. the student logits
+ *    = (q - p) * grad_scale / T.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  Scratch memory comes from the
+ *    caller's `workspace` (size from qad_workspace_bytes()).
+ *  - All work is enqueued asynchronously on `stream` (0 = the null stream);
+ *    the call returns once it is enqueued.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check returns its status and launches nothing.  A failed launch returns
+ *    QAD_ERR_HIP.  Calls that share a workspace must not overlap in time.
+ *  - Inputs must be finite.  A NaN or infinity makes the tensor amax and the
+ *    tensor scale non-finite (visible in amax_out / tscale_out, or through
+ *    qad_check_finite()); the other outputs are then unspecified.
+ *  - Alignment: tensor pointers 16-byte aligned, packed codes 4-byte aligned;
+ *    scale and scalar pointers have no requirement beyond their type.
+ *  - Results are deterministic: the same inputs give bitwise-equal outputs.
+ *  - Thread-safe: no global mutable state.
+ */
+#ifndef LIBQAD_H
+#define LIBQAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* qad_stream_t; /* the same handle as hipStream_t */
+
+typedef enum {
+    QAD_OK = 0,
+    QAD_ERR_INVALID_ARG = 1, /* null pointer where one is required, bad enum, bad parameter */
+    QAD_ERR_SHAPE = 2,       /* negative size, C not a multiple of 16, size overflow        */
+    QAD_ERR_DTYPE = 3,       /* dtype not supported by this entry point                    */
+    QAD_ERR_ALIGNMENT = 4,   /* pointer not aligned as the conventions above require       */
+    QAD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than qad_workspace_bytes()       */
+    QAD_ERR_NONFINITE = 6,   /* qad_check_finite() found a NaN or infinity                 */
+    QAD_ERR_HIP = 7          /* a HIP launch or copy failed                                */
+} qad_status_t;
+
+typedef enum { QAD_F32 = 0, QAD_BF16 = 1 } qad_dtype_t;
+
+typedef enum {
+    QAD_OP_AMAX = 0,          /* nvfp4_amax                                   */
+    QAD_OP_QUANTIZE = 1,      /* nvfp4_quantize and nvfp4_qdq_fwd             */
+    QAD_OP_MSE_CALIBRATE = 2, /* nvfp4_mse_calibrate                          */
+    QAD_OP_KL = 3             /* qad_kl_fwd_bwd: B = 1, R = tokens, C = vocab */
+} qad_op_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qad_status_string(qad_status_t status);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int qad_abi_version(void);
+
+/* Bytes of workspace entry point `op` needs for B tensors of R x C elements
+ * (for QAD_OP_KL: R token rows of C vocabulary logits).  Always a multiple of
+ * 256; 0 means no workspace is needed.  Returns 0 for invalid sizes too (the
+ * entry point then reports the shape error). */
+size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C);
+
+/* Tensor amax (max calibration, [Lightning] "量化尺度处理策略"): amax_out[b] =
+ * max |x[b]| over each of B contiguous tensors of R x C elements.
+ *   x        : device, dtype xt (QAD_F32 or QAD_BF16), [B][R][C], 16-byte aligned
+ *   amax_out : device float[B] (overwritten; also its own scratch)
+ * C need not be a multiple of 16 here. */
+qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                        float* amax_out, qad_stream_t stream);
+
+/* NVFP4 quantization of B independent tensors [R][C] ([Nano] "NVFP4-Format
+ * und warum es wichtig ist?"; dynamic vs frozen per [Lightning] "量化尺度处理策略").
+ *   x          : device, dtype xt, [B][R][C], C % 16 == 0, 16-byte aligned
+ *   scales_in  : NULL -> dynamic scales (amax, tensor scale and block scales
+ *                computed from x on every call); non-NULL -> frozen scales:
+ *                device u8 [B][R][C/16] E4M3 codes (0x00..0x7E), with
+ *   tscale_in  : device float[B] frozen tensor scales (positive, finite);
+ *                required iff scales_in is non-NULL
+ *   codes      : device u8 [B][R][C/2] packed E2M1 codes, or NULL
+ *   scales_out : device u8 [B][R][C/16] block scales used, or NULL
+ *   tscale_out : device float[B] tensor scales used, or NULL
+ *   y          : device bf16 [B][R][C] dequantized values, or NULL
+ *   workspace  : device scratch of qad_workspace_bytes(QAD_OP_QUANTIZE, ...)
+ * At least one output must be non-NULL.  x must not overlap any output. */
+qad_status_t nvfp4_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                            const uint8_t* scales_in, const float* tscale_in,
+                            uint8_t* codes, uint8_t* scales_out, float* tscale_out, void* y,
+                            void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Simulated quantization forward (quantize + dequantize, "QDQ") as run in
+ * every student forward pass ([Lightning] "QAD的工作原理"): y = the
+ * dequantized bf16 values of nvfp4_quantize, nothing else written. */
+qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                           const uint8_t* scales_in, const float* tscale_in, void* y,
+                           void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Straight-through backward of the QDQ: grad_x = grad_y bit for bit (the
+ * rounding is treated as identity; scales receive no gradient because dynamic
+ * scales are recomputed and frozen ones stay fixed, [Lightning] "量化尺度处理策略").
+ *   grad_y, grad_x : device, n elements of dtype gt, 16-byte aligned;
+ *   grad_x == grad_y is allowed (nothing is launched); partial overlap is not. */
+qad_status_t nvfp4_qdq_bwd(const void* grad_y, void* grad_x, qad_dtype_t gt, int64_t n,
+                           qad_stream_t stream);
+
+/* MSE calibration of the frozen block scales ([Lightning] "量化尺度处理策略":
+ * the MSE scale search runs once, before training, because it is too costly
+ * per step).  For each block the candidates are amax_b * k_i / 6 with k_i the
+ * binary32 value nearest to k_min + (k_max - k_min) * i / (n - 1),
+ * i = 0..n-1, each rounded to E4M3 like a dynamic scale; the error of a
+ * candidate is sum_j (x_j - dequantized_j)^2 over the block in element order
+ * (binary32, values before the bf16 rounding); the first candidate with
+ * strictly smaller error wins.  The tensor scale is the dynamic one.
+ *   w          : device, dtype wt, [B][R][C], C % 16 == 0, 16-byte aligned
+ *   n_candidates >= 1, 0 < k_min <= k_max, and when n > 1
+ *                (k_max - k_min) / (n - 1) <= k_min / 16 (consecutive
+ *                candidates then never skip an E4M3 value, which the search
+ *                relies on; the 64-candidate grid over [0.5, 1] qualifies)
+ *   scales_out : device u8 [B][R][C/16]
+ *   tscale_out : device float[B]
+ * Feed scales_out / tscale_out to nvfp4_quantize / nvfp4_qdq_fwd as the
+ * frozen scales. */
+qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64_t R, int64_t C,
+                                 int32_t n_candidates, float k_min, float k_max,
+                                 uint8_t* scales_out, float* tscale_out,
+                                 void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Fused KL(teacher || student) forward + backward over the full vocabulary
+ * ([Nano] "Von QAT zu QAD"; [Qwen] "3. QAD").
+ *   teacher, student : device, dtype lt, [tokens][vocab] row-major, 16-byte
+ *                      aligned, vocab % 8 == 0
+ *   temperature      : T > 0 (finite)
+ *   grad_scale       : multiplies the gradient (1/tokens for the mean loss)
+ *   loss_out         : device float[1]: mean over rows of the per-row KL (nats)
+ *   row_loss         : device float[tokens] per-row KL, or NULL
+ *   grad_student     : device [tokens][vocab] of dtype gt (QAD_BF16, or
+ *                      QAD_F32 for full-precision gradients), or NULL for
+ *                      the forward only; must not overlap the inputs
+ *   workspace        : qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab) */
+qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt,
+                            int64_t tokens, int64_t vocab, float temperature, float grad_scale,
+                            float* loss_out, float* row_loss, void* grad_student, qad_dtype_t gt,
+                            void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Synchronises `stream`, copies n floats from device memory `values` (an
+ * amax_out or tscale_out array) and returns QAD_ERR_NONFINITE if any is a NaN
+ * or an infinity, QAD_OK otherwise.  The only blocking call of the library. */
+qad_status_t qad_check_finite(const float* values, int64_t n, qad_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBQAD_H */

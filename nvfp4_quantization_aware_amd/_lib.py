@@ -1,0 +1,212 @@
+"""Thin ctypes binding of libqad (include/libqad.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library.  PyTorch supplies device memory (outputs and workspace are allocated
+here with torch when the caller does not pass them) and the current stream.
+If libqad.so has not been built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libqad.so")
+
+QAD_F32, QAD_BF16 = 0, 1
+QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL = 0, 1, 2, 3
+STATUS = {0: "QAD_OK", 1: "QAD_ERR_INVALID_ARG", 2: "QAD_ERR_SHAPE", 3: "QAD_ERR_DTYPE",
+          4: "QAD_ERR_ALIGNMENT", 5: "QAD_ERR_WORKSPACE", 6: "QAD_ERR_NONFINITE", 7: "QAD_ERR_HIP"}
+
+# every symbol include/libqad.h declares, with its ctypes signature
+_vp, _i64, _f32, _i32, _sz, _int = C.c_void_p, C.c_int64, C.c_float, C.c_int32, C.c_size_t, C.c_int
+SIGNATURES = {
+    "qad_status_string": (C.c_char_p, [_int]),
+    "qad_abi_version": (_int, []),
+    "qad_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
+    "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_qdq_fwd": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
+    "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qad_check_finite": (_int, [_vp, _i64, _vp]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class QadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, STATUS.get(status, status)))
+
+
+def lib() -> C.CDLL:
+    """The loaded libqad (raises if it was never built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libqad.so is not built (%s); run `python -m "
+                                   "nvfp4_quantization_aware_amd.build`" % LIB_PATH)
+            h = C.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+        return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QadError(status, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return QAD_F32
+    if t.dtype == torch.bfloat16:
+        return QAD_BF16
+    raise TypeError("libqad takes float32 or bfloat16 tensors, got %s" % t.dtype)
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _brc(x: torch.Tensor):
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1]
+    if x.dim() == 3:
+        return x.shape[0], x.shape[1], x.shape[2]
+    raise ValueError("expected [R, C] or [B, R, C], got shape %s" % (tuple(x.shape),))
+
+
+def qad_workspace_bytes(op: int, B: int, R: int, C_: int) -> int:
+    return int(lib().qad_workspace_bytes(op, B, R, C_))
+
+
+def workspace(op: int, B: int, R: int, C_: int, device) -> torch.Tensor | None:
+    n = qad_workspace_bytes(op, B, R, C_)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def nvfp4_amax(x: torch.Tensor, amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    B, R, Cc = _brc(x)
+    if amax_out is None:
+        amax_out = torch.empty(B, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_amax(_p(x), _dt(x), B, R, Cc, _p(amax_out), _stream(x.device)), "nvfp4_amax")
+    return amax_out
+
+
+def nvfp4_quantize(x: torch.Tensor, scales_in=None, tscale_in=None, codes=True, scales_out=True,
+                   tscale_out=True, y=True, ws: torch.Tensor | None = None):
+    """Returns (codes u8[B,R,C/2], scales u8[B,R,C/16], tscale f32[B], y bf16[B,R,C]).
+
+    Pass a tensor to write into it, True to have it allocated, None/False to
+    skip that output.
+    """
+    B, R, Cc = _brc(x)
+    dev = x.device
+
+    def out(arg, shape, dtype):
+        if arg is True:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        return arg if isinstance(arg, torch.Tensor) else None
+
+    codes = out(codes, (B, R, Cc // 2), torch.uint8)
+    scales_out = out(scales_out, (B, R, Cc // 16), torch.uint8)
+    tscale_out = out(tscale_out, (B,), torch.float32)
+    y = out(y, (B, R, Cc), torch.bfloat16)
+    if ws is None and scales_in is None:
+        ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, dev)
+    _check(lib().nvfp4_quantize(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
+                                _p(scales_out), _p(tscale_out), _p(y), _p(ws),
+                                0 if ws is None else ws.numel(), _stream(dev)), "nvfp4_quantize")
+    return codes, scales_out, tscale_out, y
+
+
+def nvfp4_qdq_fwd(x: torch.Tensor, scales_in=None, tscale_in=None, y: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None) -> torch.Tensor:
+    B, R, Cc = _brc(x)
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    if ws is None and scales_in is None:
+        ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, x.device)
+    _check(lib().nvfp4_qdq_fwd(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(y), _p(ws),
+                               0 if ws is None else ws.numel(), _stream(x.device)), "nvfp4_qdq_fwd")
+    return y
+
+
+def nvfp4_qdq_bwd(grad_y: torch.Tensor, grad_x: torch.Tensor | None = None) -> torch.Tensor:
+    if not grad_y.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if grad_x is None:
+        grad_x = torch.empty_like(grad_y)
+    _check(lib().nvfp4_qdq_bwd(_p(grad_y), _p(grad_x), _dt(grad_y), grad_y.numel(),
+                               _stream(grad_y.device)), "nvfp4_qdq_bwd")
+    return grad_x
+
+
+def nvfp4_mse_calibrate(w: torch.Tensor, n_candidates: int = 64, k_min: float = 0.5, k_max: float = 1.0,
+                        scales_out: torch.Tensor | None = None, tscale_out: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None):
+    B, R, Cc = _brc(w)
+    dev = w.device
+    if scales_out is None:
+        scales_out = torch.empty((B, R, Cc // 16), dtype=torch.uint8, device=dev)
+    if tscale_out is None:
+        tscale_out = torch.empty(B, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(QAD_OP_MSE_CALIBRATE, B, R, Cc, dev)
+    _check(lib().nvfp4_mse_calibrate(_p(w), _dt(w), B, R, Cc, n_candidates, k_min, k_max, _p(scales_out),
+                                     _p(tscale_out), _p(ws), 0 if ws is None else ws.numel(),
+                                     _stream(dev)), "nvfp4_mse_calibrate")
+    return scales_out, tscale_out
+
+
+def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: float = 1.0,
+                   grad_scale: float | None = None, grad_dtype=torch.bfloat16, row_loss=False,
+                   loss_out: torch.Tensor | None = None, grad: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None):
+    """Returns (loss f32[1], row_loss f32[tokens] or None, grad or None)."""
+    if teacher.shape != student.shape or teacher.dim() != 2:
+        raise ValueError("teacher and student must both be [tokens, vocab]")
+    tokens, vocab = teacher.shape
+    dev = teacher.device
+    if grad_scale is None:
+        grad_scale = 1.0 / tokens if tokens else 0.0
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
+        row_loss if isinstance(row_loss, torch.Tensor) else None)
+    if grad is None and grad_dtype is not None:
+        grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
+    gt = _dt(grad) if grad is not None else QAD_BF16
+    if ws is None and rows is None:
+        ws = workspace(QAD_OP_KL, 1, tokens, vocab, dev)
+    _check(lib().qad_kl_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, temperature,
+                                grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
+                                0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_fwd_bwd")
+    return loss_out, rows, grad
+
+
+def qad_check_finite(values: torch.Tensor) -> bool:
+    """True if every value is finite (synchronises the current stream)."""
+    st = lib().qad_check_finite(_p(values), values.numel(), _stream(values.device))
+    if st == 6:
+        return False
+    _check(st, "qad_check_finite")
+    return True

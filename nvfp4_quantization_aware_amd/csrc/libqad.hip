@@ -1,0 +1,261 @@
+// C-ABI entry points of libqad: argument validation, workspace layout and
+// launch sequencing.  Declarations, ownership and error rules:
+// include/libqad.h.  Nothing here allocates device memory or keeps state.
+#include "libqad.h"
+
+#include <math.h>
+
+#include "qad_internal.h"
+
+using qad::QuantizeArgs;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 46; // keeps every byte offset far from int64 overflow
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline int esize(qad_dtype_t t) { return t == QAD_BF16 ? 2 : 4; }
+inline bool valid_dtype(qad_dtype_t t) { return t == QAD_F32 || t == QAD_BF16; }
+inline hipStream_t hs(qad_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// B, R, C non-negative and B*R*C bounded; returns the element count or -1
+int64_t tensor_elems(int64_t B, int64_t R, int64_t C)
+{
+    if (B < 0 || R < 0 || C < 0) return -1;
+    if (B == 0 || R == 0 || C == 0) return 0;
+    if (R > kMaxElems / C) return -1;
+    const int64_t rc = R * C;
+    if (B > kMaxElems / rc) return -1;
+    return B * rc;
+}
+
+qad_status_t hip_status(hipError_t e) { return e == hipSuccess ? QAD_OK : QAD_ERR_HIP; }
+
+// the amax words live at the start of the workspace
+uint32_t* ws_amax(void* workspace) { return static_cast<uint32_t*>(workspace); }
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                           const uint8_t* scales_in, const float* tscale_in, uint8_t* codes,
+                           uint8_t* scales_out, float* tscale_out, void* y, void* workspace,
+                           size_t ws_bytes, qad_stream_t stream)
+{
+    if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(B, R, C);
+    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (!codes && !scales_out && !tscale_out && !y) return QAD_ERR_INVALID_ARG;
+    if ((scales_in == nullptr) != (tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
+    if (n == 0) return QAD_OK;
+    if (!x) return QAD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (y && !aligned(y, 16)) || (codes && !aligned(codes, 4)) ||
+        (tscale_in && !aligned(tscale_in, 4)) || (tscale_out && !aligned(tscale_out, 4)))
+        return QAD_ERR_ALIGNMENT;
+    const size_t xbytes = (size_t)n * esize(xt);
+    if ((y && ranges_overlap(x, xbytes, y, (size_t)n * 2)) || (codes && ranges_overlap(x, xbytes, codes, (size_t)n / 2)) ||
+        (scales_out && ranges_overlap(x, xbytes, scales_out, (size_t)n / 16)))
+        return QAD_ERR_INVALID_ARG;
+    const bool frozen = scales_in != nullptr;
+    if (!frozen) {
+        if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C)) return QAD_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
+    }
+    hipStream_t s = hs(stream);
+    QuantizeArgs a;
+    a.x = x;
+    a.bf16 = xt == QAD_BF16;
+    a.B = B;
+    a.elems = R * C;
+    a.scales_in = scales_in;
+    a.tscale_in = tscale_in;
+    a.amax_bits = frozen ? nullptr : ws_amax(workspace);
+    a.codes = codes;
+    a.scales_out = scales_out;
+    a.tscale_out = tscale_out;
+    a.y = static_cast<uint16_t*>(y);
+    if (!frozen) {
+        hipError_t e = qad::launch_fill_u32(ws_amax(workspace), B, 0u, s);
+        if (e == hipSuccess) e = qad::launch_amax(x, a.bf16, B, a.elems, ws_amax(workspace), s);
+        if (e != hipSuccess) return QAD_ERR_HIP;
+    }
+    return hip_status(qad::launch_quantize(a, s));
+}
+
+} // namespace
+
+extern "C" {
+
+const char* qad_status_string(qad_status_t status)
+{
+    switch (status) {
+    case QAD_OK: return "QAD_OK";
+    case QAD_ERR_INVALID_ARG: return "QAD_ERR_INVALID_ARG: invalid argument";
+    case QAD_ERR_SHAPE: return "QAD_ERR_SHAPE: invalid shape";
+    case QAD_ERR_DTYPE: return "QAD_ERR_DTYPE: unsupported dtype";
+    case QAD_ERR_ALIGNMENT: return "QAD_ERR_ALIGNMENT: misaligned pointer";
+    case QAD_ERR_WORKSPACE: return "QAD_ERR_WORKSPACE: workspace missing or too small";
+    case QAD_ERR_NONFINITE: return "QAD_ERR_NONFINITE: non-finite value";
+    case QAD_ERR_HIP: return "QAD_ERR_HIP: HIP runtime error";
+    }
+    return "unknown qad_status_t";
+}
+
+int qad_abi_version(void) { return 1; }
+
+size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
+{
+    if (tensor_elems(B, R, C) < 0) return 0;
+    switch (op) {
+    case QAD_OP_AMAX: return 0;
+    case QAD_OP_QUANTIZE:
+    case QAD_OP_MSE_CALIBRATE: return round256((size_t)B * 4);
+    case QAD_OP_KL: return round256((size_t)R * 4);
+    }
+    return 0;
+}
+
+qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C, float* amax_out,
+                        qad_stream_t stream)
+{
+    if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(B, R, C);
+    if (n < 0 || (C * esize(xt)) % 16 != 0) return QAD_ERR_SHAPE;
+    if (B == 0) return QAD_OK;
+    if (!amax_out) return QAD_ERR_INVALID_ARG;
+    if (n > 0 && !x) return QAD_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(amax_out, 4)) return QAD_ERR_ALIGNMENT;
+    hipStream_t s = hs(stream);
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax_out);
+    hipError_t e = qad::launch_fill_u32(bits, B, 0u, s);
+    if (e == hipSuccess && n > 0) e = qad::launch_amax(x, xt == QAD_BF16, B, R * C, bits, s);
+    return hip_status(e);
+}
+
+qad_status_t nvfp4_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                            const uint8_t* scales_in, const float* tscale_in, uint8_t* codes,
+                            uint8_t* scales_out, float* tscale_out, void* y, void* workspace, size_t ws_bytes,
+                            qad_stream_t stream)
+{
+    return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, codes, scales_out, tscale_out, y, workspace,
+                         ws_bytes, stream);
+}
+
+qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                           const uint8_t* scales_in, const float* tscale_in, void* y, void* workspace,
+                           size_t ws_bytes, qad_stream_t stream)
+{
+    if (!y) return QAD_ERR_INVALID_ARG;
+    return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, nullptr, nullptr, nullptr, y, workspace, ws_bytes,
+                         stream);
+}
+
+qad_status_t nvfp4_qdq_bwd(const void* grad_y, void* grad_x, qad_dtype_t gt, int64_t n, qad_stream_t stream)
+{
+    if (!valid_dtype(gt)) return QAD_ERR_DTYPE;
+    if (n < 0 || n > kMaxElems) return QAD_ERR_SHAPE;
+    if (n == 0 || grad_x == grad_y) return QAD_OK;
+    if (!grad_y || !grad_x) return QAD_ERR_INVALID_ARG;
+    if (!aligned(grad_y, 16) || !aligned(grad_x, 16)) return QAD_ERR_ALIGNMENT;
+    const size_t bytes = (size_t)n * esize(gt);
+    if (ranges_overlap(grad_y, bytes, grad_x, bytes)) return QAD_ERR_INVALID_ARG;
+    return hip_status(qad::launch_copy(grad_y, grad_x, (int64_t)bytes, hs(stream)));
+}
+
+qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64_t R, int64_t C,
+                                 int32_t n_candidates, float k_min, float k_max, uint8_t* scales_out,
+                                 float* tscale_out, void* workspace, size_t ws_bytes, qad_stream_t stream)
+{
+    if (!valid_dtype(wt)) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(B, R, C);
+    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (n_candidates < 1 || !(k_min > 0.0f) || !(k_max >= k_min) || !isfinite(k_max)) return QAD_ERR_INVALID_ARG;
+    // consecutive candidates must not be able to skip an E4M3 value (relative
+    // step at most 1/16, below the narrowest E4M3 rounding interval, 1/15)
+    if (n_candidates > 1 && ((double)k_max - (double)k_min) / (double)(n_candidates - 1) > (double)k_min / 16.0)
+        return QAD_ERR_INVALID_ARG;
+    if (n == 0) return QAD_OK;
+    if (!w || !scales_out || !tscale_out) return QAD_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(tscale_out, 4)) return QAD_ERR_ALIGNMENT;
+    if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_MSE_CALIBRATE, B, R, C)) return QAD_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
+    hipStream_t s = hs(stream);
+    qad::MseArgs a;
+    a.w = w;
+    a.bf16 = wt == QAD_BF16;
+    a.B = B;
+    a.elems = R * C;
+    a.k_lo = k_min;
+    a.k_hi = n_candidates > 1 ? k_max : k_min;
+    a.amax_bits = ws_amax(workspace);
+    a.scales_out = scales_out;
+    a.tscale_out = tscale_out;
+    hipError_t e = qad::launch_fill_u32(ws_amax(workspace), B, 0u, s);
+    if (e == hipSuccess) e = qad::launch_amax(w, a.bf16, B, a.elems, ws_amax(workspace), s);
+    if (e == hipSuccess) e = qad::launch_mse_calibrate(a, s);
+    return hip_status(e);
+}
+
+qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt, int64_t tokens,
+                            int64_t vocab, float temperature, float grad_scale, float* loss_out,
+                            float* row_loss, void* grad_student, qad_dtype_t gt, void* workspace,
+                            size_t ws_bytes, qad_stream_t stream)
+{
+    if (!valid_dtype(lt) || (grad_student && !valid_dtype(gt))) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(1, tokens, vocab);
+    if (n < 0 || vocab % 8 != 0 || tokens > 0x7FFFFFFFll) return QAD_ERR_SHAPE;
+    if (!(temperature > 0.0f) || !isfinite(temperature) || !isfinite(grad_scale)) return QAD_ERR_INVALID_ARG;
+    if (!loss_out) return QAD_ERR_INVALID_ARG;
+    if (tokens > 0 && vocab == 0) return QAD_ERR_SHAPE;
+    if (n > 0 && (!teacher || !student)) return QAD_ERR_INVALID_ARG;
+    if (!aligned(teacher, 16) || !aligned(student, 16) || (grad_student && !aligned(grad_student, 16)) ||
+        !aligned(loss_out, 4) || (row_loss && !aligned(row_loss, 4)))
+        return QAD_ERR_ALIGNMENT;
+    if (grad_student) {
+        const size_t ib = (size_t)n * esize(lt), gb = (size_t)n * esize(gt);
+        if (ranges_overlap(teacher, ib, grad_student, gb) || ranges_overlap(student, ib, grad_student, gb))
+            return QAD_ERR_INVALID_ARG;
+    }
+    float* rows = row_loss;
+    if (!rows && tokens > 0) {
+        if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab)) return QAD_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
+        rows = static_cast<float*>(workspace);
+    }
+    qad::KlArgs a;
+    a.teacher = teacher;
+    a.student = student;
+    a.bf16_in = lt == QAD_BF16;
+    a.tokens = tokens;
+    a.vocab = vocab;
+    a.temperature = temperature;
+    a.grad_scale = grad_scale;
+    a.row_loss = rows;
+    a.loss_out = loss_out;
+    a.grad = grad_student;
+    a.grad_bf16 = gt == QAD_BF16;
+    return hip_status(qad::launch_kl(a, hs(stream)));
+}
+
+qad_status_t qad_check_finite(const float* values, int64_t n, qad_stream_t stream)
+{
+    if (n < 0) return QAD_ERR_SHAPE;
+    if (n == 0) return QAD_OK;
+    if (!values) return QAD_ERR_INVALID_ARG;
+    if (hipStreamSynchronize(hs(stream)) != hipSuccess) return QAD_ERR_HIP;
+    float buf[256];
+    for (int64_t off = 0; off < n; off += 256) {
+        const int64_t k = n - off < 256 ? n - off : 256;
+        if (hipMemcpy(buf, values + off, (size_t)k * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+            return QAD_ERR_HIP;
+        for (int64_t i = 0; i < k; ++i)
+            if (!isfinite(buf[i])) return QAD_ERR_NONFINITE;
+    }
+    return QAD_OK;
+}
+
+} // extern "C"

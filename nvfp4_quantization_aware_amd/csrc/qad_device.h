@@ -1,0 +1,109 @@
+// Device-side building blocks of libqad for gfx950: the E4M3 / E2M1 codecs
+// written as bit manipulation on binary32 patterns, the shared-divisor
+// correctly rounded division, and wave-level helpers.  Page legend and the
+// numerical conventions are in include/libqad.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qad {
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// bf16 halves of a 32-bit word -> binary32 (exact widening)
+__device__ __forceinline__ float bf_lo(uint32_t w) { return as_f(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
+
+// Two binary32 values -> two bf16 (round to nearest even) packed in a word,
+// `lo` in bits 0..15.  Lowers to one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP E4M3FN) block scale, [Nano] "NVFP4-Format und warum es wichtig
+// ist?".  Encode a non-negative binary32 value with round-to-nearest-even and
+// saturation at 448 (code 0x7E).  Normal range: round the 23-bit mantissa to 3
+// bits in the integer domain (a carry into the exponent is the correct
+// result), then rebias 127 -> 7.  Below 2^-6: the value is m * 2^-9, so m is
+// v * 512 (exact) rounded to nearest even; m == 8 is code 0x08 = 2^-6.
+// The result is always a code in 0..0x7E (a NaN saturates, a negative value
+// gives 0), so it can index a 128-entry table whatever the input.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float v)
+{
+    if (!(v <= 448.0f)) return 0x7Eu;
+    if (!(v >= 0.015625f)) return (uint32_t)__builtin_rintf(__builtin_fmaxf(v, 0.0f) * 512.0f);
+    const uint32_t u = as_u(v);
+    const uint32_t t = u + 0x7FFFFu + ((u >> 20) & 1u);
+    return (t >> 20) - (120u << 3);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    return e ? as_f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 magnitude index of a quotient q (4-bit float, [Nano] "NVFP4-Format und
+// warum es wichtig ist?"; grid {0,.5,1,1.5,2,3,4,6}, nearest, ties to the
+// even index, saturating).  |q| < 1: the grid step is 0.5, so the index is
+// 2|q| rounded to nearest even.  |q| >= 1: the grid is binary32 with one
+// mantissa bit, so round the mantissa to 1 bit in the integer domain; the
+// index is then (biased exponent * 2 + mantissa bit) - 252, capped at 7
+// (which also maps infinities and NaNs to 7).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_index(float q)
+{
+    const float a = __builtin_fabsf(q);
+    const uint32_t u = as_u(a);
+    const uint32_t t = u + 0x1FFFFFu + ((u >> 22) & 1u);
+    const uint32_t hi = (t >> 22) - 252u;
+    const uint32_t lo = (uint32_t)__builtin_rintf(a + a);
+    return a < 1.0f ? lo : (hi < 7u ? hi : 7u);
+}
+
+// magnitude of grid index i (0..7)
+__device__ __forceinline__ float e2m1_value(uint32_t i)
+{
+    return i < 2u ? (float)i * 0.5f : as_f((((i >> 1) + 126u) << 23) | ((i & 1u) << 22));
+}
+
+// ---------------------------------------------------------------------------
+// x / s correctly rounded, with r = RN(1/s) precomputed once per divisor:
+// q0 = RN(x r) is within two ulps; one correction q1 = q0 + RN(x - s q0) r is
+// faithful; a second correction is then the correctly rounded quotient
+// (Markstein's theorem).  Valid while nothing under- or overflows; callers
+// use it only for s >= 2^-89 and need the exact value only where a code can
+// depend on it.  r = 0 for s = 0 yields 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_rcp(float x, float s, float r)
+{
+    const float q0 = x * r;
+    const float e0 = __builtin_fmaf(-s, q0, x);
+    const float q1 = __builtin_fmaf(e0, r, q0);
+    const float e1 = __builtin_fmaf(-s, q1, x);
+    return __builtin_fmaf(e1, r, q1);
+}
+
+// swap with the neighbouring lane (lane ^ 1) through DPP quad_perm(1,0,3,2)
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// maximum over a wave of 64 lanes
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) v = umax(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+} // namespace qad

@@ -188,20 +188,12 @@ static void quantize_block(const float* xb, float s_eff, uint8_t* code16, uint16
     }
 }
 
-void orc_nvfp4_quantize(const void* x, int dtype, int64_t R, int64_t C,
-                        const uint8_t* scales_in, const float* tscale_in,
-                        uint8_t* codes, uint8_t* scales, float* tscale,
-                        uint16_t* y)
+/* Quantize nb consecutive blocks under tensor scale s_g; block scales are
+ * computed from each block (dynamic) unless scales_in supplies them (frozen). */
+static void quantize_blocks(const void* x, int dtype, int64_t nb, float s_g,
+                            const uint8_t* scales_in, uint8_t* codes, uint8_t* scales,
+                            uint16_t* y)
 {
-    const int64_t n = R * C, nb = n / 16;
-    float s_g;
-    if (scales_in) {
-        s_g = *tscale_in;                       /* frozen: stored tensor scale */
-    } else {
-        s_g = orc_tensor_scale(orc_amax(x, dtype, n)); /* dynamic: recomputed   */
-    }
-    if (tscale) *tscale = s_g;
-
     float xb[16];
     uint8_t c16[16];
     uint16_t y16[16];
@@ -221,6 +213,29 @@ void orc_nvfp4_quantize(const void* x, int dtype, int64_t R, int64_t C,
                 codes[b * 8 + j / 2] = (uint8_t)((c16[j] & 15) | ((c16[j + 1] & 15) << 4));
         if (y) memcpy(y + b * 16, y16, sizeof y16);
     }
+}
+
+void orc_nvfp4_quantize(const void* x, int dtype, int64_t R, int64_t C,
+                        const uint8_t* scales_in, const float* tscale_in,
+                        uint8_t* codes, uint8_t* scales, float* tscale,
+                        uint16_t* y)
+{
+    const int64_t n = R * C;
+    float s_g;
+    if (scales_in) {
+        s_g = *tscale_in;                              /* frozen: stored tensor scale */
+    } else {
+        s_g = orc_tensor_scale(orc_amax(x, dtype, n)); /* dynamic: recomputed         */
+    }
+    if (tscale) *tscale = s_g;
+    quantize_blocks(x, dtype, n / 16, s_g, scales_in, codes, scales, y);
+}
+
+void orc_nvfp4_quantize_blocks(const void* x, int dtype, int64_t nblocks, float s_g,
+                               const uint8_t* scales_in, uint8_t* codes, uint8_t* scales,
+                               uint16_t* y)
+{
+    quantize_blocks(x, dtype, nblocks, s_g, scales_in, codes, scales, y);
 }
 
 /* ------------------------------------------------------------------------

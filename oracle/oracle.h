@@ -22,8 +22,8 @@
  * scale per tensor, 4-bit floating-point values), the two scale policies
  * (dynamic / frozen MSE-calibrated) and the loss (KL divergence to a frozen
  * teacher over the vocabulary).  Everything they leave open (grid, scale
- * formulas, rounding, layouts, KL direction/reduction) follows the readings
- * listed in the design notes; each function below names the reading it takes.
+ * formulas, rounding, layouts, KL direction/reduction) is fixed by the reading
+ * stated next to the code that takes it, in oracle.c.
  *
  * Precision: the quantizer is defined in IEEE binary32 with round-to-nearest-
  * even for every operation (the tensor scale is FP32 per [Nano]); the KL loss
@@ -66,6 +66,14 @@ void orc_nvfp4_quantize(const void* x, int dtype, int64_t R, int64_t C,
                         const uint8_t* scales_in, const float* tscale_in,
                         uint8_t* codes, uint8_t* scales, float* tscale,
                         uint16_t* y);
+
+/* The blocks of a tensor are independent once its tensor scale s_g is known:
+ * quantize nblocks consecutive 16-element blocks of x under s_g (dynamic block
+ * scales, or frozen ones from scales_in).  Used to check samples of tensors
+ * too large to quantize whole on the CPU. */
+void orc_nvfp4_quantize_blocks(const void* x, int dtype, int64_t nblocks, float s_g,
+                               const uint8_t* scales_in, uint8_t* codes, uint8_t* scales,
+                               uint16_t* y);
 
 /* Tensor scale from an amax. */
 float orc_tensor_scale(float amax);

@@ -56,6 +56,7 @@ def _load():
             "orc_bf16_from_f32_array": (None, [vp, i64, vp]),
             "orc_amax": (f32, [vp, i32, i64]),
             "orc_nvfp4_quantize": (None, [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]),
+            "orc_nvfp4_quantize_blocks": (None, [vp, i32, i64, f32, vp, vp, vp, vp]),
             "orc_tensor_scale": (f32, [f32]),
             "orc_mse_kgrid": (None, [i32, f32, f32, vp]),
             "orc_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
@@ -159,6 +160,21 @@ def nvfp4_quantize(x: np.ndarray, scales_in: np.ndarray | None = None,
     return codes, scales, float(ts[0]), y
 
 
+def nvfp4_quantize_blocks(x: np.ndarray, s_g: float, scales_in: np.ndarray | None = None):
+    """Quantize whole 16-element blocks of x (any shape, size % 16 == 0) under
+    tensor scale s_g.  Returns (codes u8[nb, 8], scales u8[nb], y u16[nb, 16])."""
+    x = np.ascontiguousarray(x)
+    assert x.size % 16 == 0
+    nb = x.size // 16
+    codes = np.empty((nb, 8), np.uint8)
+    scales = np.empty(nb, np.uint8)
+    y = np.empty((nb, 16), np.uint16)
+    sin = None if scales_in is None else np.ascontiguousarray(scales_in, dtype=np.uint8).reshape(-1)
+    _load().orc_nvfp4_quantize_blocks(_ptr(x), _dtype_code(x), nb, float(s_g), _ptr(sin),
+                                      _ptr(codes), _ptr(scales), _ptr(y))
+    return codes, scales, y
+
+
 def mse_kgrid(n: int = 64, k_min: float = 0.5, k_max: float = 1.0) -> np.ndarray:
     out = np.empty(n, np.float32)
     _load().orc_mse_kgrid(n, k_min, k_max, _ptr(out))
@@ -222,5 +238,5 @@ def kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0,
 __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
-    "nvfp4_quantize", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
+    "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
 ]

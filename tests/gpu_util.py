@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests (conversion of device tensors to the
+numpy forms the oracle takes, and the comparison rules)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def gpu_device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nvfp4_quantization_aware_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from nvfp4_quantization_aware_amd import build
+        build.build()
+    return torch.device("cuda:0")
+
+
+def announce(msg):
+    """Name the case before a GPU step (so a fault can be traced to it)."""
+    print("[gpu-case] " + msg, file=sys.stderr, flush=True)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy in the oracle's representation (bf16 as uint16 bits)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bf16_ulp(a: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at magnitude |a| (8 significant bits)."""
+    a = np.maximum(np.abs(a), 2.0**-133)
+    e = np.floor(np.log2(a))
+    return np.maximum(2.0 ** (e - 7), 2.0**-133)
+
+
+def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, rel=1e-5):
+    """Gradient rule: per row, |g - g_ref| <= rel * max_row |g_ref| for a
+    float32 gradient; for bf16, the bf16 rounding of a value within that band
+    (so additionally half a bf16 ulp)."""
+    g_ref = np.asarray(g_ref, np.float64)
+    tol = rel * np.abs(g_ref).max(axis=-1, keepdims=True)
+    if g_dev.dtype == np.uint16:
+        g = (g_dev.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bound = tol + 0.5 * bf16_ulp(np.abs(g_ref) + tol)
+    else:
+        g = g_dev.astype(np.float64)
+        bound = tol
+        l2 = np.linalg.norm(g - g_ref, axis=-1)
+        assert np.all(l2 <= rel * np.linalg.norm(g_ref, axis=-1)), l2.max()
+    err = np.abs(g - g_ref)
+    bad = err > bound
+    assert not bad.any(), "worst excess %g at %s" % ((err - bound).max(), np.argwhere(bad)[:3])

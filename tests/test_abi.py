@@ -1,0 +1,165 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/libqad.h declares, and rejects bad arguments on the host before any
+launch (every call here fails validation, so nothing touches a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import nvfp4_quantization_aware_amd as q
+from nvfp4_quantization_aware_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libqad.h")
+
+OK, INVALID, SHAPE, DTYPE, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P = 0x10000      # a 16-byte-aligned fake device address (never dereferenced)
+P_ODD = 0x10002  # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from nvfp4_quantization_aware_amd import build
+        build.build()
+    return q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qad_\w+|nvfp4_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_exported_symbols_in_dynamic_table(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+
+
+def test_status_strings_and_version(L):
+    assert L.qad_abi_version() == 1
+    for s in range(8):
+        assert L.qad_status_string(s).startswith(b"QAD_")
+    assert L.qad_status_string(99) == b"unknown qad_status_t"
+
+
+def test_workspace_sizes(L):
+    assert L.qad_workspace_bytes(q.QAD_OP_AMAX, 128, 2048, 4096) == 0
+    assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 128, 2048, 4096) == 512
+    assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 1, 1, 16) == 256
+    assert L.qad_workspace_bytes(q.QAD_OP_MSE_CALIBRATE, 1, 8192, 8192) == 256
+    assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, 8192, 131072) == 32768
+    assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
+
+
+def test_quantize_rejects(L):
+    f = L.nvfp4_quantize
+    ws = 1024
+    # C not a multiple of 16
+    assert f(P, 1, 1, 4, 24, None, None, None, None, None, P * 2, P * 3, ws, None) == SHAPE
+    # negative size
+    assert f(P, 1, -1, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == SHAPE
+    # bad dtype
+    assert f(P, 7, 1, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == DTYPE
+    # no output at all
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, None, P * 3, ws, None) == INVALID
+    # scales without tensor scale
+    assert f(P, 1, 1, 4, 32, P * 5, None, None, None, None, P * 2, None, 0, None) == INVALID
+    # null input
+    assert f(None, 1, 1, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == INVALID
+    # misaligned input / output / codes
+    assert f(P_ODD, 1, 1, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == ALIGN
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2 + 8, P * 3, ws, None) == ALIGN
+    assert f(P, 1, 1, 4, 32, None, None, P * 4 + 2, None, None, None, P * 3, ws, None) == ALIGN
+    # workspace missing / too small (dynamic mode needs it)
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2, None, 0, None) == WS
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2, P * 3, 8, None) == WS
+    # output overlapping the input
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, P + 16, P * 3, ws, None) == INVALID
+    # empty tensor: nothing to do
+    assert f(P, 1, 0, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == OK
+
+
+def test_qdq_fwd_bwd_reject(L):
+    assert L.nvfp4_qdq_fwd(P, 1, 1, 4, 32, None, None, None, P * 3, 1024, None) == INVALID
+    assert L.nvfp4_qdq_bwd(P, P * 2, 5, 100, None) == DTYPE
+    assert L.nvfp4_qdq_bwd(P, P * 2, 1, -3, None) == SHAPE
+    assert L.nvfp4_qdq_bwd(None, P * 2, 1, 100, None) == INVALID
+    assert L.nvfp4_qdq_bwd(P_ODD, P * 2, 1, 100, None) == ALIGN
+    assert L.nvfp4_qdq_bwd(P, P + 64, 1, 100, None) == INVALID  # partial overlap
+    # in place and empty are no-ops
+    assert L.nvfp4_qdq_bwd(P, P, 1, 100, None) == OK
+    assert L.nvfp4_qdq_bwd(P, P * 2, 1, 0, None) == OK
+
+
+def test_amax_rejects(L):
+    assert L.nvfp4_amax(P, 1, 1, 4, 12, P * 2, None) == SHAPE   # 24-byte rows
+    assert L.nvfp4_amax(P, 2, 1, 4, 16, P * 2, None) == DTYPE
+    assert L.nvfp4_amax(P, 1, 1, 4, 16, None, None) == INVALID
+    assert L.nvfp4_amax(P_ODD, 1, 1, 4, 16, P * 2, None) == ALIGN
+    assert L.nvfp4_amax(P, 1, 0, 4, 16, None, None) == OK
+
+
+def test_mse_rejects(L):
+    f = L.nvfp4_mse_calibrate
+    args = lambda n, lo, hi: (P, 1, 1, 4, 32, n, lo, hi, P * 2, P * 3, P * 4, 1024, None)
+    assert f(*args(0, 0.5, 1.0)) == INVALID
+    assert f(*args(64, 0.0, 1.0)) == INVALID
+    assert f(*args(64, 0.8, 0.5)) == INVALID
+    assert f(*args(4, 0.5, 1.0)) == INVALID          # step 1/6 > 0.5/16: could skip E4M3 codes
+    assert f(*args(64, 0.5, float("inf"))) == INVALID
+    assert f(P, 1, 1, 4, 24, 64, 0.5, 1.0, P * 2, P * 3, P * 4, 1024, None) == SHAPE
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, None, P * 3, P * 4, 1024, None) == INVALID
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3, None, 0, None) == WS
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3 + 2, P * 4, 1024, None) == ALIGN
+
+
+def test_kl_rejects(L):
+    f = L.qad_kl_fwd_bwd
+    good = [P, P * 2, 1, 4, 64, 1.0, 0.25, P * 3, None, P * 4, 1, P * 5, 1024, None]
+
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a2=9) == DTYPE
+    assert call(a10=9) == DTYPE
+    assert call(a4=60) == SHAPE                       # vocab % 8
+    assert call(a3=-1) == SHAPE
+    assert call(a5=0.0) == INVALID                    # temperature
+    assert call(a5=float("nan")) == INVALID
+    assert call(a6=float("inf")) == INVALID
+    assert call(a7=None) == INVALID                   # loss_out
+    assert call(a0=None) == INVALID
+    assert call(a1=P_ODD) == ALIGN
+    assert call(a9=P + 32) == INVALID                 # gradient overlaps the teacher
+    assert call(a11=None, a12=0) == WS                # no row_loss and no workspace
+    assert call(a12=16) == WS
+
+
+def test_check_finite_rejects(L):
+    assert L.qad_check_finite(P, -1, None) == SHAPE
+    assert L.qad_check_finite(None, 3, None) == INVALID
+    assert L.qad_check_finite(None, 0, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
