@@ -47,7 +47,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or keeps them.  Scratch memory comes from the
- *    caller's `workspace` (size from qad_workspace_bytes()).
+ *    caller's `workspace` (size from qad_workspace_bytes(), 256-byte aligned;
+ *    its contents need not be initialised and are overwritten).
  *  - All work is enqueued asynchronously on `stream` (0 = the null stream);
  *    the call returns once it is enqueued.
  *  - Arguments are checked on the host before anything is launched; a failed
@@ -100,18 +101,19 @@ const char* qad_status_string(qad_status_t status);
 int qad_abi_version(void);
 
 /* Bytes of workspace entry point `op` needs for B tensors of R x C elements
- * (for QAD_OP_KL: R token rows of C vocabulary logits).  Always a multiple of
- * 256; 0 means no workspace is needed.  Returns 0 for invalid sizes too (the
- * entry point then reports the shape error). */
+ * of either dtype (for QAD_OP_KL: R token rows of C vocabulary logits).
+ * Always a multiple of 256.  Returns 0 for invalid sizes (the entry point
+ * then reports the shape error).  Frozen-scale quantization needs none. */
 size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C);
 
 /* Tensor amax (max calibration, [Lightning] "量化尺度处理策略"): amax_out[b] =
  * max |x[b]| over each of B contiguous tensors of R x C elements.
- *   x        : device, dtype xt (QAD_F32 or QAD_BF16), [B][R][C], 16-byte aligned
- *   amax_out : device float[B] (overwritten; also its own scratch)
- * C need not be a multiple of 16 here. */
+ *   x         : device, dtype xt (QAD_F32 or QAD_BF16), [B][R][C], 16-byte
+ *               aligned; C * sizeof(dtype) must be a multiple of 16
+ *   amax_out  : device float[B]
+ *   workspace : qad_workspace_bytes(QAD_OP_AMAX, B, R, C) bytes, 256-byte aligned */
 qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
-                        float* amax_out, qad_stream_t stream);
+                        float* amax_out, void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* NVFP4 quantization of B independent tensors [R][C] ([Nano] "NVFP4-Format
  * und warum es wichtig ist?"; dynamic vs frozen per [Lightning] "量化尺度处理策略").
@@ -180,7 +182,9 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
  *   grad_student     : device [tokens][vocab] of dtype gt (QAD_BF16, or
  *                      QAD_F32 for full-precision gradients), or NULL for
  *                      the forward only; must not overlap the inputs
- *   workspace        : qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab) */
+ *   workspace        : qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab) bytes
+ *                      (per-row exchange records; per-row losses when
+ *                      row_loss is NULL) */
 qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt,
                             int64_t tokens, int64_t vocab, float temperature, float grad_scale,
                             float* loss_out, float* row_loss, void* grad_student, qad_dtype_t gt,

@@ -27,7 +27,7 @@ SIGNATURES = {
     "qad_status_string": (C.c_char_p, [_int]),
     "qad_abi_version": (_int, []),
     "qad_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
-    "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp]),
+    "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_fwd": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
@@ -103,11 +103,15 @@ def workspace(op: int, B: int, R: int, C_: int, device) -> torch.Tensor | None:
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def nvfp4_amax(x: torch.Tensor, amax_out: torch.Tensor | None = None) -> torch.Tensor:
+def nvfp4_amax(x: torch.Tensor, amax_out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None) -> torch.Tensor:
     B, R, Cc = _brc(x)
     if amax_out is None:
         amax_out = torch.empty(B, dtype=torch.float32, device=x.device)
-    _check(lib().nvfp4_amax(_p(x), _dt(x), B, R, Cc, _p(amax_out), _stream(x.device)), "nvfp4_amax")
+    if ws is None:
+        ws = workspace(QAD_OP_AMAX, B, R, Cc, x.device)
+    _check(lib().nvfp4_amax(_p(x), _dt(x), B, R, Cc, _p(amax_out), _p(ws), 0 if ws is None else ws.numel(),
+                            _stream(x.device)), "nvfp4_amax")
     return amax_out
 
 
@@ -195,7 +199,7 @@ def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: fl
     if grad is None and grad_dtype is not None:
         grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
     gt = _dt(grad) if grad is not None else QAD_BF16
-    if ws is None and rows is None:
+    if ws is None:
         ws = workspace(QAD_OP_KL, 1, tokens, vocab, dev)
     _check(lib().qad_kl_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, temperature,
                                 grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),

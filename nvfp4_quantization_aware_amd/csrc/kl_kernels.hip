@@ -4,31 +4,43 @@
 // element-wise over the vocabulary and dense fp32 copies of them do not fit,
 // so the loss streams bf16 logits and never materialises probabilities).
 //
-// One workgroup per token row.  Pass 1 streams the row once and keeps, per
-// lane, an online (max, sum) pair for teacher and student plus the
-// teacher-weighted sum of (t - s), in base 2 (v_exp_f32 computes 2^x; logits
-// are scaled by log2(e)/T inside one FMA with the running max).  A workgroup
-// reduction merges the lanes.  Pass 2 re-reads the row and writes the gradient
-// (q - p) * grad_scale / T with q = 2^(c s - m_s) / Z_s (and p alike): the
-// normaliser is a multiply, so the exponent never carries the rounding of a
-// large log-sum-exp.  Per-row losses go to row_loss; a single-group
-// kernel sums them in a fixed order (binary64) for the mean, so the result
-// never depends on scheduling.
+// One HBM pass.  A token row is cut into W segments, one workgroup each; a
+// workgroup loads its segment once and keeps the packed logits in registers.
+// Pass 1 reduces them to the segment's online-softmax state (max, sum of
+// 2^(c x - m) for teacher and student, teacher-weighted sum of t - s; c =
+// log2(e)/T, m the lane's own maxima).  The W states of a row are exchanged
+// through the workspace and merged in segment order (so every workgroup of the
+// row computes bit-identical row statistics, whatever the schedule).  Pass 2
+// computes 2^(c x - m_row) / Z_row from the logits still in registers and
+// writes the gradient (q - p) * grad_scale / T.  Recomputing two exponentials
+// costs less than holding them: it keeps ~4 workgroups resident per CU,
+// enough to hide the load and exchange latency.  Per-row losses go to row_loss; one
+// workgroup sums them in a fixed order (binary64) for the mean.
 #include "qad_device.h"
 #include "qad_internal.h"
 
 namespace qad {
 namespace {
 
-constexpr int kKlThreads = 1024;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 0x1.715476p+0f;  // RN(log2(e))
 constexpr float kLn2 = 0x1.62e430p-1f;    // RN(ln(2))
+constexpr int kSegThreads = 512;           // lanes per segment workgroup
+constexpr int kSegUnits = 4;               // 8-element units per lane and tensor
+constexpr int64_t kSegSpan = (int64_t)kSegThreads * kSegUnits; // units per segment
+constexpr int kMaxSegments = 64;           // longer rows take the two-pass kernel
+constexpr uint64_t kWaitTicks = 2000000;   // bounded wait (20 ms at 100 MHz)
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
+__device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
 
 struct Stats {
     float mt, zt, at, ms, zs;
 };
+
+__device__ __forceinline__ Stats empty_stats() { return Stats{-__builtin_inff(), 0.0f, 0.0f, -__builtin_inff(), 0.0f}; }
 
 // merge two partial (max, sum) states; equal maxima (also both -inf) need no
 // rescaling, which keeps empty partials from producing 0 * inf
@@ -49,25 +61,34 @@ __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b)
 
 __device__ __forceinline__ Stats shfl_xor_stats(const Stats& s, int o)
 {
-    Stats r;
-    r.mt = __shfl_xor(s.mt, o, 64);
-    r.zt = __shfl_xor(s.zt, o, 64);
-    r.at = __shfl_xor(s.at, o, 64);
-    r.ms = __shfl_xor(s.ms, o, 64);
-    r.zs = __shfl_xor(s.zs, o, 64);
+    return Stats{__shfl_xor(s.mt, o, 64), __shfl_xor(s.zt, o, 64), __shfl_xor(s.at, o, 64),
+                 __shfl_xor(s.ms, o, 64), __shfl_xor(s.zs, o, 64)};
+}
+
+// workgroup reduction in a fixed order (xor tree in each wave, then waves in
+// order); the result is returned to every lane
+template <int NT>
+__device__ Stats group_merge(Stats st, Stats* part)
+{
+    for (int o = 32; o > 0; o >>= 1) st = merge(st, shfl_xor_stats(st, o));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = st;
+    __syncthreads();
+    Stats r = part[0];
+    for (int w = 1; w < NT / 64; ++w) r = merge(r, part[w]);
+    __syncthreads();
     return r;
 }
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t unit, float (&v)[8])
+__device__ __forceinline__ void load8(const void* base, int64_t unit, bool valid, float (&v)[8])
 {
     if constexpr (BF16) {
-        const uint4 w = reinterpret_cast<const uint4*>(base)[unit];
+        const v4u w = valid ? ldnt(base, unit) : v4u{0u, 0u, 0u, 0u};
         v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
         v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
     } else {
-        const uint4* p = reinterpret_cast<const uint4*>(base) + 2 * unit;
-        const uint4 w0 = p[0], w1 = p[1];
+        const v4u w0 = valid ? ldnt(base, 2 * unit) : v4u{0u, 0u, 0u, 0u};
+        const v4u w1 = valid ? ldnt(base, 2 * unit + 1) : v4u{0u, 0u, 0u, 0u};
         v[0] = as_f(w0.x); v[1] = as_f(w0.y); v[2] = as_f(w0.z); v[3] = as_f(w0.w);
         v[4] = as_f(w1.x); v[5] = as_f(w1.y); v[6] = as_f(w1.z); v[7] = as_f(w1.w);
     }
@@ -77,6 +98,222 @@ __device__ __forceinline__ float max8(const float (&v)[8])
 {
     return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
 }
+
+__device__ __forceinline__ float sum8(const float (&v)[8])
+{
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+__device__ __forceinline__ void unpack8(v4u w, float (&v)[8])
+{
+    v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+    v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
+}
+
+// One unit of 8 teacher and 8 student logits, as held in registers: one
+// 16-byte vector per tensor for bf16, two for fp32.
+template <bool BF16>
+struct Unit {
+    static constexpr int V = BF16 ? 1 : 2;
+    v4u t[V], s[V];
+
+    __device__ void load(const KlArgs& a, int64_t unit, bool valid)
+    {
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            t[q] = valid ? ldnt(a.teacher, V * unit + q) : v4u{0u, 0u, 0u, 0u};
+            s[q] = valid ? ldnt(a.student, V * unit + q) : v4u{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ void values(float (&tv)[8], float (&sv)[8]) const
+    {
+        if constexpr (BF16) {
+            unpack8(t[0], tv);
+            unpack8(s[0], sv);
+        } else {
+            tv[0] = as_f(t[0].x); tv[1] = as_f(t[0].y); tv[2] = as_f(t[0].z); tv[3] = as_f(t[0].w);
+            tv[4] = as_f(t[1].x); tv[5] = as_f(t[1].y); tv[6] = as_f(t[1].z); tv[7] = as_f(t[1].w);
+            sv[0] = as_f(s[0].x); sv[1] = as_f(s[0].y); sv[2] = as_f(s[0].z); sv[3] = as_f(s[0].w);
+            sv[4] = as_f(s[1].x); sv[5] = as_f(s[1].y); sv[6] = as_f(s[1].z); sv[7] = as_f(s[1].w);
+        }
+    }
+};
+
+// Opaque to the optimiser: values derived from v before this point cannot be
+// reused after it.  Used so that widened logits are recomputed from the packed
+// registers where needed instead of being kept alive (64 extra registers).
+__device__ __forceinline__ void refresh(v4u& v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ int64_t lane_unit(int64_t seg_u0, int k) { return seg_u0 + k * kSegThreads + threadIdx.x; }
+
+// A lane's state over its units of one segment: maxima first, then the sums
+// of 2^(c x - m) and the teacher-weighted sum of t - s, unit by unit in
+// ascending order.  `get(k, unit)` supplies unit k: from registers in the
+// segment's own workgroup (UNROLL, everything in flight at once), from memory
+// one unit at a time in the bounded wait's fallback.  The arithmetic is the
+// same either way (the maximum is order-independent, the sums run in unit
+// order), so both give bit-identical states.
+template <bool BF16, bool UNROLL, class Get>
+__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get)
+{
+    float mt = -__builtin_inff(), ms = -__builtin_inff();
+#pragma unroll(UNROLL ? kSegUnits : 1)
+    for (int k = 0; k < kSegUnits; ++k) {
+        const bool valid = lane_unit(seg_u0, k) < units;
+        Unit<BF16> u;
+        get(k, u);
+        float tv[8], sv[8];
+        u.values(tv, sv);
+        if (valid) { mt = fmaxf(mt, max8(tv)); ms = fmaxf(ms, max8(sv)); }
+    }
+    mt *= c;  // c > 0: the max of the scaled logits
+    ms *= c;
+    float zt = 0.0f, zs = 0.0f, at = 0.0f;
+#pragma unroll(UNROLL ? kSegUnits : 1)
+    for (int k = 0; k < kSegUnits; ++k) {
+        const bool valid = lane_unit(seg_u0, k) < units;
+        Unit<BF16> u;
+        get(k, u);
+#pragma unroll
+        for (int q = 0; q < Unit<BF16>::V; ++q) { refresh(u.t[q]); refresh(u.s[q]); }
+        float tv[8], sv[8], pt[8], ps[8];
+        u.values(tv, sv);
+        float pa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pt[i] = valid ? exp2_hw(__builtin_fmaf(tv[i], c, -mt)) : 0.0f;
+            ps[i] = valid ? exp2_hw(__builtin_fmaf(sv[i], c, -ms)) : 0.0f;
+            pa = __builtin_fmaf(pt[i], tv[i] - sv[i], pa);
+        }
+        zt = zt + sum8(pt);
+        zs = zs + sum8(ps);
+        at = at + pa;
+    }
+    return Stats{mt, zt, at, ms, zs};
+}
+
+
+// per-row exchange record for W segments, in words (whole 128-byte lines)
+__host__ __device__ inline int64_t rec_words(int W) { return (32 + 8 * (int64_t)W + 31) & ~(int64_t)31; }
+
+// Per-row exchange record (rec_words(W) words, own cache lines): word 0 counts
+// arrived segments; segment s stores its 5 state words at 32 + 8 s.  Order is
+// carried by completion: a workgroup waits for the return of its exchanges
+// before it increments the count, so a reader that sees W arrivals also sees
+// every state.  Counts are zeroed before each launch.
+__device__ __forceinline__ uint32_t a_load(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+
+template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
+__global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+                                                             uint32_t* rec_base)
+{
+    __shared__ Stats part[kSegThreads / 64];
+    __shared__ Stats seg_stats[kMaxSegments];
+    __shared__ uint32_t arrived;
+    const int64_t row = blockIdx.x / W;
+    const int seg = (int)(blockIdx.x - row * W);
+    const int64_t units = a.vocab >> 3;
+    const int64_t row_unit0 = row * units;
+    const int tid = threadIdx.x;
+
+    const int64_t seg_u0 = seg * kSegSpan;
+    Unit<BF16_IN> mine[kSegUnits];
+    bool valid[kSegUnits];
+#pragma unroll
+    for (int k = 0; k < kSegUnits; ++k) {
+        valid[k] = lane_unit(seg_u0, k) < units;
+        mine[k].load(a, row_unit0 + lane_unit(seg_u0, k), valid[k]);
+    }
+    const Stats lane_st = lane_state<BF16_IN, true>(seg_u0, units, c, [&](int k, Unit<BF16_IN>& u) { u = mine[k]; });
+    const Stats my_seg = group_merge<kSegThreads>(lane_st, part);
+#pragma unroll
+    for (int k = 0; k < kSegUnits; ++k)
+#pragma unroll
+        for (int q = 0; q < Unit<BF16_IN>::V; ++q) { refresh(mine[k].t[q]); refresh(mine[k].s[q]); }
+
+    Stats row_st;
+    if (W == 1) {
+        row_st = my_seg;
+    } else {
+        uint32_t* rec = rec_base + row * rec_words(W);
+        if (tid < 5) {
+            const float v = tid == 0 ? my_seg.mt : tid == 1 ? my_seg.zt : tid == 2 ? my_seg.at : tid == 3 ? my_seg.ms : my_seg.zs;
+            completed(__hip_atomic_exchange(rec + 32 + 8 * seg + tid, as_u(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        if (tid == 0) {
+            completed(__hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            const uint64_t t0 = wall_clock64();
+            uint32_t n;
+            while ((n = a_load(rec)) < (uint32_t)W) {
+                __builtin_amdgcn_s_sleep(4);
+                if (wall_clock64() - t0 > kWaitTicks) break;
+            }
+            arrived = n;
+        }
+        __syncthreads();
+        if (arrived >= (uint32_t)W) {
+            if (tid < 5 * W) {
+                const int s = tid / 5, f = tid - 5 * s;
+                const float v = as_f(a_load(rec + 32 + 8 * s + f));
+                float* dst = &seg_stats[s].mt;
+                dst[f] = v;
+            }
+            __syncthreads();
+        } else {
+            // timed out: compute every segment's state here, with the same
+            // lane mapping and arithmetic as its own workgroup
+            for (int s = 0; s < W; ++s) {
+                const int64_t o_u0 = s * kSegSpan;
+                const Stats ol = lane_state<BF16_IN, false>(o_u0, units, c, [&](int k, Unit<BF16_IN>& u) {
+                    u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
+                });
+                const Stats os = group_merge<kSegThreads>(ol, part);
+                if (tid == 0) seg_stats[s] = os;
+            }
+            __syncthreads();
+        }
+        row_st = seg_stats[0];
+        for (int s = 1; s < W; ++s) row_st = merge(row_st, seg_stats[s]);
+    }
+
+    if (seg == 0 && tid == 0) {
+        // KL = E_p[t - s]/T - (LSE_t - LSE_s), LSE in log2 units m + log2 Z
+        a.row_loss[row] = (row_st.at / row_st.zt) * inv_t -
+                          kLn2 * ((row_st.mt - row_st.ms) + log2f(row_st.zt / row_st.zs));
+    }
+    if constexpr (GRAD != 0) {
+        // p = 2^(c t - m_row) / Z_row and q alike, times grad_scale / T, from
+        // the logits still held in registers
+        const float wt = gmul / row_st.zt, ws = gmul / row_st.zs;
+#pragma unroll
+        for (int k = 0; k < kSegUnits; ++k) {
+            if (!valid[k]) continue;
+            float tv[8], sv[8], g[8];
+            mine[k].values(tv, sv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
+                const float eq = exp2_hw(__builtin_fmaf(sv[i], c, -row_st.ms));
+                g[i] = __builtin_fmaf(eq, ws, -(ep * wt));
+            }
+            const int64_t u = row_unit0 + lane_unit(seg_u0, k);
+            if constexpr (GRAD == 1) {
+                stnt(a.grad, u,
+                     v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])});
+            } else {
+                stnt(a.grad, 2 * u, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
+                stnt(a.grad, 2 * u + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-pass kernel for rows longer than kMaxSegments segments: one workgroup
+// per row streams the row twice (online state, then the gradient).
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 1024;
 
 // fold one unit of 8 teacher / student logits into the lane's running state
 __device__ __forceinline__ void accumulate(Stats& st, const float (&t)[8], const float (&s)[8], float c)
@@ -88,130 +325,123 @@ __device__ __forceinline__ void accumulate(Stats& st, const float (&t)[8], const
     st.mt = nmt;
     st.ms = nms;
     float et[8], es[8];
+    float pa = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         et[i] = exp2_hw(__builtin_fmaf(t[i], c, -nmt));
         es[i] = exp2_hw(__builtin_fmaf(s[i], c, -nms));
+        pa = __builtin_fmaf(et[i], t[i] - s[i], pa);
     }
-    const float pz = ((et[0] + et[1]) + (et[2] + et[3])) + ((et[4] + et[5]) + (et[6] + et[7]));
-    const float qz = ((es[0] + es[1]) + (es[2] + es[3])) + ((es[4] + es[5]) + (es[6] + es[7]));
-    float pa = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pa = __builtin_fmaf(et[i], t[i] - s[i], pa);
-    st.zt = st.zt * ft + pz;
+    st.zt = st.zt * ft + sum8(et);
     st.at = st.at * ft + pa;
-    st.zs = st.zs * fs + qz;
+    st.zs = st.zs * fs + sum8(es);
 }
 
-template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
-__global__ __launch_bounds__(kKlThreads) void kl_row_kernel(KlArgs a, float c, float inv_t, float gmul)
+template <bool BF16_IN, int GRAD>
+__global__ __launch_bounds__(kRowThreads) void kl_row_kernel(KlArgs a, float c, float inv_t, float gmul)
 {
+    __shared__ Stats part[kRowThreads / 64];
     const int64_t row = blockIdx.x;
     const int64_t units = a.vocab >> 3;
     const int64_t ubase = row * units;
     const int tid = threadIdx.x;
-
-    Stats st = {-__builtin_inff(), 0.0f, 0.0f, -__builtin_inff(), 0.0f};
-    int64_t u = tid;
-    for (; u + kKlThreads < units; u += 2 * kKlThreads) {
-        float t0[8], s0[8], t1[8], s1[8];
-        load8<BF16_IN>(a.teacher, ubase + u, t0);
-        load8<BF16_IN>(a.student, ubase + u, s0);
-        load8<BF16_IN>(a.teacher, ubase + u + kKlThreads, t1);
-        load8<BF16_IN>(a.student, ubase + u + kKlThreads, s1);
-        accumulate(st, t0, s0, c);
-        accumulate(st, t1, s1, c);
+    Stats st = empty_stats();
+    for (int64_t u = tid; u < units; u += kRowThreads) {
+        float t[8], s[8];
+        load8<BF16_IN>(a.teacher, ubase + u, true, t);
+        load8<BF16_IN>(a.student, ubase + u, true, s);
+        accumulate(st, t, s, c);
     }
-    if (u < units) {
-        float t0[8], s0[8];
-        load8<BF16_IN>(a.teacher, ubase + u, t0);
-        load8<BF16_IN>(a.student, ubase + u, s0);
-        accumulate(st, t0, s0, c);
-    }
-
-    // workgroup reduction: waves by xor-shuffles, then the 16 wave results
-    for (int o = 32; o > 0; o >>= 1) st = merge(st, shfl_xor_stats(st, o));
-    __shared__ Stats part[kKlThreads / 64];
-    __shared__ float fin[4];
-    if ((tid & 63) == 0) part[tid >> 6] = st;
-    __syncthreads();
-    if (tid < 64) {
-        Stats w = tid < kKlThreads / 64 ? part[tid]
-                                        : Stats{-__builtin_inff(), 0.0f, 0.0f, -__builtin_inff(), 0.0f};
-        for (int o = 8; o > 0; o >>= 1) w = merge(w, shfl_xor_stats(w, o));
-        if (tid == 0) {
-            // KL = E_p[t - s]/T - (LSE_t - LSE_s), LSE in log2 units m + log2 Z
-            fin[0] = w.mt;
-            fin[1] = w.ms;
-            fin[2] = gmul / w.zt;
-            fin[3] = gmul / w.zs;
-            const float kl = (w.at / w.zt) * inv_t - kLn2 * ((w.mt - w.ms) + log2f(w.zt / w.zs));
-            a.row_loss[row] = kl;
-        }
-    }
+    const Stats w = group_merge<kRowThreads>(st, part);
+    if (tid == 0)
+        a.row_loss[row] = (w.at / w.zt) * inv_t - kLn2 * ((w.mt - w.ms) + log2f(w.zt / w.zs));
     if constexpr (GRAD == 0) return;
-    __syncthreads();
-    const float mt = fin[0], ms = fin[1], wt = fin[2], ws = fin[3];
-    for (u = tid; u < units; u += kKlThreads) {
+    const float wt = gmul / w.zt, ws = gmul / w.zs;
+    for (int64_t u = tid; u < units; u += kRowThreads) {
         float t[8], s[8], g[8];
-        load8<BF16_IN>(a.teacher, ubase + u, t);
-        load8<BF16_IN>(a.student, ubase + u, s);
+        load8<BF16_IN>(a.teacher, ubase + u, true, t);
+        load8<BF16_IN>(a.student, ubase + u, true, s);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float eq = exp2_hw(__builtin_fmaf(s[i], c, -ms));
-            const float ep = exp2_hw(__builtin_fmaf(t[i], c, -mt));
+            const float eq = exp2_hw(__builtin_fmaf(s[i], c, -w.ms));
+            const float ep = exp2_hw(__builtin_fmaf(t[i], c, -w.mt));
             g[i] = __builtin_fmaf(eq, ws, -(ep * wt));
         }
         if constexpr (GRAD == 1) {
-            reinterpret_cast<uint4*>(a.grad)[ubase + u] =
-                make_uint4(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                           pack_bf16x2(g[6], g[7]));
+            stnt(a.grad, ubase + u,
+                 v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])});
         } else {
-            float4* p = reinterpret_cast<float4*>(a.grad) + 2 * (ubase + u);
-            p[0] = make_float4(g[0], g[1], g[2], g[3]);
-            p[1] = make_float4(g[4], g[5], g[6], g[7]);
+            stnt(a.grad, 2 * (ubase + u), v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
+            stnt(a.grad, 2 * (ubase + u) + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
         }
     }
 }
 
 // mean of the per-row losses: fixed assignment of rows to lanes, binary64
 // accumulation, fixed reduction tree
-__global__ __launch_bounds__(kKlThreads) void kl_mean_kernel(const float* row_loss, int64_t rows, float* loss_out)
+__global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, int64_t rows, float* loss_out)
 {
-    __shared__ double part[kKlThreads];
+    __shared__ double part[1024];
     double acc = 0.0;
-    for (int64_t r = threadIdx.x; r < rows; r += kKlThreads) acc += (double)row_loss[r];
+    for (int64_t r = threadIdx.x; r < rows; r += 1024) acc += (double)row_loss[r];
     part[threadIdx.x] = acc;
     __syncthreads();
-    for (int w = kKlThreads / 2; w > 0; w >>= 1) {
+    for (int w = 512; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x == 0) loss_out[0] = rows > 0 ? (float)(part[0] / (double)rows) : 0.0f;
 }
 
+__global__ void zero_counts_kernel(uint32_t* rec, int64_t rows, int64_t stride)
+{
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r < rows) rec[r * stride] = 0u;
+}
+
+int segments(int64_t vocab) { return (int)(((vocab >> 3) + kSegSpan - 1) / kSegSpan); }
+
 } // namespace
 
-hipError_t launch_kl(const KlArgs& a, hipStream_t stream)
+size_t kl_workspace_bytes(int64_t tokens, int64_t vocab)
+{
+    const int W = segments(vocab);
+    const size_t rows = (size_t)tokens * 4;                         // per-row losses
+    const size_t recs = W > 1 && W <= kMaxSegments ? (size_t)tokens * rec_words(W) * 4 : 0;
+    return ((rows + 255) & ~(size_t)255) + recs;
+}
+
+hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
 {
     if (a.tokens > 0 && a.vocab > 0) {
         const float c = kLog2e / a.temperature;
         const float inv_t = 1.0f / a.temperature;
         const float gmul = a.grad_scale / a.temperature;
-        const dim3 grid((unsigned)a.tokens), block(kKlThreads);
-        if (a.bf16_in) {
-            if (!a.grad) hipLaunchKernelGGL((kl_row_kernel<true, 0>), grid, block, 0, stream, a, c, inv_t, gmul);
-            else if (a.grad_bf16) hipLaunchKernelGGL((kl_row_kernel<true, 1>), grid, block, 0, stream, a, c, inv_t, gmul);
-            else hipLaunchKernelGGL((kl_row_kernel<true, 2>), grid, block, 0, stream, a, c, inv_t, gmul);
+        const int W = segments(a.vocab);
+        const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
+        if (W <= kMaxSegments) {
+            uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                        (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
+            if (W > 1) {
+                hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((a.tokens + 255) / 256)), dim3(256), 0, stream,
+                                   rec, a.tokens, rec_words(W));
+            }
+            const dim3 grid((unsigned)(a.tokens * W)), block(kSegThreads);
+#define KS(BF, G) hipLaunchKernelGGL((kl_seg_kernel<BF, G>), grid, block, 0, stream, a, W, c, inv_t, gmul, rec)
+            if (a.bf16_in) { if (gmode == 0) KS(true, 0); else if (gmode == 1) KS(true, 1); else KS(true, 2); }
+            else { if (gmode == 0) KS(false, 0); else if (gmode == 1) KS(false, 1); else KS(false, 2); }
+#undef KS
         } else {
-            if (!a.grad) hipLaunchKernelGGL((kl_row_kernel<false, 0>), grid, block, 0, stream, a, c, inv_t, gmul);
-            else if (a.grad_bf16) hipLaunchKernelGGL((kl_row_kernel<false, 1>), grid, block, 0, stream, a, c, inv_t, gmul);
-            else hipLaunchKernelGGL((kl_row_kernel<false, 2>), grid, block, 0, stream, a, c, inv_t, gmul);
+            const dim3 grid((unsigned)a.tokens), block(kRowThreads);
+#define KR(BF, G) hipLaunchKernelGGL((kl_row_kernel<BF, G>), grid, block, 0, stream, a, c, inv_t, gmul)
+            if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
+            else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
+#undef KR
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(kKlThreads), 0, stream, a.row_loss, a.tokens, a.loss_out);
+    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
     return hipGetLastError();
 }
 

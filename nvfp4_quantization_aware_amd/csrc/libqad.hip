@@ -32,8 +32,15 @@ int64_t tensor_elems(int64_t B, int64_t R, int64_t C)
 
 qad_status_t hip_status(hipError_t e) { return e == hipSuccess ? QAD_OK : QAD_ERR_HIP; }
 
-// the amax words live at the start of the workspace
-uint32_t* ws_amax(void* workspace) { return static_cast<uint32_t*>(workspace); }
+uint32_t* ws_words(void* workspace) { return static_cast<uint32_t*>(workspace); }
+
+// workspace of the tensor records for B tensors of rc elements (sized for
+// fp32, whose 32 KiB chunks are the most numerous; bf16 needs less)
+size_t record_bytes(int64_t B, int64_t rc)
+{
+    const int64_t P = qad::quantize_chunks(false, rc);
+    return round256((size_t)B * (size_t)qad::record_words(P) * 4);
+}
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {
@@ -63,7 +70,7 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     const bool frozen = scales_in != nullptr;
     if (!frozen) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C)) return QAD_ERR_WORKSPACE;
-        if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
+        if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
     }
     hipStream_t s = hs(stream);
     QuantizeArgs a;
@@ -73,17 +80,18 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     a.elems = R * C;
     a.scales_in = scales_in;
     a.tscale_in = tscale_in;
-    a.amax_bits = frozen ? nullptr : ws_amax(workspace);
     a.codes = codes;
     a.scales_out = scales_out;
     a.tscale_out = tscale_out;
     a.y = static_cast<uint16_t*>(y);
-    if (!frozen) {
-        hipError_t e = qad::launch_fill_u32(ws_amax(workspace), B, 0u, s);
-        if (e == hipSuccess) e = qad::launch_amax(x, a.bf16, B, a.elems, ws_amax(workspace), s);
-        if (e != hipSuccess) return QAD_ERR_HIP;
-    }
-    return hip_status(qad::launch_quantize(a, s));
+    if (frozen) return hip_status(qad::launch_quantize(a, qad::QUANT_FROZEN, nullptr, s));
+    // dynamic scales: one pass when every chunk of a tensor can be resident at
+    // once, otherwise an amax pass first
+    if (qad::quantize_one_pass_ok(a.bf16, B, a.elems))
+        return hip_status(qad::launch_quantize(a, qad::QUANT_ONE_PASS, ws_words(workspace), s));
+    hipError_t e = qad::launch_amax(x, a.bf16, B, a.elems, ws_words(workspace), s);
+    if (e != hipSuccess) return QAD_ERR_HIP;
+    return hip_status(qad::launch_quantize(a, qad::QUANT_AMAX_GIVEN, ws_words(workspace), s));
 }
 
 } // namespace
@@ -111,16 +119,16 @@ size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
 {
     if (tensor_elems(B, R, C) < 0) return 0;
     switch (op) {
-    case QAD_OP_AMAX: return 0;
+    case QAD_OP_AMAX:
     case QAD_OP_QUANTIZE:
-    case QAD_OP_MSE_CALIBRATE: return round256((size_t)B * 4);
-    case QAD_OP_KL: return round256((size_t)R * 4);
+    case QAD_OP_MSE_CALIBRATE: return record_bytes(B, R * C);
+    case QAD_OP_KL: return round256(qad::kl_workspace_bytes(R, C));
     }
     return 0;
 }
 
 qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C, float* amax_out,
-                        qad_stream_t stream)
+                        void* workspace, size_t ws_bytes, qad_stream_t stream)
 {
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
@@ -130,9 +138,12 @@ qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int
     if (n > 0 && !x) return QAD_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(amax_out, 4)) return QAD_ERR_ALIGNMENT;
     hipStream_t s = hs(stream);
-    uint32_t* bits = reinterpret_cast<uint32_t*>(amax_out);
-    hipError_t e = qad::launch_fill_u32(bits, B, 0u, s);
-    if (e == hipSuccess && n > 0) e = qad::launch_amax(x, xt == QAD_BF16, B, R * C, bits, s);
+    uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
+    if (n == 0) return hip_status(qad::launch_fill_u32(out, B, 0u, s));
+    if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_AMAX, B, R, C)) return QAD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
+    hipError_t e = qad::launch_amax(x, xt == QAD_BF16, B, R * C, ws_words(workspace), s);
+    if (e == hipSuccess) e = qad::launch_amax_out(ws_words(workspace), B, R * C, xt == QAD_BF16, out, s);
     return hip_status(e);
 }
 
@@ -182,7 +193,7 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
     if (!w || !scales_out || !tscale_out) return QAD_ERR_INVALID_ARG;
     if (!aligned(w, 16) || !aligned(tscale_out, 4)) return QAD_ERR_ALIGNMENT;
     if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_MSE_CALIBRATE, B, R, C)) return QAD_ERR_WORKSPACE;
-    if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
+    if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
     hipStream_t s = hs(stream);
     qad::MseArgs a;
     a.w = w;
@@ -191,13 +202,9 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
     a.elems = R * C;
     a.k_lo = k_min;
     a.k_hi = n_candidates > 1 ? k_max : k_min;
-    a.amax_bits = ws_amax(workspace);
     a.scales_out = scales_out;
     a.tscale_out = tscale_out;
-    hipError_t e = qad::launch_fill_u32(ws_amax(workspace), B, 0u, s);
-    if (e == hipSuccess) e = qad::launch_amax(w, a.bf16, B, a.elems, ws_amax(workspace), s);
-    if (e == hipSuccess) e = qad::launch_mse_calibrate(a, s);
-    return hip_status(e);
+    return hip_status(qad::launch_mse_calibrate(a, ws_words(workspace), s));
 }
 
 qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt, int64_t tokens,
@@ -220,12 +227,11 @@ qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_
         if (ranges_overlap(teacher, ib, grad_student, gb) || ranges_overlap(student, ib, grad_student, gb))
             return QAD_ERR_INVALID_ARG;
     }
-    float* rows = row_loss;
-    if (!rows && tokens > 0) {
+    if (tokens > 0) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab)) return QAD_ERR_WORKSPACE;
-        if (!aligned(workspace, 4)) return QAD_ERR_ALIGNMENT;
-        rows = static_cast<float*>(workspace);
+        if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
     }
+    float* rows = row_loss ? row_loss : static_cast<float*>(workspace);
     qad::KlArgs a;
     a.teacher = teacher;
     a.student = student;
@@ -238,7 +244,7 @@ qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_
     a.loss_out = loss_out;
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
-    return hip_status(qad::launch_kl(a, hs(stream)));
+    return hip_status(qad::launch_kl(a, workspace, hs(stream)));
 }
 
 qad_status_t qad_check_finite(const float* values, int64_t n, qad_stream_t stream)

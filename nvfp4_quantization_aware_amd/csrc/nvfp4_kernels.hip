@@ -1,89 +1,162 @@
 // NVFP4 simulated-quantization kernels for gfx950: tensor amax, quantize /
 // dequantize with dynamic or frozen scales, the straight-through copy and the
 // MSE block-scale search.  Page legend and numerical conventions: see
-// include/libqad.h.  All kernels are HBM-streaming (no MFMA: nothing here is a
-// contraction); 16-byte loads and stores, one wave-lane pair per 16-element
-// block for the quantizer.
+// include/libqad.h.  Nothing here is a contraction, so there is no MFMA; every
+// kernel streams HBM with 16-byte non-temporal loads and stores, and every
+// workgroup owns one small contiguous chunk of a tensor (this access pattern
+// measured fastest on MI355X: ~6.2 TB/s copy, ~7.1 TB/s read).
+//
+// Dynamic scales need the tensor amax before any element can be coded.  For
+// tensors whose chunks fit on the chip at once (an MoE expert: 16 MiB), the
+// quantizer reads the tensor ONCE: each workgroup keeps its chunk in
+// registers, publishes the chunk maximum, waits for the tensor's maximum and
+// codes from registers (see "one-pass protocol" below).  Larger tensors take
+// two passes (amax kernel, then quantizer).
 #include "qad_device.h"
 #include "qad_internal.h"
 
 namespace qad {
 namespace {
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 // RN(1/6) in binary32 (0x3E2AAAAB)
 constexpr float kRcp6 = 0x1.555556p-3f;
 // Tensor scales at or above this use the reciprocal division (its validity
 // range); smaller ones take IEEE division everywhere.
 constexpr float kFastMinScale = 0x1p-80f;
-// Units of 8 elements handled per lane per tile of the quantizer.
-constexpr int kUnroll = 4;
-// Workgroups to aim for per launch (16 per compute unit on 256 CUs).
-constexpr int64_t kTargetGroups = 4096;
+constexpr int kQThreads = 256;
+// A bounded wait: after this many wall-clock ticks (20 ms at the 100 MHz
+// counter) a workgroup stops waiting and computes what it waited for itself.
+constexpr uint64_t kWaitTicks = 2000000;
 
-__global__ void fill_u32_kernel(uint32_t* out, int64_t n, uint32_t v)
+__device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
+__device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
+__device__ __forceinline__ void stnt32(void* p, int64_t i, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p) + i); }
+
+// ---- agent-scope atomics used by the one-pass protocol ---------------------
+__device__ __forceinline__ uint32_t a_load(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void a_store(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ uint32_t a_max(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ uint32_t a_add(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Wait until the value returned by a preceding atomic has arrived, i.e. the
+// atomic has been performed, before any later memory operation is issued.
+__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+
+// units of 8 elements per lane in one chunk: 128 bytes of input per lane
+template <bool BF16> struct Chunk {
+    static constexpr int U = BF16 ? 8 : 4;
+    static constexpr int64_t UNITS = (int64_t)kQThreads * U;
+};
+
+// raw input of one unit (8 elements): one 16-byte vector for bf16, two for fp32
+template <bool BF16> struct Raw;
+template <> struct Raw<true> { v4u a; };
+template <> struct Raw<false> { v4u a, b; };
+
+template <bool BF16>
+__device__ __forceinline__ Raw<BF16> load_raw(const void* x, int64_t unit, bool valid)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = v;
+    Raw<BF16> r;
+    if constexpr (BF16) {
+        r.a = valid ? ldnt(x, unit) : v4u{0u, 0u, 0u, 0u};
+    } else {
+        r.a = valid ? ldnt(x, 2 * unit) : v4u{0u, 0u, 0u, 0u};
+        r.b = valid ? ldnt(x, 2 * unit + 1) : v4u{0u, 0u, 0u, 0u};
+    }
+    return r;
 }
 
-// ---------------------------------------------------------------------------
-// Tensor amax ([Lightning] "量化尺度处理策略": dynamic scales start from the
-// max of each tensor, recomputed every step).  The magnitude of a finite
-// binary32 / bf16 value orders like its bit pattern with the sign cleared, so
-// the maximum is an integer max: exact and independent of evaluation order.
-// One atomicMax per workgroup per tensor.
-// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void unpack(const Raw<BF16>& r, float (&e)[8])
+{
+    if constexpr (BF16) {
+        e[0] = bf_lo(r.a.x); e[1] = bf_hi(r.a.x); e[2] = bf_lo(r.a.y); e[3] = bf_hi(r.a.y);
+        e[4] = bf_lo(r.a.z); e[5] = bf_hi(r.a.z); e[6] = bf_lo(r.a.w); e[7] = bf_hi(r.a.w);
+    } else {
+        e[0] = as_f(r.a.x); e[1] = as_f(r.a.y); e[2] = as_f(r.a.z); e[3] = as_f(r.a.w);
+        e[4] = as_f(r.b.x); e[5] = as_f(r.b.y); e[6] = as_f(r.b.z); e[7] = as_f(r.b.w);
+    }
+}
+
+// largest magnitude of a unit as binary32 bits: magnitudes of finite values
+// order like their bit patterns with the sign cleared (integer max: exact and
+// independent of evaluation order)
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
-__device__ __forceinline__ uint32_t absmax_vec(const uint4& v, uint32_t m)
+__device__ __forceinline__ uint32_t unit_absmax(const Raw<BF16>& r)
 {
     if constexpr (BF16) {
-        us2 acc = __builtin_bit_cast(us2, m);
-        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(us2, v.x & 0x7FFF7FFFu));
-        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(us2, v.y & 0x7FFF7FFFu));
-        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(us2, v.z & 0x7FFF7FFFu));
-        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(us2, v.w & 0x7FFF7FFFu));
-        return __builtin_bit_cast(uint32_t, acc);
+        // both bf16 halves of each word at once (packed 16-bit integer max)
+        us2 m = __builtin_elementwise_max(__builtin_bit_cast(us2, r.a.x & 0x7FFF7FFFu),
+                                          __builtin_bit_cast(us2, r.a.y & 0x7FFF7FFFu));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, r.a.z & 0x7FFF7FFFu));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, r.a.w & 0x7FFF7FFFu));
+        return umax((uint32_t)m.x, (uint32_t)m.y) << 16;
     } else {
-        m = umax(m, v.x & 0x7FFFFFFFu);
-        m = umax(m, v.y & 0x7FFFFFFFu);
-        m = umax(m, v.z & 0x7FFFFFFFu);
-        m = umax(m, v.w & 0x7FFFFFFFu);
-        return m;
+        return umax(umax(umax(r.a.x & 0x7FFFFFFFu, r.a.y & 0x7FFFFFFFu), umax(r.a.z & 0x7FFFFFFFu, r.a.w & 0x7FFFFFFFu)),
+                    umax(umax(r.b.x & 0x7FFFFFFFu, r.b.y & 0x7FFFFFFFu), umax(r.b.z & 0x7FFFFFFFu, r.b.w & 0x7FFFFFFFu)));
     }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t vecs, int groups,
-                                                        uint32_t* __restrict__ amax_bits)
+// workgroup maximum (result valid in every thread)
+__device__ __forceinline__ uint32_t group_max(uint32_t m, uint32_t* red)
 {
-    const int b = blockIdx.x / groups, g = blockIdx.x - b * groups;
-    const uint4* xb = x + (int64_t)b * vecs;
-    const int64_t stride = (int64_t)groups * kThreads;
-    int64_t i = (int64_t)g * kThreads + threadIdx.x;
-    uint32_t m = 0;
-    for (; i + 3 * stride < vecs; i += 4 * stride) {
-        const uint4 v0 = xb[i], v1 = xb[i + stride], v2 = xb[i + 2 * stride], v3 = xb[i + 3 * stride];
-        m = absmax_vec<BF16>(v0, m);
-        m = absmax_vec<BF16>(v1, m);
-        m = absmax_vec<BF16>(v2, m);
-        m = absmax_vec<BF16>(v3, m);
-    }
-    for (; i < vecs; i += stride) m = absmax_vec<BF16>(xb[i], m);
-    if constexpr (BF16) m = umax(m & 0xFFFFu, m >> 16) << 16; // bf16 bits -> binary32 bits
     m = wave_max_u32(m);
-    __shared__ uint32_t part[kThreads / 64];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < kThreads / 64; ++w) m = umax(m, part[w]);
-        if (m) atomicMax(amax_bits + b, m);
-    }
+    uint32_t r = red[0];
+    for (int w = 1; w < kQThreads / 64; ++w) r = umax(r, red[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float tensor_scale_of(uint32_t amax_bits)
+{
+    const float amax = as_f(amax_bits);
+    return amax > 0.0f ? amax / 2688.0f : 1.0f;
 }
 
 // ---------------------------------------------------------------------------
-// Per-tensor tables in LDS: effective scale dec(c) * s_g of every E4M3 code c
+// Per-tensor record in the workspace, used by the amax publication.
+//   word 0: tensor amax (binary32 bits), word 1: completed sub-groups
+//   sub-group s (16 consecutive chunks): words 32+32s (max), 33+32s (arrivals)
+//   broadcast slot of chunk j: word 32 + 32*nsub + 16*j (amax | 0x80000000)
+// Every field sits on its own 64- or 128-byte line so that no address sees
+// more than ~16 atomics or one poller.  Records are zeroed before each launch.
+// ---------------------------------------------------------------------------
+struct Record {
+    uint32_t* w;
+    int64_t chunks, nsub;
+    __device__ Record(uint32_t* base, int64_t b, int64_t P)
+        : w(base + b * record_words(P)), chunks(P), nsub((P + 15) / 16) {}
+    __device__ uint32_t* slot(int64_t j) const { return w + 32 + 32 * nsub + 16 * j; }
+};
+
+// Publish chunk j's maximum m (thread 0 only).  Returns true in exactly one
+// chunk: the one whose arrival completes the tensor; record word 0 then holds
+// the tensor amax.  Order is carried by completion: each atomic's returned
+// value is awaited before the next is issued, so an arrival count is only
+// ever observed after the maxima it accounts for have been performed.
+__device__ bool publish_max(const Record& r, int64_t j, uint32_t m)
+{
+    const int64_t s = j / 16;
+    const uint32_t members = (uint32_t)(r.chunks - s * 16 < 16 ? r.chunks - s * 16 : 16);
+    uint32_t* sw = r.w + 32 + 32 * s;
+    completed(a_max(sw, m));
+    const uint32_t k = a_add(sw + 1, 1u);
+    completed(k);
+    if (k != members - 1) return false;
+    const uint32_t sub = a_load(sw);
+    completed(a_max(r.w, sub));
+    const uint32_t k2 = a_add(r.w + 1, 1u);
+    completed(k2);
+    return k2 == (uint32_t)r.nsub - 1;
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor table in LDS: effective scale dec(c) * s_g of every E4M3 code c
 // and its correctly rounded reciprocal (0 for a zero scale).
 // ---------------------------------------------------------------------------
 struct ScaleTable {
@@ -117,124 +190,225 @@ __device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_g, fl
     return e4m3_encode(raw);
 }
 
-// E2M1 magnitude index of x / s (s = 0 gives index 0)
+// x / s correctly rounded, with x's sign bit (s = 0 gives a signed zero)
 template <bool FAST>
-__device__ __forceinline__ uint32_t element_index(float x, float s, float r)
+__device__ __forceinline__ float quotient(float x, float s, float r)
 {
     float q;
     if constexpr (FAST) q = div_rcp(x, s, r);
     else q = s > 0.0f ? x / s : 0.0f;
-    return e2m1_index(q);
+    return __builtin_copysignf(q, x);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void load_unit(const void* x, int64_t unit, bool valid, float (&e)[8])
+// Code one unit (half a block; the lane pair owns the block).  Returns the
+// block's scale code; writes the 8 packed codes (even element in the low
+// nibble) and the 8 bf16 outputs y = bf16(dec(code) * s_eff).
+template <bool FROZEN, bool FAST>
+__device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t frozen_code, const ScaleTable& tab,
+                                                  float s_g, float rcp_g, uint32_t& code, uint32_t (&yw)[4])
 {
-    if constexpr (BF16) {
-        uint4 v = valid ? reinterpret_cast<const uint4*>(x)[unit] : make_uint4(0, 0, 0, 0);
-        e[0] = bf_lo(v.x); e[1] = bf_hi(v.x); e[2] = bf_lo(v.y); e[3] = bf_hi(v.y);
-        e[4] = bf_lo(v.z); e[5] = bf_hi(v.z); e[6] = bf_lo(v.w); e[7] = bf_hi(v.w);
-    } else {
-        const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * unit;
-        uint4 v0 = valid ? p[0] : make_uint4(0, 0, 0, 0);
-        uint4 v1 = valid ? p[1] : make_uint4(0, 0, 0, 0);
-        e[0] = as_f(v0.x); e[1] = as_f(v0.y); e[2] = as_f(v0.z); e[3] = as_f(v0.w);
-        e[4] = as_f(v1.x); e[5] = as_f(v1.y); e[6] = as_f(v1.z); e[7] = as_f(v1.w);
-    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = umax(m, as_u(e[i]) & 0x7FFFFFFFu);
+    m = umax(m, swap_pair(m));
+    uint32_t sb = FROZEN ? frozen_code : block_scale_code<FAST>(as_f(m), s_g, rcp_g);
+    sb &= 127u;
+    const float s = tab.seff[sb], r = tab.rcp[sb];
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quotient<FAST>(e[i], s, r);
+    uint32_t c = 0;
+    c = fp4_encode_pair<0>(c, q[0], q[1]);
+    c = fp4_encode_pair<1>(c, q[2], q[3]);
+    c = fp4_encode_pair<2>(c, q[4], q[5]);
+    c = fp4_encode_pair<3>(c, q[6], q[7]);
+    code = c;
+    float g[8];
+    fp4_decode_pair<0>(c, g[0], g[1]);
+    fp4_decode_pair<1>(c, g[2], g[3]);
+    fp4_decode_pair<2>(c, g[4], g[5]);
+    fp4_decode_pair<3>(c, g[6], g[7]);
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) yw[i >> 1] = pack_bf16x2(g[i] * s, g[i + 1] * s);
+    return sb;
 }
 
-// ---------------------------------------------------------------------------
-// Quantize / dequantize.  A lane owns a "unit" of 8 consecutive elements; the
-// lane pair (2k, 2k+1) owns one 16-element block and exchanges its half-block
-// amax through DPP.  Per element: code = E2M1(x / s_eff) (sign from x),
-// y = bf16(dec(code) * s_eff).
-// ---------------------------------------------------------------------------
-template <bool BF16, bool FROZEN, bool FAST>
-__device__ __forceinline__ void quantize_tensor(const QuantizeArgs& a, int b, int g, int groups,
-                                                const ScaleTable& tab, float s_g)
+enum { MODE_FROZEN = 0, MODE_AMAX = 1, MODE_ONEPASS = 2 };
+
+template <bool BF16, int MODE, bool FAST>
+__device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16> (&raw)[Chunk<BF16>::U],
+                                           int64_t ubase, int64_t u0, int64_t units, const ScaleTable& tab,
+                                           float s_g)
 {
-    const int64_t units = a.elems >> 3;
-    const int64_t ubase = (int64_t)b * units;
     const float rcp_g = 1.0f / s_g;
-    constexpr int64_t kTile = (int64_t)kThreads * kUnroll;
     const int t = threadIdx.x;
-    for (int64_t tile = g; tile * kTile < units; tile += groups) {
-        float e[kUnroll][8];
-        bool valid[kUnroll];
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t u = tile * kTile + k * kThreads + t;
-            valid[k] = u < units;
-            load_unit<BF16>(a.x, ubase + u, valid[k], e[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t u = tile * kTile + k * kThreads + t;
-            uint32_t m = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) m = umax(m, as_u(e[k][i]) & 0x7FFFFFFFu);
-            m = umax(m, swap_pair(m));
-            uint32_t sb;
-            if constexpr (FROZEN) sb = valid[k] ? a.scales_in[(ubase + u) >> 1] : 0u;
-            else sb = block_scale_code<FAST>(as_f(m), s_g, rcp_g);
-            sb &= 127u;
-            const float s = tab.seff[sb], r = tab.rcp[sb];
-            uint32_t code = 0, yw[4];
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const uint32_t i0 = element_index<FAST>(e[k][i], s, r);
-                const uint32_t i1 = element_index<FAST>(e[k][i + 1], s, r);
-                code |= (i0 | ((as_u(e[k][i]) >> 31) << 3)) << (4 * i);
-                code |= (i1 | ((as_u(e[k][i + 1]) >> 31) << 3)) << (4 * i + 4);
-                const float y0 = __builtin_copysignf(e2m1_value(i0) * s, e[k][i]);
-                const float y1 = __builtin_copysignf(e2m1_value(i1) * s, e[k][i + 1]);
-                yw[i >> 1] = pack_bf16x2(y0, y1);
-            }
-            if (valid[k]) {
-                if (a.y) reinterpret_cast<uint4*>(a.y)[ubase + u] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-                if (a.codes) reinterpret_cast<uint32_t*>(a.codes)[ubase + u] = code;
-                if (a.scales_out && !(t & 1)) a.scales_out[(ubase + u) >> 1] = (uint8_t)sb;
-            }
+    for (int k = 0; k < Chunk<BF16>::U; ++k) {
+        const int64_t u = u0 + k * kQThreads + t;
+        const bool valid = u < units;
+        float e[8];
+        unpack<BF16>(raw[k], e);
+        uint32_t frozen_code = 0;
+        if constexpr (MODE == MODE_FROZEN) frozen_code = valid ? a.scales_in[(ubase + u) >> 1] : 0u;
+        uint32_t code, yw[4];
+        const uint32_t sb = quantize_unit<MODE == MODE_FROZEN, FAST>(e, frozen_code, tab, s_g, rcp_g, code, yw);
+        if (valid) {
+            if (a.y) stnt(a.y, ubase + u, v4u{yw[0], yw[1], yw[2], yw[3]});
+            if (a.codes) stnt32(a.codes, ubase + u, code);
+            if (a.scales_out && !(t & 1)) a.scales_out[(ubase + u) >> 1] = (uint8_t)sb;
         }
     }
 }
 
-template <bool BF16, bool FROZEN>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int groups)
+// tensor amax by a full scan of tensor b by one workgroup (the bounded wait's
+// fallback; exact, so its result equals the published one)
+template <bool BF16>
+__device__ uint32_t scan_amax(const void* x, int64_t ubase, int64_t units, uint32_t* red)
 {
+    uint32_t m = 0;
+    for (int64_t u = threadIdx.x; u < units; u += kQThreads) m = umax(m, unit_absmax<BF16>(load_raw<BF16>(x, ubase + u, true)));
+    return group_max(m, red);
+}
+
+// ---------------------------------------------------------------------------
+// The quantizer.  One workgroup per chunk of Chunk::UNITS units (32 KiB of
+// bf16 / fp32 input); chunk c is chunk j = c % P of tensor b = c / P.  A lane
+// holds units u0 + k*256 + lane, so lanes 2i and 2i+1 hold the two halves of a
+// block.  s_g comes from the frozen input (MODE_FROZEN), from the amax kernel
+// (MODE_AMAX) or from the one-pass protocol (MODE_ONEPASS):
+//   1. every workgroup reduces its chunk's maximum and publishes it
+//      (publish_max); the workgroup completing the tensor writes the amax
+//      into every chunk's broadcast slot;
+//   2. each workgroup waits on its own slot, then codes from registers.
+// Progress: workgroups are dispatched in order on each XCD and the host only
+// takes this path when at most half of the resident workgroups are needed to
+// hold one tensor, so the chunks a waiting workgroup depends on are always
+// resident or finished.  The wait is nevertheless bounded; on time-out the
+// workgroup computes the amax itself (exact, so the result is unchanged).
+// ---------------------------------------------------------------------------
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int64_t P, uint32_t* ws)
+{
+    using CH = Chunk<BF16>;
     __shared__ ScaleTable tab;
-    const int b = blockIdx.x / groups, g = blockIdx.x - b * groups;
+    __shared__ uint32_t red[kQThreads / 64];
+    __shared__ uint32_t sh_bcast, sh_amax;
+    const int64_t c = blockIdx.x;
+    const int64_t b = c / P, j = c - b * P;
+    const int64_t units = a.elems >> 3;
+    const int64_t ubase = b * units;
+    const int64_t u0 = j * CH::UNITS;
+    const int t = threadIdx.x;
+
+    Raw<BF16> raw[CH::U];
+#pragma unroll
+    for (int k = 0; k < CH::U; ++k) {
+        const int64_t u = u0 + k * kQThreads + t;
+        raw[k] = load_raw<BF16>(a.x, ubase + u, u < units);
+    }
+
     float s_g;
-    if constexpr (FROZEN) {
+    if constexpr (MODE == MODE_FROZEN) {
         s_g = a.tscale_in[b];
+    } else if constexpr (MODE == MODE_AMAX) {
+        s_g = tensor_scale_of(Record(ws, b, P).w[0]); // written by amax_kernel (same chunking)
     } else {
-        const float amax = as_f(a.amax_bits[b]);
-        s_g = amax > 0.0f ? amax / 2688.0f : 1.0f;
+        const Record rec(ws, b, P);
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < CH::U; ++k) m = umax(m, unit_absmax<BF16>(raw[k]));
+        m = group_max(m, red);
+        if (t == 0) sh_bcast = publish_max(rec, j, m) ? (a_load(rec.w) | 0x80000000u) : 0u;
+        __syncthreads();
+        const uint32_t bc = sh_bcast;
+        if (bc)
+            for (int64_t i = t; i < P; i += kQThreads) a_store(rec.slot(i), bc);
+        if (t == 0) {
+            const uint64_t t0 = wall_clock64();
+            uint32_t w;
+            while (!((w = a_load(rec.slot(j))) & 0x80000000u)) {
+                __builtin_amdgcn_s_sleep(8);
+                if (wall_clock64() - t0 > kWaitTicks) break;
+            }
+            sh_amax = w;
+        }
+        __syncthreads();
+        uint32_t am = sh_amax;
+        if (!(am & 0x80000000u)) am = scan_amax<BF16>(a.x, ubase, units, red); // timed out
+        s_g = tensor_scale_of(am & 0x7FFFFFFFu);
     }
     build_table(tab, s_g);
-    if (g == 0 && threadIdx.x == 0 && a.tscale_out) a.tscale_out[b] = s_g;
+    if (j == 0 && t == 0 && a.tscale_out) a.tscale_out[b] = s_g;
     __syncthreads();
-    if (s_g >= kFastMinScale) quantize_tensor<BF16, FROZEN, true>(a, b, g, groups, tab, s_g);
-    else quantize_tensor<BF16, FROZEN, false>(a, b, g, groups, tab, s_g);
+    if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true>(a, raw, ubase, u0, units, tab, s_g);
+    else code_chunk<BF16, MODE, false>(a, raw, ubase, u0, units, tab, s_g);
 }
 
 // ---------------------------------------------------------------------------
-// Straight-through backward: a 16-byte vector copy.
+// Tensor amax for the two-pass path and nvfp4_amax: one workgroup per chunk,
+// hierarchical publication into the tensor record (word 0 ends as the amax).
+// `vecs` counts 16-byte vectors per tensor.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                        int64_t vecs, const uint16_t* __restrict__ src_tail,
-                                                        uint16_t* __restrict__ dst_tail, int tail_halves)
+template <bool BF16>
+__global__ __launch_bounds__(kQThreads) void amax_kernel(const void* x, int64_t vecs, int64_t P, uint32_t* ws)
 {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + 3 * stride < vecs; i += 4 * stride) {
-        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-        dst[i] = v0;
-        dst[i + stride] = v1;
-        dst[i + 2 * stride] = v2;
-        dst[i + 3 * stride] = v3;
+    __shared__ uint32_t red[kQThreads / 64];
+    constexpr int64_t kVecs = (int64_t)kQThreads * 8; // 32 KiB per chunk
+    const int64_t c = blockIdx.x, b = c / P, j = c - b * P;
+    const int64_t v0 = j * kVecs, base = b * vecs;
+    uint32_t m = 0;
+    v4u v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int64_t i = v0 + k * kQThreads + threadIdx.x;
+        v[k] = i < vecs ? ldnt(x, base + i) : v4u{0u, 0u, 0u, 0u};
     }
-    for (; i < vecs; i += stride) dst[i] = src[i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if constexpr (BF16) {
+            Raw<true> r{v[k]};
+            m = umax(m, unit_absmax<true>(r));
+        } else {
+            m = umax(m, umax(umax(v[k].x & 0x7FFFFFFFu, v[k].y & 0x7FFFFFFFu), umax(v[k].z & 0x7FFFFFFFu, v[k].w & 0x7FFFFFFFu)));
+        }
+    }
+    m = group_max(m, red);
+    if (threadIdx.x == 0) publish_max(Record(ws, b, P), j, m);
+}
+
+// record word 0 of every tensor -> out[b] (nvfp4_amax result)
+__global__ void amax_out_kernel(const uint32_t* ws, int64_t B, int64_t P, uint32_t* out)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) out[b] = ws[b * record_words(P)];
+}
+
+__global__ void fill_u32_kernel(uint32_t* out, int64_t n, uint32_t v)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Straight-through backward: chunked 16-byte non-temporal copy (16 KiB per
+// workgroup) plus a tail of up to seven 16-bit halves.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kQThreads) void copy_kernel(const void* __restrict__ src, void* __restrict__ dst,
+                                                         int64_t vecs, const uint16_t* __restrict__ src_tail,
+                                                         uint16_t* __restrict__ dst_tail, int tail_halves)
+{
+    const int64_t v0 = (int64_t)blockIdx.x * (kQThreads * 4);
+    v4u v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t i = v0 + k * kQThreads + threadIdx.x;
+        if (i < vecs) v[k] = ldnt(src, i);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t i = v0 + k * kQThreads + threadIdx.x;
+        if (i < vecs) stnt(dst, i, v[k]);
+    }
     if (blockIdx.x == 0 && threadIdx.x < tail_halves) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
 }
 
@@ -250,63 +424,76 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict_
 template <bool FAST>
 __device__ __forceinline__ float block_error(const float (&e)[16], float s, float r)
 {
+    // squared error of the block under effective scale s, summed in element
+    // order; magnitudes only (|x - dec * s| is symmetric in the sign)
+    float q[16], g[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = quotient<FAST>(__builtin_fabsf(e[j]), s, r);
+#pragma unroll
+    for (int j = 0; j < 16; j += 8) {
+        uint32_t c = 0;
+        c = fp4_encode_pair<0>(c, q[j], q[j + 1]);
+        c = fp4_encode_pair<1>(c, q[j + 2], q[j + 3]);
+        c = fp4_encode_pair<2>(c, q[j + 4], q[j + 5]);
+        c = fp4_encode_pair<3>(c, q[j + 6], q[j + 7]);
+        fp4_decode_pair<0>(c, g[j], g[j + 1]);
+        fp4_decode_pair<1>(c, g[j + 2], g[j + 3]);
+        fp4_decode_pair<2>(c, g[j + 4], g[j + 5]);
+        fp4_decode_pair<3>(c, g[j + 6], g[j + 7]);
+    }
     float err = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const uint32_t idx = element_index<FAST>(e[j], s, r);
-        const float d = __builtin_fabsf(e[j]) - e2m1_value(idx) * s;
+        const float d = __builtin_fabsf(e[j]) - g[j] * s;
         err = err + d * d;
     }
     return err;
 }
 
 template <bool BF16, bool FAST>
-__device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int b, int g, int groups,
+__device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int64_t b, int64_t g, int64_t groups,
                                                  const ScaleTable& tab, float s_g)
 {
     const int64_t nblk = a.elems >> 4;
     const float rcp_g = 1.0f / s_g;
-    const int64_t stride = (int64_t)groups * kThreads;
-    for (int64_t blk = (int64_t)g * kThreads + threadIdx.x; blk < nblk; blk += stride) {
-        const int64_t gb = (int64_t)b * nblk + blk;
+    const int64_t stride = groups * kQThreads;
+    for (int64_t blk = g * kQThreads + threadIdx.x; blk < nblk; blk += stride) {
+        const int64_t gb = b * nblk + blk;
         float e[16];
         if constexpr (BF16) {
-            const uint4* p = reinterpret_cast<const uint4*>(a.w) + 2 * gb;
-            const uint4 v0 = p[0], v1 = p[1];
+            const v4u v0 = ldnt(a.w, 2 * gb), v1 = ldnt(a.w, 2 * gb + 1);
             const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) { e[2 * j] = bf_lo(w[j]); e[2 * j + 1] = bf_hi(w[j]); }
+            for (int q = 0; q < 8; ++q) { e[2 * q] = bf_lo(w[q]); e[2 * q + 1] = bf_hi(w[q]); }
         } else {
-            const uint4* p = reinterpret_cast<const uint4*>(a.w) + 4 * gb;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 v = p[j];
-                e[4 * j] = as_f(v.x); e[4 * j + 1] = as_f(v.y); e[4 * j + 2] = as_f(v.z); e[4 * j + 3] = as_f(v.w);
+            for (int q = 0; q < 4; ++q) {
+                const v4u v = ldnt(a.w, 4 * gb + q);
+                e[4 * q] = as_f(v.x); e[4 * q + 1] = as_f(v.y); e[4 * q + 2] = as_f(v.z); e[4 * q + 3] = as_f(v.w);
             }
         }
         uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) m = umax(m, as_u(e[j]) & 0x7FFFFFFFu);
+        for (int q = 0; q < 16; ++q) m = umax(m, as_u(e[q]) & 0x7FFFFFFFu);
         const float amax_b = as_f(m);
         const uint32_t c_lo = block_scale_code<FAST>(amax_b * a.k_lo, s_g, rcp_g);
         const uint32_t c_hi = block_scale_code<FAST>(amax_b * a.k_hi, s_g, rcp_g);
         uint32_t best = c_lo;
         float best_err = __builtin_inff();
-        for (uint32_t c = c_lo; c <= c_hi; ++c) {
-            const float err = block_error<FAST>(e, tab.seff[c], tab.rcp[c]);
-            if (err < best_err) { best_err = err; best = c; }
+        for (uint32_t cc = c_lo; cc <= c_hi; ++cc) {
+            const float err = block_error<FAST>(e, tab.seff[cc], tab.rcp[cc]);
+            if (err < best_err) { best_err = err; best = cc; }
         }
         a.scales_out[gb] = (uint8_t)best;
     }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void mse_kernel(MseArgs a, int groups)
+__global__ __launch_bounds__(kQThreads) void mse_kernel(MseArgs a, int64_t groups, int64_t P, const uint32_t* ws)
 {
     __shared__ ScaleTable tab;
-    const int b = blockIdx.x / groups, g = blockIdx.x - b * groups;
-    const float amax = as_f(a.amax_bits[b]);
-    const float s_g = amax > 0.0f ? amax / 2688.0f : 1.0f;
+    const int64_t b = blockIdx.x / groups, g = blockIdx.x - b * groups;
+    const float s_g = tensor_scale_of(ws[b * record_words(P)]);
     build_table(tab, s_g);
     if (g == 0 && threadIdx.x == 0) a.tscale_out[b] = s_g;
     __syncthreads();
@@ -314,50 +501,98 @@ __global__ __launch_bounds__(kThreads) void mse_kernel(MseArgs a, int groups)
     else calibrate_tensor<BF16, false>(a, b, g, groups, tab, s_g);
 }
 
-int groups_for(int64_t B, int64_t work_items, int64_t per_group)
+// resident workgroups of a kernel on the current device (cached per device)
+template <bool BF16>
+int64_t resident_groups()
 {
-    int64_t need = (work_items + per_group - 1) / per_group;
-    int64_t want = (kTargetGroups + B - 1) / B;
-    int64_t g = need < want ? need : want;
-    if (g < 1) g = 1;
-    if (g * B > 0x7FFFFFFFll) g = 0x7FFFFFFFll / B;
-    return (int)g;
+    static int64_t cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int64_t v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v) return v;
+    auto kernel = quantize_kernel<BF16, MODE_ONEPASS>;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kQThreads, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    v = (int64_t)per_cu * cus;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    return v;
 }
 
 } // namespace
 
+int64_t quantize_chunks(bool bf16, int64_t elems)
+{
+    const int64_t units = elems >> 3;
+    const int64_t per = bf16 ? Chunk<true>::UNITS : Chunk<false>::UNITS;
+    return (units + per - 1) / per;
+}
+
+int64_t amax_chunks(int64_t bytes_per_tensor)
+{
+    const int64_t vecs = bytes_per_tensor / 16;
+    const int64_t per = (int64_t)kQThreads * 8; // 32 KiB, as the quantizer's chunk
+    return (vecs + per - 1) / per;
+}
+
 hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t v, hipStream_t stream)
 {
     if (n <= 0) return hipSuccess;
-    int64_t grid = (n + kThreads - 1) / kThreads;
-    if (grid > 1024) grid = 1024;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, out, n, v);
+    int64_t grid = (n + kQThreads - 1) / kQThreads;
+    if (grid > 4096) grid = 4096;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream, out, n, v);
     return hipGetLastError();
 }
 
-hipError_t launch_amax(const void* x, bool bf16, int64_t B, int64_t elems, uint32_t* amax_bits, hipStream_t stream)
+hipError_t launch_amax(const void* x, bool bf16, int64_t B, int64_t elems, uint32_t* ws, hipStream_t stream)
 {
-    const int64_t vecs = elems * (bf16 ? 2 : 4) / 16;
-    if (B <= 0 || vecs <= 0) return hipSuccess;
-    const int groups = groups_for(B, vecs, (int64_t)kThreads * 16);
-    const dim3 grid((unsigned)(groups * B));
-    if (bf16) hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kThreads), 0, stream,
-                                 (const uint4*)x, vecs, groups, amax_bits);
-    else hipLaunchKernelGGL(amax_kernel<false>, grid, dim3(kThreads), 0, stream,
-                            (const uint4*)x, vecs, groups, amax_bits);
+    const int64_t bytes = elems * (bf16 ? 2 : 4);
+    const int64_t P = amax_chunks(bytes);
+    if (B <= 0 || P <= 0) return hipSuccess;
+    hipError_t e = launch_fill_u32(ws, B * record_words(P), 0u, stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(B * P));
+    if (bf16) hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kQThreads), 0, stream, x, bytes / 16, P, ws);
+    else hipLaunchKernelGGL(amax_kernel<false>, grid, dim3(kQThreads), 0, stream, x, bytes / 16, P, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream)
+hipError_t launch_amax_out(const uint32_t* ws, int64_t B, int64_t elems, bool bf16, uint32_t* out, hipStream_t stream)
+{
+    const int64_t P = amax_chunks(elems * (bf16 ? 2 : 4));
+    if (B <= 0) return hipSuccess;
+    if (P <= 0) return launch_fill_u32(out, B, 0u, stream);
+    hipLaunchKernelGGL(amax_out_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, ws, B, P, out);
+    return hipGetLastError();
+}
+
+bool quantize_one_pass_ok(bool bf16, int64_t B, int64_t elems)
+{
+    const int64_t P = quantize_chunks(bf16, elems);
+    const int64_t resident = bf16 ? resident_groups<true>() : resident_groups<false>();
+    (void)B;
+    return P >= 1 && resident > 0 && P <= resident / 2;
+}
+
+hipError_t launch_quantize(const QuantizeArgs& a, int mode, uint32_t* ws, hipStream_t stream)
 {
     if (a.B <= 0 || a.elems <= 0) return hipSuccess;
-    const int groups = groups_for(a.B, a.elems >> 3, (int64_t)kThreads * kUnroll);
-    const dim3 grid((unsigned)(groups * a.B));
-    const bool frozen = a.scales_in != nullptr;
-    if (a.bf16 && frozen) hipLaunchKernelGGL((quantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, a, groups);
-    else if (a.bf16) hipLaunchKernelGGL((quantize_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, groups);
-    else if (frozen) hipLaunchKernelGGL((quantize_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, groups);
-    else hipLaunchKernelGGL((quantize_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, groups);
+    // the amax kernel and the quantizer cut a tensor into the same 32 KiB chunks
+    const int64_t P = quantize_chunks(a.bf16, a.elems);
+    if (mode == MODE_ONEPASS) {
+        hipError_t e = launch_fill_u32(ws, a.B * record_words(P), 0u, stream);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(a.B * P)), block(kQThreads);
+#define QK(BF, M) hipLaunchKernelGGL((quantize_kernel<BF, M>), grid, block, 0, stream, a, P, ws)
+    if (mode == MODE_ONEPASS) {
+        if (a.bf16) QK(true, MODE_ONEPASS); else QK(false, MODE_ONEPASS);
+    } else if (mode == MODE_AMAX) {
+        if (a.bf16) QK(true, MODE_AMAX); else QK(false, MODE_AMAX);
+    } else {
+        if (a.bf16) QK(true, MODE_FROZEN); else QK(false, MODE_FROZEN);
+    }
+#undef QK
     return hipGetLastError();
 }
 
@@ -366,23 +601,28 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
     const int64_t vecs = bytes / 16;
     const int tail_halves = (int)((bytes - vecs * 16) / 2);
     if (vecs == 0 && tail_halves == 0) return hipSuccess;
-    int64_t grid = (vecs + (int64_t)kThreads * 4 - 1) / ((int64_t)kThreads * 4);
-    if (grid > kTargetGroups) grid = kTargetGroups;
+    int64_t grid = (vecs + kQThreads * 4 - 1) / (kQThreads * 4);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       (const uint4*)src, (uint4*)dst, vecs,
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream, src, dst, vecs,
                        (const uint16_t*)((const char*)src + vecs * 16), (uint16_t*)((char*)dst + vecs * 16),
                        tail_halves);
     return hipGetLastError();
 }
 
-hipError_t launch_mse_calibrate(const MseArgs& a, hipStream_t stream)
+hipError_t launch_mse_calibrate(const MseArgs& a, uint32_t* ws, hipStream_t stream)
 {
     if (a.B <= 0 || a.elems <= 0) return hipSuccess;
-    const int groups = groups_for(a.B, a.elems >> 4, kThreads);
+    hipError_t e = launch_amax(a.w, a.bf16, a.B, a.elems, ws, stream);
+    if (e != hipSuccess) return e;
+    const int64_t P = amax_chunks(a.elems * (a.bf16 ? 2 : 4));
+    const int64_t nblk = a.elems >> 4;
+    int64_t groups = (nblk + kQThreads - 1) / kQThreads;
+    const int64_t want = (16384 + a.B - 1) / a.B;
+    if (groups > want) groups = want;
+    if (groups < 1) groups = 1;
     const dim3 grid((unsigned)(groups * a.B));
-    if (a.bf16) hipLaunchKernelGGL(mse_kernel<true>, grid, dim3(kThreads), 0, stream, a, groups);
-    else hipLaunchKernelGGL(mse_kernel<false>, grid, dim3(kThreads), 0, stream, a, groups);
+    if (a.bf16) hipLaunchKernelGGL(mse_kernel<true>, grid, dim3(kQThreads), 0, stream, a, groups, P, ws);
+    else hipLaunchKernelGGL(mse_kernel<false>, grid, dim3(kQThreads), 0, stream, a, groups, P, ws);
     return hipGetLastError();
 }
 

@@ -50,31 +50,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c)
 }
 
 // ---------------------------------------------------------------------------
-// E2M1 magnitude index of a quotient q (4-bit float, [Nano] "NVFP4-Format und
-// warum es wichtig ist?"; grid {0,.5,1,1.5,2,3,4,6}, nearest, ties to the
-// even index, saturating).  |q| < 1: the grid step is 0.5, so the index is
-// 2|q| rounded to nearest even.  |q| >= 1: the grid is binary32 with one
-// mantissa bit, so round the mantissa to 1 bit in the integer domain; the
-// index is then (biased exponent * 2 + mantissa bit) - 252, capped at 7
-// (which also maps infinities and NaNs to 7).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e2m1_index(float q)
-{
-    const float a = __builtin_fabsf(q);
-    const uint32_t u = as_u(a);
-    const uint32_t t = u + 0x1FFFFFu + ((u >> 22) & 1u);
-    const uint32_t hi = (t >> 22) - 252u;
-    const uint32_t lo = (uint32_t)__builtin_rintf(a + a);
-    return a < 1.0f ? lo : (hi < 7u ? hi : 7u);
-}
-
-// magnitude of grid index i (0..7)
-__device__ __forceinline__ float e2m1_value(uint32_t i)
-{
-    return i < 2u ? (float)i * 0.5f : as_f((((i >> 1) + 126u) << 23) | ((i & 1u) << 22));
-}
-
-// ---------------------------------------------------------------------------
 // x / s correctly rounded, with r = RN(1/s) precomputed once per divisor:
 // q0 = RN(x r) is within two ulps; one correction q1 = q0 + RN(x - s q0) r is
 // faithful; a second correction is then the correctly rounded quotient
@@ -89,6 +64,28 @@ __device__ __forceinline__ float div_rcp(float x, float s, float r)
     const float q1 = __builtin_fmaf(e0, r, q0);
     const float e1 = __builtin_fmaf(-s, q1, x);
     return __builtin_fmaf(e1, r, q1);
+}
+
+// ---------------------------------------------------------------------------
+// gfx950 FP4 conversions with unit scale.  Encoding rounds to the nearest
+// E2M1 value with ties to the even code and saturates, taking the code's sign
+// from the input's sign bit: checked equal to that definition on every
+// non-NaN binary32 input.  SEL picks the byte of `word` receiving the pair
+// (first value in the low nibble).  Decoding gives the exact signed grid
+// values of the pair in byte SEL.
+// ---------------------------------------------------------------------------
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_encode_pair(uint32_t word, float lo, float hi)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lo, hi, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ void fp4_decode_pair(uint32_t word, float& lo, float& hi)
+{
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+    lo = v[0];
+    hi = v[1];
 }
 
 // swap with the neighbouring lane (lane ^ 1) through DPP quad_perm(1,0,3,2)

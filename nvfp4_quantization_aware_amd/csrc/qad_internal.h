@@ -9,16 +9,27 @@
 
 namespace qad {
 
-constexpr int kThreads = 256;
-
 // out[i] = v for i < n (graph-safe replacement for a memset)
 hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t v, hipStream_t stream);
 
-// amax of B tensors of `elems` elements (elems * esize % 16 == 0); result as
-// binary32 bit patterns, max-accumulated into amax_bits[B] (which must be
-// zero or a lower bound beforehand).
-hipError_t launch_amax(const void* x, bool bf16, int64_t B, int64_t elems, uint32_t* amax_bits,
-                       hipStream_t stream);
+// Words of one tensor's record in the workspace for a tensor cut into P
+// chunks (amax publication, sub-group counters, broadcast slots).
+__host__ __device__ inline int64_t record_words(int64_t P)
+{
+    const int64_t w = 32 + 32 * ((P + 15) / 16) + 16 * P;
+    return (w + 31) & ~(int64_t)31;
+}
+// chunks (32 KiB of input) per tensor of `elems` elements
+int64_t quantize_chunks(bool bf16, int64_t elems);
+int64_t amax_chunks(int64_t bytes_per_tensor);
+
+// Tensor amax of B tensors of `elems` elements (elems * esize % 16 == 0) into
+// the tensor records at ws (zeroes them first); word 0 of record b ends as
+// the amax of tensor b (binary32 bits).
+hipError_t launch_amax(const void* x, bool bf16, int64_t B, int64_t elems, uint32_t* ws, hipStream_t stream);
+// copy the amax of every record to out[B]
+hipError_t launch_amax_out(const uint32_t* ws, int64_t B, int64_t elems, bool bf16, uint32_t* out,
+                           hipStream_t stream);
 
 struct QuantizeArgs {
     const void* x;
@@ -27,13 +38,17 @@ struct QuantizeArgs {
     int64_t elems;             // R * C per tensor, multiple of 16
     const uint8_t* scales_in;  // frozen block scales or null (dynamic)
     const float* tscale_in;    // frozen tensor scales
-    const uint32_t* amax_bits; // dynamic: per-tensor amax from launch_amax
     uint8_t* codes;
     uint8_t* scales_out;
     float* tscale_out;
     uint16_t* y;
 };
-hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t stream);
+enum { QUANT_FROZEN = 0, QUANT_AMAX_GIVEN = 1, QUANT_ONE_PASS = 2 };
+// whether every chunk of one tensor can be resident at once with room to spare
+bool quantize_one_pass_ok(bool bf16, int64_t B, int64_t elems);
+// QUANT_AMAX_GIVEN expects launch_amax's records in ws; QUANT_ONE_PASS
+// zeroes and uses them itself; QUANT_FROZEN ignores ws.
+hipError_t launch_quantize(const QuantizeArgs& a, int mode, uint32_t* ws, hipStream_t stream);
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
@@ -43,11 +58,11 @@ struct MseArgs {
     int64_t B;
     int64_t elems;
     float k_lo, k_hi;          // first and last candidate multipliers
-    const uint32_t* amax_bits;
     uint8_t* scales_out;
     float* tscale_out;
 };
-hipError_t launch_mse_calibrate(const MseArgs& a, hipStream_t stream);
+// amax records in ws, then the search
+hipError_t launch_mse_calibrate(const MseArgs& a, uint32_t* ws, hipStream_t stream);
 
 struct KlArgs {
     const void* teacher;
@@ -55,11 +70,13 @@ struct KlArgs {
     bool bf16_in;
     int64_t tokens, vocab;
     float temperature, grad_scale;
-    float* row_loss;           // [tokens], never null (workspace if needed)
+    float* row_loss;           // [tokens], never null (start of the workspace if the caller has none)
     float* loss_out;
     void* grad;                // null: forward only
     bool grad_bf16;
 };
-hipError_t launch_kl(const KlArgs& a, hipStream_t stream);
+// scratch of launch_kl: per-row losses, then per-row exchange records
+size_t kl_workspace_bytes(int64_t tokens, int64_t vocab);
+hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);
 
 } // namespace qad

@@ -56,18 +56,34 @@ def test_status_strings_and_version(L):
     assert L.qad_status_string(99) == b"unknown qad_status_t"
 
 
+def _record_bytes(B, rc):
+    # per tensor: 32-word header, one 32-word line per 16 chunks, one 16-word
+    # slot per chunk; chunks of 8192 fp32 elements (the most numerous case)
+    P = -(-rc // 8192)
+    words = 32 + 32 * (-(-P // 16)) + 16 * P
+    words = (words + 31) // 32 * 32
+    return -(-(B * words * 4) // 256) * 256
+
+
 def test_workspace_sizes(L):
-    assert L.qad_workspace_bytes(q.QAD_OP_AMAX, 128, 2048, 4096) == 0
-    assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 128, 2048, 4096) == 512
-    assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 1, 1, 16) == 256
-    assert L.qad_workspace_bytes(q.QAD_OP_MSE_CALIBRATE, 1, 8192, 8192) == 256
-    assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, 8192, 131072) == 32768
+    for op in (q.QAD_OP_AMAX, q.QAD_OP_QUANTIZE, q.QAD_OP_MSE_CALIBRATE):
+        for B, R, C_ in ((128, 2048, 4096), (1, 1, 16), (1, 8192, 8192), (3, 7, 48)):
+            assert L.qad_workspace_bytes(op, B, R, C_) == _record_bytes(B, R * C_)
+    # KL: per-row losses, then one exchange record per row when a row spans
+    # several segments of 16384 logits (32 header words + 8 per segment)
+    for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20)):
+        W = -(-vocab // 16384)
+        rec = ((32 + 8 * W + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
+        expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
+        assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
     assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
+    for op in range(4):
+        assert L.qad_workspace_bytes(op, 1, 1, 16) % 256 == 0
 
 
 def test_quantize_rejects(L):
     f = L.nvfp4_quantize
-    ws = 1024
+    ws = 1 << 16
     # C not a multiple of 16
     assert f(P, 1, 1, 4, 24, None, None, None, None, None, P * 2, P * 3, ws, None) == SHAPE
     # negative size
@@ -87,6 +103,7 @@ def test_quantize_rejects(L):
     # workspace missing / too small (dynamic mode needs it)
     assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2, None, 0, None) == WS
     assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2, P * 3, 8, None) == WS
+    assert f(P, 1, 1, 4, 32, None, None, None, None, None, P * 2, P * 3 + 16, ws, None) == ALIGN
     # output overlapping the input
     assert f(P, 1, 1, 4, 32, None, None, None, None, None, P + 16, P * 3, ws, None) == INVALID
     # empty tensor: nothing to do
@@ -94,7 +111,7 @@ def test_quantize_rejects(L):
 
 
 def test_qdq_fwd_bwd_reject(L):
-    assert L.nvfp4_qdq_fwd(P, 1, 1, 4, 32, None, None, None, P * 3, 1024, None) == INVALID
+    assert L.nvfp4_qdq_fwd(P, 1, 1, 4, 32, None, None, None, P * 3, 1 << 16, None) == INVALID
     assert L.nvfp4_qdq_bwd(P, P * 2, 5, 100, None) == DTYPE
     assert L.nvfp4_qdq_bwd(P, P * 2, 1, -3, None) == SHAPE
     assert L.nvfp4_qdq_bwd(None, P * 2, 1, 100, None) == INVALID
@@ -106,30 +123,35 @@ def test_qdq_fwd_bwd_reject(L):
 
 
 def test_amax_rejects(L):
-    assert L.nvfp4_amax(P, 1, 1, 4, 12, P * 2, None) == SHAPE   # 24-byte rows
-    assert L.nvfp4_amax(P, 2, 1, 4, 16, P * 2, None) == DTYPE
-    assert L.nvfp4_amax(P, 1, 1, 4, 16, None, None) == INVALID
-    assert L.nvfp4_amax(P_ODD, 1, 1, 4, 16, P * 2, None) == ALIGN
-    assert L.nvfp4_amax(P, 1, 0, 4, 16, None, None) == OK
+    ws = 1 << 16
+    assert L.nvfp4_amax(P, 1, 1, 4, 12, P * 2, P * 4, ws, None) == SHAPE   # 24-byte rows
+    assert L.nvfp4_amax(P, 2, 1, 4, 16, P * 2, P * 4, ws, None) == DTYPE
+    assert L.nvfp4_amax(P, 1, 1, 4, 16, None, P * 4, ws, None) == INVALID
+    assert L.nvfp4_amax(P_ODD, 1, 1, 4, 16, P * 2, P * 4, ws, None) == ALIGN
+    assert L.nvfp4_amax(P, 1, 1, 4, 16, P * 2, None, 0, None) == WS
+    assert L.nvfp4_amax(P, 1, 1, 4, 16, P * 2, P * 4, 16, None) == WS
+    assert L.nvfp4_amax(P, 1, 1, 4, 16, P * 2, P * 4 + 64, ws, None) == ALIGN
+    assert L.nvfp4_amax(P, 1, 0, 4, 16, None, None, 0, None) == OK
 
 
 def test_mse_rejects(L):
     f = L.nvfp4_mse_calibrate
-    args = lambda n, lo, hi: (P, 1, 1, 4, 32, n, lo, hi, P * 2, P * 3, P * 4, 1024, None)
+    args = lambda n, lo, hi: (P, 1, 1, 4, 32, n, lo, hi, P * 2, P * 3, P * 4, 1 << 16, None)
     assert f(*args(0, 0.5, 1.0)) == INVALID
     assert f(*args(64, 0.0, 1.0)) == INVALID
     assert f(*args(64, 0.8, 0.5)) == INVALID
     assert f(*args(4, 0.5, 1.0)) == INVALID          # step 1/6 > 0.5/16: could skip E4M3 codes
     assert f(*args(64, 0.5, float("inf"))) == INVALID
-    assert f(P, 1, 1, 4, 24, 64, 0.5, 1.0, P * 2, P * 3, P * 4, 1024, None) == SHAPE
-    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, None, P * 3, P * 4, 1024, None) == INVALID
+    assert f(P, 1, 1, 4, 24, 64, 0.5, 1.0, P * 2, P * 3, P * 4, 1 << 16, None) == SHAPE
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, None, P * 3, P * 4, 1 << 16, None) == INVALID
     assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3, None, 0, None) == WS
-    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3 + 2, P * 4, 1024, None) == ALIGN
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3 + 2, P * 4, 1 << 16, None) == ALIGN
+    assert f(P, 1, 1, 4, 32, 64, 0.5, 1.0, P * 2, P * 3, P * 4 + 32, 1 << 16, None) == ALIGN
 
 
 def test_kl_rejects(L):
     f = L.qad_kl_fwd_bwd
-    good = [P, P * 2, 1, 4, 64, 1.0, 0.25, P * 3, None, P * 4, 1, P * 5, 1024, None]
+    good = [P, P * 2, 1, 4, 64, 1.0, 0.25, P * 3, None, P * 4, 1, P * 5, 1 << 16, None]
 
     def call(**kw):
         a = list(good)
@@ -148,8 +170,9 @@ def test_kl_rejects(L):
     assert call(a0=None) == INVALID
     assert call(a1=P_ODD) == ALIGN
     assert call(a9=P + 32) == INVALID                 # gradient overlaps the teacher
-    assert call(a11=None, a12=0) == WS                # no row_loss and no workspace
+    assert call(a11=None, a12=0) == WS                # no workspace
     assert call(a12=16) == WS
+    assert call(a11=P * 5 + 64) == ALIGN
 
 
 def test_check_finite_rejects(L):
