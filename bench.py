@@ -42,8 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-scale", type=float, default=1.0,
-                    help="multiplies the size of the CPU-baseline sample")
+    ap.add_argument("--cpu-fraction", type=float, default=0.25,
+                    help="share of one step the CPU-oracle baseline runs (every part in proportion)")
     return ap.parse_args()
 
 
@@ -119,53 +119,82 @@ class Workload:
         rec(7)
 
 
-def cpu_baseline(scale: float):
-    """The CPU oracle (single-threaded C) on a bounded sample of each part."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "kl_seg_kernel_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "nvfp4_quantization_aware_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in ("kl_kernels.hip", "qad_device.h", "qad_internal.h"))
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec["traffic_bytes"]
+
+
+def cpu_baseline(fraction: float):
+    """The CPU oracle (single-threaded C) on `fraction` of one step: the same
+    share of every part, so its GB/s compares directly with the GPU step."""
     import numpy as np
-    import torch
     import oracle
     from nvfp4_quantization_aware_amd import synth
     oracle.build(force=False)
     bits = synth.bf16_bits
-    rows2 = max(16, int(2048 * scale))
-    rows3 = max(16, int(512 * scale))
-    rows4 = max(16, int(64 * scale))
-    rows5 = max(2, int(24 * scale))
-    w, g = synth.moe_weights_bf16(1, rows2, 4096, seed=2)
-    x, g3 = synth.student_t_activations_bf16(rows3, 4096, seed=3)
-    w4 = synth.gaussian_weight_bf16(rows4, 8192, seed=4)
-    t5, s5 = synth.logits_bf16(rows5, 131072, seed=5)
-    w, g, x, g3, w4, t5, s5 = (bits(a) for a in (w, g, x, g3, w4, t5, s5))
-    timings = []
+    experts = max(1, round(128 * fraction))
+    rows3 = max(16, round(32768 * fraction))
+    rows4 = max(16, round(8192 * fraction))
+    rows5 = max(2, round(8192 * fraction))
+    parts = {}
 
-    def timed(fn, nbytes):
+    def timed(name, fn, nbytes):
         t0 = time.perf_counter()
         fn()
-        timings.append((time.perf_counter() - t0, nbytes))
+        parts[name] = (time.perf_counter() - t0, nbytes)
 
-    timed(lambda: oracle.nvfp4_quantize(w[0]), 4 * w.size)
-    timed(lambda: np.copy(g), 4 * g.size)
-    timed(lambda: oracle.nvfp4_quantize(x), 4 * x.size)
-    timed(lambda: np.copy(g3), 4 * g3.size)
+    w, g = synth.moe_weights_bf16(experts, 2048, 4096, seed=2)
+    w, g = bits(w), bits(g)
 
-    def mse_then_frozen():
-        sc, ts = oracle.mse_calibrate(w4)
-        oracle.nvfp4_quantize(w4, sc, ts)
+    def moe_fwd():
+        for e in range(experts):
+            oracle.nvfp4_quantize(w[e])
 
-    timed(mse_then_frozen, 2 * w4.size + w4.size // 16 + 2 * w4.size + w4.size // 16 + 2 * w4.size)
-    timed(lambda: oracle.kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
-    secs = sum(t for t, _ in timings)
-    nbytes = sum(b for _, b in timings)
+    timed("moe_qdq_fwd", moe_fwd, 4 * w.size)
+    timed("moe_ste_bwd", lambda: np.copy(g), 4 * g.size)   # the oracle's STE is the identity
+    del w, g
+    x, g3 = synth.student_t_activations_bf16(rows3, 4096, seed=3)
+    x, g3 = bits(x), bits(g3)
+    timed("act_qdq_fwd", lambda: oracle.nvfp4_quantize(x), 4 * x.size)
+    timed("act_ste_bwd", lambda: np.copy(g3), 4 * g3.size)
+    del x, g3
+    w4 = bits(synth.gaussian_weight_bf16(rows4, 8192, seed=4))
+    cal = {}
+
+    def mse():
+        cal["s"] = oracle.mse_calibrate(w4)
+
+    timed("mse_calibrate", mse, 2 * w4.size + w4.size // 16)
+    timed("mse_frozen_qdq", lambda: oracle.nvfp4_quantize(w4, cal["s"][0], cal["s"][1]),
+          2 * w4.size + w4.size // 16 + 2 * w4.size)
+    del w4
+    t5, s5 = synth.logits_bf16(rows5, 131072, seed=5)
+    t5, s5 = bits(t5), bits(s5)
+    timed("kl_fwd_bwd", lambda: oracle.kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
+    secs = sum(t for t, _ in parts.values())
+    nbytes = sum(b for _, b in parts.values())
     return {
         "value": round(nbytes / secs / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "seconds": round(secs, 2),
-        "sample": ("one step's parts on a slice: 1 expert x %d x 4096 QDQ + its STE copy; %d x 4096 "
-                   "activation QDQ + STE copy; MSE calibration + frozen QDQ of %d x 8192; KL fwd+bwd "
-                   "of %d x 131072 rows (binary64); same generators and seeds as the GPU workload"
-                   % (rows2, rows3, rows4, rows5)),
+        "part_seconds": {k: round(v[0], 3) for k, v in parts.items()},
+        "kl_tokens_per_s": round(rows5 / parts["kl_fwd_bwd"][0], 2),
+        "sample": ("1/%d of one step, every part in proportion: %d of 128 experts QDQ + STE copy, %d of "
+                   "32768 activation rows QDQ + STE copy, %d of 8192 rows MSE calibration + frozen QDQ, "
+                   "%d of 8192 KL rows fwd+bwd (binary64); same generators and seeds as the GPU workload"
+                   % (round(1 / fraction), experts, rows3, rows4, rows5)),
     }
 
 
@@ -242,12 +271,13 @@ def main():
         "kl_tokens_per_s": round(kl_tokens_s, 1),
         "parts": parts,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("kl_seg_kernel<true, 1>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_scale)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
     print(json.dumps(out), flush=True)
 
 

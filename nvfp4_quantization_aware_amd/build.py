@@ -44,6 +44,25 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_test_pins(verbose: bool = False) -> list:
+    """GPU check programs the test-suite runs (tests/pins/*.hip)."""
+    pins = os.path.join(ROOT, "tests", "pins")
+    out_dir = os.path.join(pins, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    outs = []
+    for name in sorted(os.listdir(pins)):
+        if not name.endswith(".hip"):
+            continue
+        out = os.path.join(out_dir, name[:-4])
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-ffp-contract=off", "-Xclang",
+               "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out, os.path.join(pins, name)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        outs.append(out)
+    return outs
+
+
 def emit_asm(out_dir: str) -> list:
     """Device assembly of each kernel source (for reading the gfx950 code)."""
     os.makedirs(out_dir, exist_ok=True)
@@ -58,4 +77,5 @@ def emit_asm(out_dir: str) -> list:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_test_pins(verbose=True))
     sys.exit(0)

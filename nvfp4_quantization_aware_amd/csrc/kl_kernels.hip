@@ -26,8 +26,17 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 0x1.715476p+0f;  // RN(log2(e))
 constexpr float kLn2 = 0x1.62e430p-1f;    // RN(ln(2))
-constexpr int kSegThreads = 512;           // lanes per segment workgroup
-constexpr int kSegUnits = 4;               // 8-element units per lane and tensor
+// Segment shape: 256 lanes x 8 units of 8 logits = 16384 logits per tensor
+// (64 KiB of bf16 teacher + student per workgroup; measured fastest among
+// 64..1024 lanes x 2..24 units on MI355X).
+#ifndef QAD_KL_THREADS
+#define QAD_KL_THREADS 256
+#endif
+#ifndef QAD_KL_UNITS
+#define QAD_KL_UNITS 8
+#endif
+constexpr int kSegThreads = QAD_KL_THREADS; // lanes per segment workgroup
+constexpr int kSegUnits = QAD_KL_UNITS;     // 8-element units per lane and tensor
 constexpr int64_t kSegSpan = (int64_t)kSegThreads * kSegUnits; // units per segment
 constexpr int kMaxSegments = 64;           // longer rows take the two-pass kernel
 constexpr uint64_t kWaitTicks = 2000000;   // bounded wait (20 ms at 100 MHz)
@@ -194,15 +203,13 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
 
 
 // per-row exchange record for W segments, in words (whole 128-byte lines)
-__host__ __device__ inline int64_t rec_words(int W) { return (32 + 8 * (int64_t)W + 31) & ~(int64_t)31; }
+__host__ __device__ inline int64_t rec_words(int W) { return (10 * (int64_t)W + 31) & ~(int64_t)31; }
 
-// Per-row exchange record (rec_words(W) words, own cache lines): word 0 counts
-// arrived segments; segment s stores its 5 state words at 32 + 8 s.  Order is
-// carried by completion: a workgroup waits for the return of its exchanges
-// before it increments the count, so a reader that sees W arrivals also sees
-// every state.  Counts are zeroed before each launch.
-__device__ __forceinline__ uint32_t a_load(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
+// Per-row exchange record (rec_words(W) words, own cache lines): segment s
+// publishes its 5 state words as 64-bit {value, tag = 1} pairs at 5 s .. 5 s
+// + 4 with single-copy-atomic stores (no round trip for the writer); a
+// reader waits until all 5W tags are set.  Records are zeroed before each
+// launch.
 
 template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
 __global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
@@ -237,30 +244,42 @@ __global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, fl
         row_st = my_seg;
     } else {
         uint32_t* rec = rec_base + row * rec_words(W);
+        uint64_t* rec64 = reinterpret_cast<uint64_t*>(rec);
         if (tid < 5) {
             const float v = tid == 0 ? my_seg.mt : tid == 1 ? my_seg.zt : tid == 2 ? my_seg.at : tid == 3 ? my_seg.ms : my_seg.zs;
-            completed(__hip_atomic_exchange(rec + 32 + 8 * seg + tid, as_u(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            __hip_atomic_store(rec64 + 5 * seg + tid, ((uint64_t)1 << 32) | as_u(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (tid == 0) {
-            completed(__hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (tid < 64) {
+            // wave 0 polls: lane l watches words l, l + 64, ... (5W <= 320)
+            constexpr int kPer = (5 * kMaxSegments + 63) / 64;
+            uint64_t w[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) w[j] = 0;
             const uint64_t t0 = wall_clock64();
-            uint32_t n;
-            while ((n = a_load(rec)) < (uint32_t)W) {
-                __builtin_amdgcn_s_sleep(4);
+            bool done = false;
+            while (true) {
+                bool mine_done = true;
+#pragma unroll
+                for (int j = 0; j < kPer; ++j) {
+                    const int i = tid + 64 * j;
+                    if (i < 5 * W && !(w[j] >> 32)) w[j] = __hip_atomic_load(rec64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    mine_done = mine_done && (i >= 5 * W || (w[j] >> 32) != 0);
+                }
+                done = __all(mine_done);
+                if (done) break;
+                __builtin_amdgcn_s_sleep(2);
                 if (wall_clock64() - t0 > kWaitTicks) break;
             }
-            arrived = n;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = tid + 64 * j;
+                if (i < 5 * W) (&seg_stats[i / 5].mt)[i % 5] = as_f((uint32_t)w[j]);
+            }
+            if (tid == 0) arrived = done ? (uint32_t)W : 0u;
         }
         __syncthreads();
-        if (arrived >= (uint32_t)W) {
-            if (tid < 5 * W) {
-                const int s = tid / 5, f = tid - 5 * s;
-                const float v = as_f(a_load(rec + 32 + 8 * s + f));
-                float* dst = &seg_stats[s].mt;
-                dst[f] = v;
-            }
-            __syncthreads();
-        } else {
+        if (arrived < (uint32_t)W) {
             // timed out: compute every segment's state here, with the same
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {
@@ -393,10 +412,11 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, in
     if (threadIdx.x == 0) loss_out[0] = rows > 0 ? (float)(part[0] / (double)rows) : 0.0f;
 }
 
-__global__ void zero_counts_kernel(uint32_t* rec, int64_t rows, int64_t stride)
+// clear every tag a launch waits on (the whole records)
+__global__ void zero_records_kernel(uint32_t* rec, int64_t words)
 {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r < rows) rec[r * stride] = 0u;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < words) rec[i] = 0u;
 }
 
 int segments(int64_t vocab) { return (int)(((vocab >> 3) + kSegSpan - 1) / kSegSpan); }
@@ -423,8 +443,9 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
             uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
                                                         (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
             if (W > 1) {
-                hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((a.tokens + 255) / 256)), dim3(256), 0, stream,
-                                   rec, a.tokens, rec_words(W));
+                const int64_t n = a.tokens * rec_words(W);
+                hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                                   rec, n);
             }
             const dim3 grid((unsigned)(a.tokens * W)), block(kSegThreads);
 #define KS(BF, G) hipLaunchKernelGGL((kl_seg_kernel<BF, G>), grid, block, 0, stream, a, W, c, inv_t, gmul, rec)
