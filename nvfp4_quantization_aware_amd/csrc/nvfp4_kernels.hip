@@ -204,13 +204,11 @@ __device__ __forceinline__ float quotient(float x, float s, float r)
 // block's scale code; writes the 8 packed codes (even element in the low
 // nibble) and the 8 bf16 outputs y = bf16(dec(code) * s_eff).
 template <bool FROZEN, bool FAST>
-__device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t frozen_code, const ScaleTable& tab,
-                                                  float s_g, float rcp_g, uint32_t& code, uint32_t (&yw)[4])
+__device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t unit_max, uint32_t frozen_code,
+                                                  const ScaleTable& tab, float s_g, float rcp_g, uint32_t& code,
+                                                  uint32_t (&yw)[4])
 {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = umax(m, as_u(e[i]) & 0x7FFFFFFFu);
-    m = umax(m, swap_pair(m));
+    const uint32_t m = umax(unit_max, swap_pair(unit_max)); // block amax (binary32 bits)
     uint32_t sb = FROZEN ? frozen_code : block_scale_code<FAST>(as_f(m), s_g, rcp_g);
     sb &= 127u;
     const float s = tab.seff[sb], r = tab.rcp[sb];
@@ -237,8 +235,8 @@ enum { MODE_FROZEN = 0, MODE_AMAX = 1, MODE_ONEPASS = 2 };
 
 template <bool BF16, int MODE, bool FAST>
 __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16> (&raw)[Chunk<BF16>::U],
-                                           int64_t ubase, int64_t u0, int64_t units, const ScaleTable& tab,
-                                           float s_g)
+                                           const uint32_t (&unit_max)[Chunk<BF16>::U], int64_t ubase, int64_t u0,
+                                           int64_t units, const ScaleTable& tab, float s_g)
 {
     const float rcp_g = 1.0f / s_g;
     const int t = threadIdx.x;
@@ -251,7 +249,8 @@ __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16
         uint32_t frozen_code = 0;
         if constexpr (MODE == MODE_FROZEN) frozen_code = valid ? a.scales_in[(ubase + u) >> 1] : 0u;
         uint32_t code, yw[4];
-        const uint32_t sb = quantize_unit<MODE == MODE_FROZEN, FAST>(e, frozen_code, tab, s_g, rcp_g, code, yw);
+        const uint32_t sb = quantize_unit<MODE == MODE_FROZEN, FAST>(e, unit_max[k], frozen_code, tab, s_g, rcp_g,
+                                                                     code, yw);
         if (valid) {
             if (a.y) stnt(a.y, ubase + u, v4u{yw[0], yw[1], yw[2], yw[3]});
             if (a.codes) stnt32(a.codes, ubase + u, code);
@@ -306,6 +305,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         const int64_t u = u0 + k * kQThreads + t;
         raw[k] = load_raw<BF16>(a.x, ubase + u, u < units);
     }
+    // each unit's largest magnitude (binary32 bits), from the packed data
+    uint32_t unit_max[CH::U];
+#pragma unroll
+    for (int k = 0; k < CH::U; ++k) unit_max[k] = unit_absmax<BF16>(raw[k]);
 
     float s_g;
     if constexpr (MODE == MODE_FROZEN) {
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         const Record rec(ws, b, P);
         uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < CH::U; ++k) m = umax(m, unit_absmax<BF16>(raw[k]));
+        for (int k = 0; k < CH::U; ++k) m = umax(m, unit_max[k]);
         m = group_max(m, red);
         if (t == 0) sh_bcast = publish_max(rec, j, m) ? (a_load(rec.w) | 0x80000000u) : 0u;
         __syncthreads();
@@ -340,8 +343,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
     build_table(tab, s_g);
     if (j == 0 && t == 0 && a.tscale_out) a.tscale_out[b] = s_g;
     __syncthreads();
-    if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true>(a, raw, ubase, u0, units, tab, s_g);
-    else code_chunk<BF16, MODE, false>(a, raw, ubase, u0, units, tab, s_g);
+    if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true>(a, raw, unit_max, ubase, u0, units, tab, s_g);
+    else code_chunk<BF16, MODE, false>(a, raw, unit_max, ubase, u0, units, tab, s_g);
 }
 
 // ---------------------------------------------------------------------------
@@ -418,8 +421,8 @@ __global__ __launch_bounds__(kQThreads) void copy_kernel(const void* __restrict_
 // E4M3 are non-decreasing in i and, for grids no coarser than k_min/16 per
 // step, visit every code between the first and the last candidate's code
 // without a gap.  So the search runs over that contiguous code range (at most
-// 9 codes for k in [0.5, 1]) instead of all n candidates; ascending order
-// keeps "first candidate with strictly smaller error" as the tie rule.
+// 9 codes for k in [0.5, 1]) instead of all n candidates, and equal errors go
+// to the lowest code ("first candidate with strictly smaller error").
 // ---------------------------------------------------------------------------
 template <bool FAST>
 __device__ __forceinline__ float block_error(const float (&e)[16], float s, float r)
@@ -450,6 +453,20 @@ __device__ __forceinline__ float block_error(const float (&e)[16], float s, floa
     return err;
 }
 
+// squared error of the block's largest element alone under effective scale
+// s, computed exactly as its term inside block_error: a lower bound of the
+// block error (a binary32 running sum of non-negative terms never falls
+// below any of its terms)
+template <bool FAST>
+__device__ __forceinline__ float max_term(float amax_b, float s, float r)
+{
+    const float q = quotient<FAST>(amax_b, s, r);
+    float g, unused;
+    fp4_decode_pair<0>(fp4_encode_pair<0>(0u, q, 0.0f), g, unused);
+    const float d = amax_b - g * s;
+    return d * d;
+}
+
 template <bool BF16, bool FAST>
 __device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int64_t b, int64_t g, int64_t groups,
                                                  const ScaleTable& tab, float s_g)
@@ -478,11 +495,21 @@ __device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int64_t b, in
         const float amax_b = as_f(m);
         const uint32_t c_lo = block_scale_code<FAST>(amax_b * a.k_lo, s_g, rcp_g);
         const uint32_t c_hi = block_scale_code<FAST>(amax_b * a.k_hi, s_g, rcp_g);
-        uint32_t best = c_lo;
+        // Candidates from the largest code down; "<=" keeps the lowest code
+        // among equal errors, which is the first candidate in k order.  A
+        // candidate whose largest element alone already costs more than the
+        // best error so far cannot win; once the largest element is clipped
+        // (6 s <= amax_b) that cost only grows for smaller codes, so stop.
+        uint32_t best = c_hi;
         float best_err = __builtin_inff();
-        for (uint32_t cc = c_lo; cc <= c_hi; ++cc) {
-            const float err = block_error<FAST>(e, tab.seff[cc], tab.rcp[cc]);
-            if (err < best_err) { best_err = err; best = cc; }
+        for (int cc = (int)c_hi; cc >= (int)c_lo; --cc) {
+            const float s = tab.seff[cc], r = tab.rcp[cc];
+            if (max_term<FAST>(amax_b, s, r) > best_err) {
+                if (6.0f * s <= amax_b) break;
+                continue;
+            }
+            const float err = block_error<FAST>(e, s, r);
+            if (err <= best_err) { best_err = err; best = (uint32_t)cc; }
         }
         a.scales_out[gb] = (uint8_t)best;
     }
