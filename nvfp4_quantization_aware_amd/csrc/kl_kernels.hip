@@ -36,7 +36,7 @@ constexpr float kLn2 = 0x1.62e430p-1f;    // RN(ln(2))
 #define QAD_KL_UNITS 8
 #endif
 constexpr int kSegThreads = QAD_KL_THREADS; // lanes per segment workgroup
-constexpr int kSegUnits = QAD_KL_UNITS;     // 8-element units per lane and tensor
+constexpr int kSegUnits = QAD_KL_UNITS;     // 8-element units per lane, row and tensor
 constexpr int64_t kSegSpan = (int64_t)kSegThreads * kSegUnits; // units per segment
 constexpr int kMaxSegments = 64;           // longer rows take the two-pass kernel
 constexpr uint64_t kWaitTicks = 2000000;   // bounded wait (20 ms at 100 MHz)
@@ -56,12 +56,12 @@ __device__ __forceinline__ Stats empty_stats() { return Stats{-__builtin_inff(),
 __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b)
 {
     Stats r;
-    r.mt = fmaxf(a.mt, b.mt);
+    r.mt = maxnan(a.mt, b.mt);
     const float fa = a.mt == r.mt ? 1.0f : exp2_hw(a.mt - r.mt);
     const float fb = b.mt == r.mt ? 1.0f : exp2_hw(b.mt - r.mt);
     r.zt = a.zt * fa + b.zt * fb;
     r.at = a.at * fa + b.at * fb;
-    r.ms = fmaxf(a.ms, b.ms);
+    r.ms = maxnan(a.ms, b.ms);
     const float ga = a.ms == r.ms ? 1.0f : exp2_hw(a.ms - r.ms);
     const float gb = b.ms == r.ms ? 1.0f : exp2_hw(b.ms - r.ms);
     r.zs = a.zs * ga + b.zs * gb;
@@ -105,7 +105,15 @@ __device__ __forceinline__ void load8(const void* base, int64_t unit, bool valid
 
 __device__ __forceinline__ float max8(const float (&v)[8])
 {
-    return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    return maxnan(maxnan(maxnan(v[0], v[1]), maxnan(v[2], v[3])), maxnan(maxnan(v[4], v[5]), maxnan(v[6], v[7])));
+}
+
+// max(acc, v[0..7]) in four three-operand maxima
+__device__ __forceinline__ float fold_max8(float acc, const float (&v)[8])
+{
+    const float p = maxnan(maxnan(v[0], v[1]), v[2]);
+    const float q = maxnan(maxnan(v[3], v[4]), v[5]);
+    return maxnan(maxnan(maxnan(acc, p), q), maxnan(v[6], v[7]));
 }
 
 __device__ __forceinline__ float sum8(const float (&v)[8])
@@ -159,39 +167,42 @@ __device__ __forceinline__ int64_t lane_unit(int64_t seg_u0, int k) { return seg
 // of 2^(c x - m) and the teacher-weighted sum of t - s, unit by unit in
 // ascending order.  `get(k, unit)` supplies unit k: from registers in the
 // segment's own workgroup (UNROLL, everything in flight at once), from memory
-// one unit at a time in the bounded wait's fallback.  The arithmetic is the
-// same either way (the maximum is order-independent, the sums run in unit
-// order), so both give bit-identical states.
-template <bool BF16, bool UNROLL, class Get>
-__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get)
+// one unit at a time in the bounded wait's fallback; `between()` runs after
+// the maxima.  FULL: every unit lies inside the row (no validity tests).  The
+// arithmetic is the same in every form (the maximum is order-independent, the
+// sums run in unit order, a valid unit takes the same operations), so all
+// give bit-identical states.
+template <bool BF16, bool UNROLL, bool FULL, class Get, class Between>
+__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get, Between between)
 {
+    constexpr int kUnroll = UNROLL ? kSegUnits : 1;
     float mt = -__builtin_inff(), ms = -__builtin_inff();
-#pragma unroll(UNROLL ? kSegUnits : 1)
+#pragma unroll kUnroll
     for (int k = 0; k < kSegUnits; ++k) {
-        const bool valid = lane_unit(seg_u0, k) < units;
+        const bool valid = FULL || lane_unit(seg_u0, k) < units;
         Unit<BF16> u;
         get(k, u);
         float tv[8], sv[8];
         u.values(tv, sv);
-        if (valid) { mt = fmaxf(mt, max8(tv)); ms = fmaxf(ms, max8(sv)); }
+        if (valid) { mt = fold_max8(mt, tv); ms = fold_max8(ms, sv); }
     }
+    between();
     mt *= c;  // c > 0: the max of the scaled logits
     ms *= c;
     float zt = 0.0f, zs = 0.0f, at = 0.0f;
-#pragma unroll(UNROLL ? kSegUnits : 1)
+#pragma unroll kUnroll
     for (int k = 0; k < kSegUnits; ++k) {
-        const bool valid = lane_unit(seg_u0, k) < units;
+        const bool valid = FULL || lane_unit(seg_u0, k) < units;
         Unit<BF16> u;
         get(k, u);
-#pragma unroll
-        for (int q = 0; q < Unit<BF16>::V; ++q) { refresh(u.t[q]); refresh(u.s[q]); }
         float tv[8], sv[8], pt[8], ps[8];
         u.values(tv, sv);
         float pa = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            pt[i] = valid ? exp2_hw(__builtin_fmaf(tv[i], c, -mt)) : 0.0f;
-            ps[i] = valid ? exp2_hw(__builtin_fmaf(sv[i], c, -ms)) : 0.0f;
+            pt[i] = exp2_hw(__builtin_fmaf(tv[i], c, -mt));
+            ps[i] = exp2_hw(__builtin_fmaf(sv[i], c, -ms));
+            if (!FULL) { pt[i] = valid ? pt[i] : 0.0f; ps[i] = valid ? ps[i] : 0.0f; }
             pa = __builtin_fmaf(pt[i], tv[i] - sv[i], pa);
         }
         zt = zt + sum8(pt);
@@ -201,6 +212,21 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
     return Stats{mt, zt, at, ms, zs};
 }
 
+// every lane's state over a segment held in registers
+template <bool BF16, bool FULL, class Regs>
+__device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c)
+{
+    // make the logits opaque between the two loops, so that their widened
+    // values are recomputed rather than kept alive from the first loop
+    return lane_state<BF16, true, FULL>(
+        seg_u0, units, c, [&](int k, Unit<BF16>& u) { u = m[k]; },
+        [&]() {
+#pragma unroll
+            for (int k = 0; k < kSegUnits; ++k)
+#pragma unroll
+                for (int q = 0; q < Unit<BF16>::V; ++q) { refresh(m[k].t[q]); refresh(m[k].s[q]); }
+        });
+}
 
 // per-row exchange record for W segments, in words (whole 128-byte lines)
 __host__ __device__ inline int64_t rec_words(int W) { return (10 * (int64_t)W + 31) & ~(int64_t)31; }
@@ -210,106 +236,143 @@ __host__ __device__ inline int64_t rec_words(int W) { return (10 * (int64_t)W + 
 // + 4 with single-copy-atomic stores (no round trip for the writer); a
 // reader waits until all 5W tags are set.  Records are zeroed before each
 // launch.
-
-template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
-__global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
-                                                             uint32_t* rec_base)
+__device__ __forceinline__ void publish(uint64_t* rec64, int seg, const Stats& st)
 {
-    __shared__ Stats part[kSegThreads / 64];
-    __shared__ Stats seg_stats[kMaxSegments];
-    __shared__ uint32_t arrived;
-    const int64_t row = blockIdx.x / W;
-    const int seg = (int)(blockIdx.x - row * W);
-    const int64_t units = a.vocab >> 3;
-    const int64_t row_unit0 = row * units;
     const int tid = threadIdx.x;
-
-    const int64_t seg_u0 = seg * kSegSpan;
-    Unit<BF16_IN> mine[kSegUnits];
-    bool valid[kSegUnits];
-#pragma unroll
-    for (int k = 0; k < kSegUnits; ++k) {
-        valid[k] = lane_unit(seg_u0, k) < units;
-        mine[k].load(a, row_unit0 + lane_unit(seg_u0, k), valid[k]);
+    if (tid < 5) {
+        const float v = tid == 0 ? st.mt : tid == 1 ? st.zt : tid == 2 ? st.at : tid == 3 ? st.ms : st.zs;
+        __hip_atomic_store(rec64 + 5 * seg + tid, ((uint64_t)1 << 32) | as_u(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    const Stats lane_st = lane_state<BF16_IN, true>(seg_u0, units, c, [&](int k, Unit<BF16_IN>& u) { u = mine[k]; });
-    const Stats my_seg = group_merge<kSegThreads>(lane_st, part);
-#pragma unroll
-    for (int k = 0; k < kSegUnits; ++k)
-#pragma unroll
-        for (int q = 0; q < Unit<BF16_IN>::V; ++q) { refresh(mine[k].t[q]); refresh(mine[k].s[q]); }
+}
 
-    Stats row_st;
-    if (W == 1) {
-        row_st = my_seg;
-    } else {
-        uint32_t* rec = rec_base + row * rec_words(W);
-        uint64_t* rec64 = reinterpret_cast<uint64_t*>(rec);
-        if (tid < 5) {
-            const float v = tid == 0 ? my_seg.mt : tid == 1 ? my_seg.zt : tid == 2 ? my_seg.at : tid == 3 ? my_seg.ms : my_seg.zs;
-            __hip_atomic_store(rec64 + 5 * seg + tid, ((uint64_t)1 << 32) | as_u(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (tid < 64) {
-            // wave 0 polls: lane l watches words l, l + 64, ... (5W <= 320)
-            constexpr int kPer = (5 * kMaxSegments + 63) / 64;
-            uint64_t w[kPer];
+// Wave 0 waits (bounded) for all W segment states of a row and copies them to
+// `seg`; returns, to every lane of the workgroup, whether they all arrived.
+__device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg, uint32_t* flag)
+{
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        // lane l watches words l, l + 64, ... (5W <= 5 kMaxSegments)
+        constexpr int kPer = (5 * kMaxSegments + 63) / 64;
+        uint64_t w[kPer];
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) w[j] = 0;
-            const uint64_t t0 = wall_clock64();
-            bool done = false;
-            while (true) {
-                bool mine_done = true;
-#pragma unroll
-                for (int j = 0; j < kPer; ++j) {
-                    const int i = tid + 64 * j;
-                    if (i < 5 * W && !(w[j] >> 32)) w[j] = __hip_atomic_load(rec64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    mine_done = mine_done && (i >= 5 * W || (w[j] >> 32) != 0);
-                }
-                done = __all(mine_done);
-                if (done) break;
-                __builtin_amdgcn_s_sleep(2);
-                if (wall_clock64() - t0 > kWaitTicks) break;
-            }
+        for (int j = 0; j < kPer; ++j) w[j] = 0;
+        const uint64_t t0 = wall_clock64();
+        bool done = false;
+        while (true) {
+            bool mine_done = true;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int i = tid + 64 * j;
-                if (i < 5 * W) (&seg_stats[i / 5].mt)[i % 5] = as_f((uint32_t)w[j]);
+                if (i < 5 * W && !(w[j] >> 32)) w[j] = __hip_atomic_load(rec64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                mine_done = mine_done && (i >= 5 * W || (w[j] >> 32) != 0);
             }
-            if (tid == 0) arrived = done ? (uint32_t)W : 0u;
+            done = __all(mine_done);
+            if (done) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (wall_clock64() - t0 > kWaitTicks) break;
         }
-        __syncthreads();
-        if (arrived < (uint32_t)W) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + 64 * j;
+            if (i < 5 * W) (&seg[i / 5].mt)[i % 5] = as_f((uint32_t)w[j]);
+        }
+        if (tid == 0) *flag = done ? 1u : 0u;
+    }
+    __syncthreads();
+    return *flag != 0u;  // the caller synchronises before the flag is written again
+}
+
+// Merge the W segment states of a row in a fixed tree (lane l of every wave
+// starts from segment l; xor partners, merge is symmetric in its operands),
+// so every workgroup of the row obtains bit-identical row statistics.
+__device__ __forceinline__ Stats merge_segments(const Stats* seg, int W)
+{
+    const int l = threadIdx.x & 63;
+    Stats st = l < W ? seg[l] : empty_stats();
+    for (int o = 1; o < W; o <<= 1) st = merge(st, shfl_xor_stats(st, o));
+    return Stats{__shfl(st.mt, 0, 64), __shfl(st.zt, 0, 64), __shfl(st.at, 0, 64), __shfl(st.ms, 0, 64),
+                 __shfl(st.zs, 0, 64)};
+}
+
+template <bool BF16_IN>
+using SegRegs = Unit<BF16_IN>[kSegUnits];
+
+// issue the loads of one segment (units past the row end read as zeros)
+template <bool BF16_IN, bool FULL>
+__device__ __forceinline__ void seg_load(SegRegs<BF16_IN>& m, const KlArgs& a, int64_t row_unit0, int64_t seg_u0,
+                                         int64_t units)
+{
+#pragma unroll
+    for (int k = 0; k < kSegUnits; ++k)
+        m[k].load(a, row_unit0 + lane_unit(seg_u0, k), FULL || lane_unit(seg_u0, k) < units);
+}
+
+// pass 1: the segment's state, identical in every lane
+template <bool BF16_IN, bool FULL>
+__device__ __forceinline__ Stats seg_pass1(SegRegs<BF16_IN>& m, int64_t seg_u0, int64_t units, float c, Stats* part)
+{
+    const Stats lane_st = lane_state_regs<BF16_IN, FULL>(m, seg_u0, units, c);
+    const Stats st = group_merge<kSegThreads>(lane_st, part);
+#pragma unroll
+    for (int k = 0; k < kSegUnits; ++k)
+#pragma unroll
+        for (int q = 0; q < Unit<BF16_IN>::V; ++q) { refresh(m[k].t[q]); refresh(m[k].s[q]); }
+    return st;
+}
+
+struct SegShared {
+    Stats part[kSegThreads / 64];
+    Stats seg_stats[kMaxSegments];
+    uint32_t flag;
+};
+
+// the row's statistics (exchange + merge), its loss (segment 0) and pass 2:
+// p = 2^(c t - m_row) / Z_row and q alike, times grad_scale / T, written as
+// the gradient from the logits still held in registers
+template <bool BF16_IN, int GRAD, bool FULL>
+__device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a, int W, int64_t row, int seg,
+                                           const Stats& my_seg, float c, float inv_t, float gmul,
+                                           uint32_t* rec_base, SegShared& sh)
+{
+    const int64_t units = a.vocab >> 3;
+    const int64_t row_unit0 = row * units;
+    const int64_t seg_u0 = seg * kSegSpan;
+    Stats row_st = my_seg;
+    if (W > 1) {
+        const uint64_t* rec64 = reinterpret_cast<const uint64_t*>(rec_base + row * rec_words(W));
+        if (!collect(rec64, W, sh.seg_stats, &sh.flag)) {
             // timed out: compute every segment's state here, with the same
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {
                 const int64_t o_u0 = s * kSegSpan;
-                const Stats ol = lane_state<BF16_IN, false>(o_u0, units, c, [&](int k, Unit<BF16_IN>& u) {
-                    u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
-                });
-                const Stats os = group_merge<kSegThreads>(ol, part);
-                if (tid == 0) seg_stats[s] = os;
+                const Stats ol = lane_state<BF16_IN, false, false>(
+                    o_u0, units, c,
+                    [&](int k, Unit<BF16_IN>& u) {
+                        u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
+                    },
+                    [] {});
+                const Stats os = group_merge<kSegThreads>(ol, sh.part);
+                if (threadIdx.x == 0) sh.seg_stats[s] = os;
             }
             __syncthreads();
         }
-        row_st = seg_stats[0];
-        for (int s = 1; s < W; ++s) row_st = merge(row_st, seg_stats[s]);
+        row_st = merge_segments(sh.seg_stats, W);
+        __syncthreads();  // seg_stats and flag are reused by the next row
     }
 
-    if (seg == 0 && tid == 0) {
+    if (seg == 0 && threadIdx.x == 0) {
         // KL = E_p[t - s]/T - (LSE_t - LSE_s), LSE in log2 units m + log2 Z
         a.row_loss[row] = (row_st.at / row_st.zt) * inv_t -
                           kLn2 * ((row_st.mt - row_st.ms) + log2f(row_st.zt / row_st.zs));
     }
     if constexpr (GRAD != 0) {
-        // p = 2^(c t - m_row) / Z_row and q alike, times grad_scale / T, from
-        // the logits still held in registers
         const float wt = gmul / row_st.zt, ws = gmul / row_st.zs;
 #pragma unroll
         for (int k = 0; k < kSegUnits; ++k) {
-            if (!valid[k]) continue;
+            if (!FULL && lane_unit(seg_u0, k) >= units) continue;
             float tv[8], sv[8], g[8];
-            mine[k].values(tv, sv);
+            m[k].values(tv, sv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
@@ -318,14 +381,48 @@ __global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, fl
             }
             const int64_t u = row_unit0 + lane_unit(seg_u0, k);
             if constexpr (GRAD == 1) {
-                stnt(a.grad, u,
-                     v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])});
+                stnt(a.grad, u, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                                    pack_bf16x2(g[6], g[7])});
             } else {
                 stnt(a.grad, 2 * u, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
                 stnt(a.grad, 2 * u + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
             }
         }
     }
+}
+
+__device__ __forceinline__ uint64_t* rec_of(uint32_t* rec_base, int64_t row, int W)
+{
+    return reinterpret_cast<uint64_t*>(rec_base + row * rec_words(W));
+}
+
+template <bool BF16_IN, int GRAD, bool FULL>
+__device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, int seg, float c, float inv_t, float gmul,
+                                         uint32_t* rec_base, SegShared& sh)
+{
+    const int64_t units = a.vocab >> 3;
+    const int64_t seg_u0 = seg * kSegSpan;
+    SegRegs<BF16_IN> m;
+    seg_load<BF16_IN, FULL>(m, a, row * units, seg_u0, units);
+    const Stats st = seg_pass1<BF16_IN, FULL>(m, seg_u0, units, c, sh.part);
+    if (W > 1) publish(rec_of(rec_base, row, W), seg, st);
+    seg_finish<BF16_IN, GRAD, FULL>(m, a, W, row, seg, st, c, inv_t, gmul, rec_base, sh);
+}
+
+// One workgroup per segment: load, pass 1, publish, wait, pass 2.  Segments
+// that lie wholly inside the row (all but a ragged last one) take a form
+// without per-unit bounds tests.
+template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
+__global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+                                                             uint32_t* rec_base)
+{
+    __shared__ SegShared sh;
+    const int64_t row = blockIdx.x / W;
+    const int seg = (int)(blockIdx.x - row * W);
+    if ((seg + 1) * kSegSpan <= (a.vocab >> 3))
+        seg_body<BF16_IN, GRAD, true>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+    else
+        seg_body<BF16_IN, GRAD, false>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -337,8 +434,8 @@ constexpr int kRowThreads = 1024;
 // fold one unit of 8 teacher / student logits into the lane's running state
 __device__ __forceinline__ void accumulate(Stats& st, const float (&t)[8], const float (&s)[8], float c)
 {
-    const float nmt = fmaxf(st.mt, max8(t) * c);
-    const float nms = fmaxf(st.ms, max8(s) * c);
+    const float nmt = maxnan(st.mt, max8(t) * c);
+    const float nms = maxnan(st.ms, max8(s) * c);
     const float ft = st.mt == nmt ? 1.0f : exp2_hw(st.mt - nmt);
     const float fs = st.ms == nms ? 1.0f : exp2_hw(st.ms - nms);
     st.mt = nmt;
@@ -415,11 +512,16 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, in
 // clear every tag a launch waits on (the whole records)
 __global__ void zero_records_kernel(uint32_t* rec, int64_t words)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < words) rec[i] = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        rec[i] = 0u;
 }
 
-int segments(int64_t vocab) { return (int)(((vocab >> 3) + kSegSpan - 1) / kSegSpan); }
+// segments of a row, kMaxSegments + 1 standing for "too many"
+int segments(int64_t vocab)
+{
+    const int64_t w = ((vocab >> 3) + kSegSpan - 1) / kSegSpan;
+    return (int)min(w, (int64_t)kMaxSegments + 1);
+}
 
 } // namespace
 
@@ -439,28 +541,41 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
         const float gmul = a.grad_scale / a.temperature;
         const int W = segments(a.vocab);
         const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
-        if (W <= kMaxSegments) {
-            uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                        (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
-            if (W > 1) {
-                const int64_t n = a.tokens * rec_words(W);
-                hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                                   rec, n);
-            }
-            const dim3 grid((unsigned)(a.tokens * W)), block(kSegThreads);
-#define KS(BF, G) hipLaunchKernelGGL((kl_seg_kernel<BF, G>), grid, block, 0, stream, a, W, c, inv_t, gmul, rec)
-            if (a.bf16_in) { if (gmode == 0) KS(true, 0); else if (gmode == 1) KS(true, 1); else KS(true, 2); }
-            else { if (gmode == 0) KS(false, 0); else if (gmode == 1) KS(false, 1); else KS(false, 2); }
-#undef KS
-        } else {
-            const dim3 grid((unsigned)a.tokens), block(kRowThreads);
-#define KR(BF, G) hipLaunchKernelGGL((kl_row_kernel<BF, G>), grid, block, 0, stream, a, c, inv_t, gmul)
-            if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
-            else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
-#undef KR
+        uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                    (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
+        if (W > 1 && W <= kMaxSegments) {
+            const int64_t n = a.tokens * rec_words(W);
+            hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)min((n + 255) / 256, (int64_t)65536)), dim3(256), 0,
+                               stream, rec, n);
         }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        // rows in batches, so that no grid exceeds 2^22 workgroups
+        const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+        const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
+        const int64_t batch = W <= kMaxSegments ? ((int64_t)1 << 22) / W : (int64_t)1 << 20;
+        for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+            KlArgs b = a;
+            b.tokens = min(batch, a.tokens - r0);
+            b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
+            b.student = static_cast<const char*>(a.student) + r0 * in_row;
+            b.row_loss = a.row_loss + r0;
+            if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
+            if (W <= kMaxSegments) {
+                uint32_t* brec = rec + r0 * rec_words(W);
+                const dim3 grid((unsigned)(b.tokens * W)), block(kSegThreads);
+#define KS(BF, GM) hipLaunchKernelGGL((kl_seg_kernel<BF, GM>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
+                if (a.bf16_in) { if (gmode == 0) KS(true, 0); else if (gmode == 1) KS(true, 1); else KS(true, 2); }
+                else { if (gmode == 0) KS(false, 0); else if (gmode == 1) KS(false, 1); else KS(false, 2); }
+#undef KS
+            } else {
+                const dim3 grid((unsigned)b.tokens), block(kRowThreads);
+#define KR(BF, GM) hipLaunchKernelGGL((kl_row_kernel<BF, GM>), grid, block, 0, stream, b, c, inv_t, gmul)
+                if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
+                else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
+#undef KR
+            }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
     return hipGetLastError();

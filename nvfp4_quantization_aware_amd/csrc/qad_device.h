@@ -17,12 +17,20 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return as_f(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
 
 // Two binary32 values -> two bf16 (round to nearest even) packed in a word,
-// `lo` in bits 0..15.  Lowers to one v_cvt_pk_bf16_f32.
+// `lo` in bits 0..15.  A two-lane vector conversion, so that it lowers to a
+// single v_cvt_pk_bf16_f32 with both sources (converting the halves one by
+// one costs two conversions, a shift and an or).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// IEEE 754-2019 maximum (a NaN operand gives NaN).  Unlike fmaxf it needs
+// no quieting of its operands; gfx950 does it in v_maximum3_f32.
+__device__ __forceinline__ float maxnan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // ---------------------------------------------------------------------------
 // E4M3 (OCP E4M3FN) block scale, [Nano] "NVFP4-Format und warum es wichtig

@@ -70,8 +70,9 @@ def test_workspace_sizes(L):
         for B, R, C_ in ((128, 2048, 4096), (1, 1, 16), (1, 8192, 8192), (3, 7, 48)):
             assert L.qad_workspace_bytes(op, B, R, C_) == _record_bytes(B, R * C_)
     # KL: per-row losses, then one exchange record per row when a row spans
-    # several segments of 16384 logits (5 tagged 64-bit words per segment)
-    for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20)):
+    # 2..64 segments of 16384 logits (5 tagged 64-bit words per segment)
+    for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20), (3, (1 << 20) + 8),
+                          (3, 1 << 22)):
         W = -(-vocab // 16384)
         rec = ((10 * W + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
         expect = -(-(tokens * 4) // 256) * 256 + tokens * rec

@@ -48,6 +48,8 @@ def run_kl(dev, t, s, T, grad_dtype, label):
     (3, 8, 1.0, torch.bfloat16, torch.bfloat16),
     (33, 12344, 0.5, torch.bfloat16, torch.bfloat16),
     (2, 24584, 1.0, torch.float32, torch.bfloat16),
+    (3, 1 << 20, 1.0, torch.bfloat16, torch.float32),        # 64 segments of 16384 logits
+    (2, (1 << 20) + 8, 1.0, torch.bfloat16, torch.bfloat16),  # one unit past 64 segments: two-pass kernel
 ])
 def test_kl_small(dev, orc, tokens, vocab, T, in_dt, g_dt):
     t, s = synth.logits_bf16(tokens=tokens, vocab=vocab, seed=tokens * 7 + vocab)
@@ -57,6 +59,19 @@ def test_kl_small(dev, orc, tokens, vocab, T, in_dt, g_dt):
     assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
     _check_rows(rows, ref_rows)
     assert_kl_grad_close(g, ref_g)
+
+
+@pytest.mark.parametrize("g_dt", [torch.bfloat16, None])
+def test_kl_many_rounds(dev, orc, g_dt):
+    # 1024 rows x 5 segments (the last one ragged): many more workgroups than
+    # fit on the device at once, so exchanges span many dispatch waves
+    t, s = synth.logits_bf16(tokens=1024, vocab=65544, seed=17)
+    loss, rows, g = run_kl(dev, t, s, 1.0, g_dt, "many rounds")
+    ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), grad_scale=1.0 / 1024)
+    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
+    _check_rows(rows, ref_rows)
+    if g_dt is not None:
+        assert_kl_grad_close(g, ref_g)
 
 
 def test_kl_forward_only_matches(dev):
