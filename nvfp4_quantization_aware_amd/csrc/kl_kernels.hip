@@ -108,14 +108,6 @@ __device__ __forceinline__ float max8(const float (&v)[8])
     return maxnan(maxnan(maxnan(v[0], v[1]), maxnan(v[2], v[3])), maxnan(maxnan(v[4], v[5]), maxnan(v[6], v[7])));
 }
 
-// max(acc, v[0..7]) in four three-operand maxima
-__device__ __forceinline__ float fold_max8(float acc, const float (&v)[8])
-{
-    const float p = maxnan(maxnan(v[0], v[1]), v[2]);
-    const float q = maxnan(maxnan(v[3], v[4]), v[5]);
-    return maxnan(maxnan(maxnan(acc, p), q), maxnan(v[6], v[7]));
-}
-
 __device__ __forceinline__ float sum8(const float (&v)[8])
 {
     return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
@@ -163,51 +155,51 @@ __device__ __forceinline__ void refresh(v4u& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ int64_t lane_unit(int64_t seg_u0, int k) { return seg_u0 + k * kSegThreads + threadIdx.x; }
 
-// A lane's state over its units of one segment: maxima first, then the sums
-// of 2^(c x - m) and the teacher-weighted sum of t - s, unit by unit in
-// ascending order.  `get(k, unit)` supplies unit k: from registers in the
-// segment's own workgroup (UNROLL, everything in flight at once), from memory
-// one unit at a time in the bounded wait's fallback; `between()` runs after
-// the maxima.  FULL: every unit lies inside the row (no validity tests).  The
-// arithmetic is the same in every form (the maximum is order-independent, the
-// sums run in unit order, a valid unit takes the same operations), so all
-// give bit-identical states.
-template <bool BF16, bool UNROLL, bool FULL, class Get, class Between>
-__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get, Between between)
+// A lane's state over its units of one segment, in one pass: unit by unit
+// in ascending order, the running maxima (of c x) are raised to the unit's
+// and the sums of 2^(c x - m) and the teacher-weighted sum of t - s are
+// rescaled by 2^(m_old - m_new) when they move, then the unit is added.  A
+// unit is thus consumed as soon as its loads land, while later units are
+// still in flight.  `get(k, unit)` supplies unit k: from registers in the
+// segment's own workgroup (UNROLL), from memory one unit at a time in the
+// bounded wait's fallback.  FULL: every unit lies inside the row.  The
+// arithmetic is the same in every form (a unit past the row end is skipped
+// and a valid one takes the same operations), so all give bit-identical
+// states.
+template <bool BF16, bool UNROLL, bool FULL, class Get>
+__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get)
 {
     constexpr int kUnroll = UNROLL ? kSegUnits : 1;
     float mt = -__builtin_inff(), ms = -__builtin_inff();
-#pragma unroll kUnroll
-    for (int k = 0; k < kSegUnits; ++k) {
-        const bool valid = FULL || lane_unit(seg_u0, k) < units;
-        Unit<BF16> u;
-        get(k, u);
-        float tv[8], sv[8];
-        u.values(tv, sv);
-        if (valid) { mt = fold_max8(mt, tv); ms = fold_max8(ms, sv); }
-    }
-    between();
-    mt *= c;  // c > 0: the max of the scaled logits
-    ms *= c;
     float zt = 0.0f, zs = 0.0f, at = 0.0f;
 #pragma unroll kUnroll
     for (int k = 0; k < kSegUnits; ++k) {
         const bool valid = FULL || lane_unit(seg_u0, k) < units;
         Unit<BF16> u;
         get(k, u);
+        if (!valid) continue;
         float tv[8], sv[8], pt[8], ps[8];
         u.values(tv, sv);
+        // c > 0: the max of the scaled logits is the scaled max
+        const float nmt = maxnan(mt, max8(tv) * c);
+        const float nms = maxnan(ms, max8(sv) * c);
+        // equal maxima (also both -inf) need no rescaling
+        const float ft = nmt == mt ? 1.0f : exp2_hw(mt - nmt);
+        const float fs = nms == ms ? 1.0f : exp2_hw(ms - nms);
+        mt = nmt;
+        ms = nms;
         float pa = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             pt[i] = exp2_hw(__builtin_fmaf(tv[i], c, -mt));
             ps[i] = exp2_hw(__builtin_fmaf(sv[i], c, -ms));
-            if (!FULL) { pt[i] = valid ? pt[i] : 0.0f; ps[i] = valid ? ps[i] : 0.0f; }
             pa = __builtin_fmaf(pt[i], tv[i] - sv[i], pa);
         }
-        zt = zt + sum8(pt);
-        zs = zs + sum8(ps);
-        at = at + pa;
+        zt = zt * ft + sum8(pt);
+        at = at * ft + pa;
+        zs = zs * fs + sum8(ps);
+        // unit by unit: later units' work is not hoisted above this point
+        if (UNROLL) asm volatile("" : "+v"(zt), "+v"(zs), "+v"(at), "+v"(mt), "+v"(ms));
     }
     return Stats{mt, zt, at, ms, zs};
 }
@@ -216,16 +208,7 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
 template <bool BF16, bool FULL, class Regs>
 __device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c)
 {
-    // make the logits opaque between the two loops, so that their widened
-    // values are recomputed rather than kept alive from the first loop
-    return lane_state<BF16, true, FULL>(
-        seg_u0, units, c, [&](int k, Unit<BF16>& u) { u = m[k]; },
-        [&]() {
-#pragma unroll
-            for (int k = 0; k < kSegUnits; ++k)
-#pragma unroll
-                for (int q = 0; q < Unit<BF16>::V; ++q) { refresh(m[k].t[q]); refresh(m[k].s[q]); }
-        });
+    return lane_state<BF16, true, FULL>(seg_u0, units, c, [&](int k, Unit<BF16>& u) { u = m[k]; });
 }
 
 // per-row exchange record for W segments, in words (whole 128-byte lines)
@@ -346,12 +329,9 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {
                 const int64_t o_u0 = s * kSegSpan;
-                const Stats ol = lane_state<BF16_IN, false, false>(
-                    o_u0, units, c,
-                    [&](int k, Unit<BF16_IN>& u) {
-                        u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
-                    },
-                    [] {});
+                const Stats ol = lane_state<BF16_IN, false, false>(o_u0, units, c, [&](int k, Unit<BF16_IN>& u) {
+                    u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
+                });
                 const Stats os = group_merge<kSegThreads>(ol, sh.part);
                 if (threadIdx.x == 0) sh.seg_stats[s] = os;
             }
@@ -413,8 +393,7 @@ __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, in
 // that lie wholly inside the row (all but a ragged last one) take a form
 // without per-unit bounds tests.
 template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
-__global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
-                                                             uint32_t* rec_base)
+__device__ __forceinline__ void seg_entry(const KlArgs& a, int W, float c, float inv_t, float gmul, uint32_t* rec_base)
 {
     __shared__ SegShared sh;
     const int64_t row = blockIdx.x / W;
@@ -423,6 +402,21 @@ __global__ __launch_bounds__(kSegThreads) void kl_seg_kernel(KlArgs a, int W, fl
         seg_body<BF16_IN, GRAD, true>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
     else
         seg_body<BF16_IN, GRAD, false>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+}
+
+// bf16 logits: held to 128 VGPRs, four workgroups per CU
+template <int GRAD>
+__global__ __launch_bounds__(kSegThreads, 4) void kl_seg_bf16_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+                                                                     uint32_t* rec_base)
+{
+    seg_entry<true, GRAD>(a, W, c, inv_t, gmul, rec_base);
+}
+
+template <int GRAD>
+__global__ __launch_bounds__(kSegThreads) void kl_seg_f32_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+                                                                 uint32_t* rec_base)
+{
+    seg_entry<false, GRAD>(a, W, c, inv_t, gmul, rec_base);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,9 +556,14 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
             if (W <= kMaxSegments) {
                 uint32_t* brec = rec + r0 * rec_words(W);
                 const dim3 grid((unsigned)(b.tokens * W)), block(kSegThreads);
-#define KS(BF, GM) hipLaunchKernelGGL((kl_seg_kernel<BF, GM>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
-                if (a.bf16_in) { if (gmode == 0) KS(true, 0); else if (gmode == 1) KS(true, 1); else KS(true, 2); }
-                else { if (gmode == 0) KS(false, 0); else if (gmode == 1) KS(false, 1); else KS(false, 2); }
+#define KS(K, GM) hipLaunchKernelGGL((K<GM>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
+                if (a.bf16_in) {
+                    if (gmode == 0) KS(kl_seg_bf16_kernel, 0); else if (gmode == 1) KS(kl_seg_bf16_kernel, 1);
+                    else KS(kl_seg_bf16_kernel, 2);
+                } else {
+                    if (gmode == 0) KS(kl_seg_f32_kernel, 0); else if (gmode == 1) KS(kl_seg_f32_kernel, 1);
+                    else KS(kl_seg_f32_kernel, 2);
+                }
 #undef KS
             } else {
                 const dim3 grid((unsigned)b.tokens), block(kRowThreads);

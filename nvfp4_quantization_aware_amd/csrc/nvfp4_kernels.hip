@@ -26,6 +26,8 @@ constexpr float kRcp6 = 0x1.555556p-3f;
 // range); smaller ones take IEEE division everywhere.
 constexpr float kFastMinScale = 0x1p-80f;
 constexpr int kQThreads = 256;
+// candidate codes the unrolled MSE walk covers (k in [0.5, 1] spans <= 9)
+constexpr int kMseCodes = 9;
 // A bounded wait: after this many wall-clock ticks (20 ms at the 100 MHz
 // counter) a workgroup stops waiting and computes what it waited for itself.
 constexpr uint64_t kWaitTicks = 2000000;
@@ -502,14 +504,38 @@ __device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int64_t b, in
         // (6 s <= amax_b) that cost only grows for smaller codes, so stop.
         uint32_t best = c_hi;
         float best_err = __builtin_inff();
-        for (int cc = (int)c_hi; cc >= (int)c_lo; --cc) {
-            const float s = tab.seff[cc], r = tab.rcp[cc];
-            if (max_term<FAST>(amax_b, s, r) > best_err) {
-                if (6.0f * s <= amax_b) break;
-                continue;
+        if (c_hi - c_lo < (uint32_t)kMseCodes) {
+            // the usual case (k in [0.5, 1] spans at most 9 codes): a fixed,
+            // unrolled walk whose table reads are all issued up front
+            float sv[kMseCodes], rv[kMseCodes];
+#pragma unroll
+            for (int j = 0; j < kMseCodes; ++j) {
+                const int cc = max((int)c_hi - j, 0);
+                sv[j] = tab.seff[cc];
+                rv[j] = tab.rcp[cc];
             }
-            const float err = block_error<FAST>(e, s, r);
-            if (err <= best_err) { best_err = err; best = (uint32_t)cc; }
+            bool live = true;
+#pragma unroll
+            for (int j = 0; j < kMseCodes; ++j) {
+                live = live && (int)c_hi - j >= (int)c_lo;
+                if (!live) continue;
+                if (max_term<FAST>(amax_b, sv[j], rv[j]) > best_err) {
+                    live = !(6.0f * sv[j] <= amax_b);
+                    continue;
+                }
+                const float err = block_error<FAST>(e, sv[j], rv[j]);
+                if (err <= best_err) { best_err = err; best = c_hi - (uint32_t)j; }
+            }
+        } else {
+            for (int cc = (int)c_hi; cc >= (int)c_lo; --cc) {
+                const float s = tab.seff[cc], r = tab.rcp[cc];
+                if (max_term<FAST>(amax_b, s, r) > best_err) {
+                    if (6.0f * s <= amax_b) break;
+                    continue;
+                }
+                const float err = block_error<FAST>(e, s, r);
+                if (err <= best_err) { best_err = err; best = (uint32_t)cc; }
+            }
         }
         a.scales_out[gb] = (uint8_t)best;
     }
