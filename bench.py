@@ -123,7 +123,7 @@ def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel's sources changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "kl_seg_kernel_traffic.json")
+    path = os.path.join(ROOT, "profiles", "kl_seg_bf16_kernel_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -272,7 +272,7 @@ def main():
         "parts": parts,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("kl_seg_kernel<true, 1>") if dom == "kl_fwd_bwd" else None},
+                     "traffic": measured_traffic("kl_seg_bf16_kernel<1>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -192,14 +192,19 @@ __device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_g, fl
     return e4m3_encode(raw);
 }
 
+// x / s correctly rounded for x >= 0 (+0 included; s = 0 gives +0)
+template <bool FAST>
+__device__ __forceinline__ float quotient_pos(float x, float s, float r)
+{
+    if constexpr (FAST) return div_rcp(x, s, r);
+    else return s > 0.0f ? x / s : 0.0f;
+}
+
 // x / s correctly rounded, with x's sign bit (s = 0 gives a signed zero)
 template <bool FAST>
 __device__ __forceinline__ float quotient(float x, float s, float r)
 {
-    float q;
-    if constexpr (FAST) q = div_rcp(x, s, r);
-    else q = s > 0.0f ? x / s : 0.0f;
-    return __builtin_copysignf(q, x);
+    return __builtin_copysignf(quotient_pos<FAST>(__builtin_fabsf(x), s, r), x);
 }
 
 // Code one unit (half a block; the lane pair owns the block).  Returns the
@@ -433,7 +438,7 @@ __device__ __forceinline__ float block_error(const float (&e)[16], float s, floa
     // order; magnitudes only (|x - dec * s| is symmetric in the sign)
     float q[16], g[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = quotient<FAST>(__builtin_fabsf(e[j]), s, r);
+    for (int j = 0; j < 16; ++j) q[j] = quotient_pos<FAST>(__builtin_fabsf(e[j]), s, r);
 #pragma unroll
     for (int j = 0; j < 16; j += 8) {
         uint32_t c = 0;
@@ -462,7 +467,7 @@ __device__ __forceinline__ float block_error(const float (&e)[16], float s, floa
 template <bool FAST>
 __device__ __forceinline__ float max_term(float amax_b, float s, float r)
 {
-    const float q = quotient<FAST>(amax_b, s, r);
+    const float q = quotient_pos<FAST>(amax_b, s, r);
     float g, unused;
     fp4_decode_pair<0>(fp4_encode_pair<0>(0u, q, 0.0f), g, unused);
     const float d = amax_b - g * s;
