@@ -11,6 +11,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
@@ -377,5 +378,73 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
         if (row_kl) row_kl[r] = kl;
         total += kl;
     }
+    return rows > 0 ? total / (double)rows : 0.0;
+}
+
+/* ------------------------------------------------------------------------
+ * Teacher-top-k KL ([Qwen] "3. QAD": the distillation run restricts the KD
+ * loss to the teacher's top-4096 vocabulary entries so that dense
+ * [seq, vocab] logits need not exist).  The page gives neither the selection
+ * rule at ties nor the normalisation; the reading taken:
+ *   tau = the k-th largest teacher logit of the row (k >= V: every entry);
+ *   S   = { v : t_v >= tau }   (every entry tied with tau is kept, so |S| >= k);
+ *   p~, q~ = softmax(t/T), softmax(s/T) renormalised over S;
+ *   row loss = sum_{v in S} p~_v (log p~_v - log q~_v);
+ *   gradient = (q~_v - p~_v) * grad_scale / T on S, 0 elsewhere.
+ * Binary64, straightforward: a sorted copy of the row gives tau.
+ * ---------------------------------------------------------------------- */
+static int cmp_desc(const void* a, const void* b)
+{
+    const double x = *(const double*)a, y = *(const double*)b;
+    return x < y ? 1 : x > y ? -1 : 0;
+}
+
+double orc_kl_topk_fwd_bwd(const void* teacher, const void* student, int dtype,
+                           int64_t rows, int64_t V, int64_t k, double T, double grad_scale,
+                           double* row_kl, double* grad, int64_t* row_count)
+{
+    double total = 0.0;
+    double* sorted = (double*)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    if (!sorted) return NAN;
+    const int64_t kk = k < V ? k : V;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t o = r * V;
+        for (int64_t v = 0; v < V; ++v) sorted[v] = load_d(teacher, dtype, o + v);
+        qsort(sorted, (size_t)V, sizeof(double), cmp_desc);
+        const double tau = sorted[kk - 1];
+        double mt = -INFINITY, ms = -INFINITY;
+        int64_t count = 0;
+        for (int64_t v = 0; v < V; ++v) {
+            const double tv = load_d(teacher, dtype, o + v);
+            if (!(tv >= tau)) continue;
+            ++count;
+            const double t = tv / T, s = load_d(student, dtype, o + v) / T;
+            if (t > mt) mt = t;
+            if (s > ms) ms = s;
+        }
+        double zt = 0.0, zs = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            if (!(load_d(teacher, dtype, o + v) >= tau)) continue;
+            zt += exp(load_d(teacher, dtype, o + v) / T - mt);
+            zs += exp(load_d(student, dtype, o + v) / T - ms);
+        }
+        const double lse_t = mt + log(zt), lse_s = ms + log(zs);
+        double kl = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            const double tv = load_d(teacher, dtype, o + v);
+            if (!(tv >= tau)) {
+                if (grad) grad[o + v] = 0.0;
+                continue;
+            }
+            const double logp = tv / T - lse_t, logq = load_d(student, dtype, o + v) / T - lse_s;
+            const double p = exp(logp);
+            kl += p * (logp - logq);
+            if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
+        }
+        if (row_kl) row_kl[r] = kl;
+        if (row_count) row_count[r] = count;
+        total += kl;
+    }
+    free(sorted);
     return rows > 0 ? total / (double)rows : 0.0;
 }

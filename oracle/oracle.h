@@ -105,6 +105,14 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
                       int64_t rows, int64_t V, double T, double grad_scale,
                       double* row_kl, double* grad);
 
+/* ---- teacher-top-k KL -----------------------------------------------------
+ * As orc_kl_fwd_bwd restricted to S = { v : t_v >= k-th largest teacher logit
+ * of the row } (ties kept), both distributions renormalised over S; gradient
+ * 0 outside S.  Optional row_count[rows] = |S|.  k >= 1.                    */
+double orc_kl_topk_fwd_bwd(const void* teacher, const void* student, int dtype,
+                           int64_t rows, int64_t V, int64_t k, double T, double grad_scale,
+                           double* row_kl, double* grad, int64_t* row_count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,7 @@ def _load():
             "orc_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
             "orc_mse_calibrate_blocks": (None, [vp, i64, f32, i32, f32, f32, vp, vp, vp, vp]),
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
+            "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -235,8 +236,33 @@ def kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0,
     return float(loss), row, g
 
 
+def kl_topk_fwd_bwd(teacher: np.ndarray, student: np.ndarray, k: int, T: float = 1.0,
+                    grad_scale: float | None = None, want_grad: bool = True):
+    """Binary64 KL restricted to the teacher's top-k entries of each row (all
+    entries tied with the k-th largest kept), both softmaxes renormalised over
+    that set; gradient 0 outside it.
+
+    Returns (mean loss, row losses f64[rows], gradient f64[rows, V] or None,
+    set sizes i64[rows]).
+    """
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    assert t.shape == s.shape and t.dtype == s.dtype and k >= 1
+    V = t.shape[-1]
+    rows = t.size // V if V else 0
+    if grad_scale is None:
+        grad_scale = 1.0 / rows if rows else 0.0
+    row = np.empty(rows, np.float64)
+    cnt = np.empty(rows, np.int64)
+    g = np.empty((rows, V), np.float64) if want_grad else None
+    loss = _load().orc_kl_topk_fwd_bwd(_ptr(t), _ptr(s), _dtype_code(t), rows, V, int(k), float(T),
+                                       float(grad_scale), _ptr(row), _ptr(g), _ptr(cnt))
+    return float(loss), row, g, cnt
+
+
 __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
+    "kl_topk_fwd_bwd",
 ]
