@@ -91,7 +91,8 @@ typedef enum {
     QAD_OP_AMAX = 0,          /* nvfp4_amax                                   */
     QAD_OP_QUANTIZE = 1,      /* nvfp4_quantize and nvfp4_qdq_fwd             */
     QAD_OP_MSE_CALIBRATE = 2, /* nvfp4_mse_calibrate                          */
-    QAD_OP_KL = 3             /* qad_kl_fwd_bwd: B = 1, R = tokens, C = vocab */
+    QAD_OP_KL = 3,            /* qad_kl_fwd_bwd: B = 1, R = tokens, C = vocab */
+    QAD_OP_KL_TOPK = 4        /* qad_kl_topk_fwd_bwd: B = 1, R = tokens, C = vocab */
 } qad_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -189,6 +190,25 @@ qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_
                             int64_t tokens, int64_t vocab, float temperature, float grad_scale,
                             float* loss_out, float* row_loss, void* grad_student, qad_dtype_t gt,
                             void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Teacher-top-k KL forward + backward ([Qwen] "3. QAD": the distillation run
+ * restricts the KD loss to the teacher's top-4096 vocabulary entries; the page
+ * gives neither the tie rule nor the normalisation).  Per token row:
+ *   tau = the k-th largest teacher logit (k >= vocab: the smallest);
+ *   S   = every entry with teacher logit >= tau (entries tied with tau are all
+ *         kept, so |S| >= min(k, vocab); -0 and +0 count as equal);
+ *   loss = KL(p~ || q~) with p~, q~ = softmax(t/T), softmax(s/T) renormalised
+ *          over S; gradient (q~ - p~) * grad_scale / T on S and exactly 0
+ *          elsewhere.
+ * Arguments as qad_kl_fwd_bwd, plus
+ *   k         : >= 1
+ *   workspace : qad_workspace_bytes(QAD_OP_KL_TOPK, 1, tokens, vocab) bytes
+ *               (per-row losses when row_loss is NULL; may be NULL then if
+ *               row_loss is given) */
+qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt,
+                                 int64_t tokens, int64_t vocab, int64_t k, float temperature,
+                                 float grad_scale, float* loss_out, float* row_loss, void* grad_student,
+                                 qad_dtype_t gt, void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* Synchronises `stream`, copies n floats from device memory `values` (an
  * amax_out or tscale_out array) and returns QAD_ERR_NONFINITE if any is a NaN

@@ -5,7 +5,7 @@ the C ABI in include/libqad.h); this package is its thin Python binding plus
 the seeded synthetic input generators.  Build with
 ``python -m nvfp4_quantization_aware_amd.build``.
 """
-from ._lib import (QAD_BF16, QAD_F32, QAD_OP_AMAX, QAD_OP_KL, QAD_OP_MSE_CALIBRATE,  # noqa: F401
-                   QAD_OP_QUANTIZE, QadError, lib, nvfp4_amax, nvfp4_mse_calibrate,
+from ._lib import (QAD_BF16, QAD_F32, QAD_OP_AMAX, QAD_OP_KL, QAD_OP_KL_TOPK,  # noqa: F401
+                   QAD_OP_MSE_CALIBRATE, QAD_OP_QUANTIZE, QadError, lib, nvfp4_amax, nvfp4_mse_calibrate,
                    nvfp4_qdq_bwd, nvfp4_qdq_fwd, nvfp4_quantize, qad_check_finite,
-                   qad_kl_fwd_bwd, qad_workspace_bytes, workspace)
+                   qad_kl_fwd_bwd, qad_kl_topk_fwd_bwd, qad_workspace_bytes, workspace)

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libqad.so")
 
 QAD_F32, QAD_BF16 = 0, 1
-QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL = 0, 1, 2, 3
+QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL, QAD_OP_KL_TOPK = 0, 1, 2, 3, 4
 STATUS = {0: "QAD_OK", 1: "QAD_ERR_INVALID_ARG", 2: "QAD_ERR_SHAPE", 3: "QAD_ERR_DTYPE",
           4: "QAD_ERR_ALIGNMENT", 5: "QAD_ERR_WORKSPACE", 6: "QAD_ERR_NONFINITE", 7: "QAD_ERR_HIP"}
 
@@ -33,6 +33,8 @@ SIGNATURES = {
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qad_kl_topk_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz,
+                                   _vp]),
     "qad_check_finite": (_int, [_vp, _i64, _vp]),
 }
 
@@ -204,6 +206,34 @@ def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: fl
     _check(lib().qad_kl_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, temperature,
                                 grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
                                 0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_fwd_bwd")
+    return loss_out, rows, grad
+
+
+def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, temperature: float = 1.0,
+                        grad_scale: float | None = None, grad_dtype=torch.bfloat16, row_loss=False,
+                        loss_out: torch.Tensor | None = None, grad: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None):
+    """KL over the teacher's top-k entries of each row (ties with the k-th
+    largest kept, both softmaxes renormalised over them).  Returns (loss
+    f32[1], row_loss f32[tokens] or None, grad or None)."""
+    if teacher.shape != student.shape or teacher.dim() != 2:
+        raise ValueError("teacher and student must both be [tokens, vocab]")
+    tokens, vocab = teacher.shape
+    dev = teacher.device
+    if grad_scale is None:
+        grad_scale = 1.0 / tokens if tokens else 0.0
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
+        row_loss if isinstance(row_loss, torch.Tensor) else None)
+    if grad is None and grad_dtype is not None:
+        grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
+    gt = _dt(grad) if grad is not None else QAD_BF16
+    if ws is None and rows is None:
+        ws = workspace(QAD_OP_KL_TOPK, 1, tokens, vocab, dev)
+    _check(lib().qad_kl_topk_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, int(k), temperature,
+                                     grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
+                                     0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topk_fwd_bwd")
     return loss_out, rows, grad
 
 

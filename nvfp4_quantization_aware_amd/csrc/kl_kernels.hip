@@ -503,6 +503,220 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, in
     if (threadIdx.x == 0) loss_out[0] = rows > 0 ? (float)(part[0] / (double)rows) : 0.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Teacher-top-k KL ([Qwen] "3. QAD": the distillation run restricts the KD
+// loss to the teacher's top-4096 vocabulary entries; the page gives no tie
+// rule and no normalisation).  Kept set of a row: every entry whose teacher
+// logit is at least the k-th largest (ties kept); both softmaxes renormalised
+// over it; gradient 0 elsewhere.  One workgroup of 1024 lanes per row:
+//   1. the k-th largest teacher logit, exactly: radix select over
+//      order-preserving integer keys (16-bit for bf16, 32-bit for fp32),
+//      digits of up to 12 bits from the top; each round counts, in an LDS
+//      histogram, the keys that match the digits chosen so far, and a suffix
+//      scan over the bins picks the digit holding rank k;
+//   2. the online softmax state of the kept entries, teacher and student;
+//   3. the gradient (q~ - p~) grad_scale / T on kept entries, 0 elsewhere.
+// Every step streams the teacher row again (a 1024-lane workgroup cannot hold
+// a 128K-logit row in registers without spilling).
+// ---------------------------------------------------------------------------
+constexpr int kTopThreads = 1024;
+constexpr int kDigitBits = 12;
+
+// order-preserving unsigned keys: a larger key is a larger value; -0 is
+// folded onto +0 so that equal values have equal keys
+__device__ __forceinline__ uint32_t key16(uint32_t h)
+{
+    h = h == 0x8000u ? 0u : h;
+    return (h & 0x8000u) ? (h ^ 0xFFFFu) : (h | 0x8000u);
+}
+
+__device__ __forceinline__ uint32_t key32(uint32_t u)
+{
+    u = u == 0x80000000u ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void teacher_keys(const Unit<BF16>& u, uint32_t (&k)[8])
+{
+    if constexpr (BF16) {
+        const uint32_t w[4] = {u.t[0].x, u.t[0].y, u.t[0].z, u.t[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { k[2 * i] = key16(w[i] & 0xFFFFu); k[2 * i + 1] = key16(w[i] >> 16); }
+    } else {
+        const uint32_t w[8] = {u.t[0].x, u.t[0].y, u.t[0].z, u.t[0].w, u.t[1].x, u.t[1].y, u.t[1].z, u.t[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) k[i] = key32(w[i]);
+    }
+}
+
+struct TopShared {
+    uint32_t hist[1 << kDigitBits];
+    uint32_t wave_tot[kTopThreads / 64];
+    uint32_t digit, above;
+    Stats part[kTopThreads / 64];
+};
+
+// inclusive prefix sum over the workgroup's lanes in lane order
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wave_tot)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t n = __shfl_up(v, o, 64);
+        if (lane >= o) v += n;
+    }
+    if (lane == 63) wave_tot[w] = v;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int i = 0; i < w; ++i) off += wave_tot[i];
+    __syncthreads();
+    return v + off;
+}
+
+// the key of the k-th largest teacher logit of the row (1 <= k <= vocab);
+// for_t(f) calls f(unit, valid) for each of the lane's teacher units
+template <bool BF16, class ForT>
+__device__ uint32_t kth_largest_key(uint32_t k, ForT for_t, TopShared& sh)
+{
+    constexpr int KB = BF16 ? 16 : 32;
+    uint32_t prefix = 0, remaining = k;
+    for (int used = 0; used < KB;) {
+        const int d = KB - used < kDigitBits ? KB - used : kDigitBits;
+        const int nb = 1 << d, shift = KB - used - d;
+        for (int i = threadIdx.x; i < nb; i += kTopThreads) sh.hist[i] = 0u;
+        __syncthreads();
+        for_t([&](const Unit<BF16>& u, bool valid) {
+            if (!valid) return;
+            uint32_t key[8];
+            teacher_keys<BF16>(u, key);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (used == 0 || (key[i] >> (KB - used)) == prefix) atomicAdd(&sh.hist[(key[i] >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        // lane l sums the g bins below nb - l g (from the top), then a scan
+        // gives every group the count above it; one group holds rank k
+        const int g = nb >= kTopThreads ? nb / kTopThreads : 1;
+        const int groups = nb / g;
+        const int top = nb - 1 - (int)threadIdx.x * g;
+        uint32_t local = 0;
+        if ((int)threadIdx.x < groups)
+            for (int b = 0; b < g; ++b) local += sh.hist[top - b];
+        const uint32_t incl = block_incl_scan(local, sh.wave_tot);
+        if ((int)threadIdx.x < groups && incl - local < remaining && remaining <= incl) {
+            uint32_t cum = incl - local;
+            for (int b = 0; b < g; ++b) {
+                const uint32_t h = sh.hist[top - b];
+                if (remaining <= cum + h) {
+                    sh.digit = (uint32_t)(top - b);
+                    sh.above = cum;
+                    break;
+                }
+                cum += h;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << d) | sh.digit;
+        remaining -= sh.above;
+        used += d;
+        __syncthreads();  // hist, digit and above are rewritten next round
+    }
+    return prefix;
+}
+
+template <bool BF16_IN, int GRAD>
+__global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t k, float c, float inv_t, float gmul)
+{
+    __shared__ TopShared sh;
+    const int64_t row = blockIdx.x;
+    const int64_t units = a.vocab >> 3;
+    const int64_t ubase = row * units;
+    const int UL = (int)((units + kTopThreads - 1) / kTopThreads);
+    const int tid = threadIdx.x;
+
+    // f(teacher unit, valid) over the lane's units
+    auto for_t = [&](auto f) {
+#pragma unroll 4
+        for (int j = 0; j < UL; ++j) {
+            const int64_t u = (int64_t)j * kTopThreads + tid;
+            Unit<BF16_IN> un;
+            un.load(a, ubase + u, u < units);
+            f(un, u < units);
+        }
+    };
+    const uint32_t tau = kth_largest_key<BF16_IN>(k, for_t, sh);
+
+    // f(teacher and student unit, valid, unit index) over the lane's units
+    auto for_ts = [&](auto f) {
+#pragma unroll 4
+        for (int j = 0; j < UL; ++j) {
+            const int64_t u = (int64_t)j * kTopThreads + tid;
+            Unit<BF16_IN> un;
+            un.load(a, ubase + u, u < units);
+            f(un, u < units, ubase + u);
+        }
+    };
+
+    // kept-set softmax state, online as in the full-vocabulary kernel
+    float mt = -__builtin_inff(), ms = -__builtin_inff(), zt = 0.0f, zs = 0.0f, at = 0.0f;
+    for_ts([&](const Unit<BF16_IN>& both, bool valid, int64_t) {
+        if (!valid) return;
+        uint32_t key[8];
+        teacher_keys<BF16_IN>(both, key);
+        float tv[8], sv[8], pt[8], ps[8];
+        both.values(tv, sv);
+        float umt = -__builtin_inff(), ums = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (key[i] >= tau) { umt = maxnan(umt, tv[i]); ums = maxnan(ums, sv[i]); }
+        }
+        const float nmt = maxnan(mt, umt * c), nms = maxnan(ms, ums * c);
+        const float ft = nmt == mt ? 1.0f : exp2_hw(mt - nmt);
+        const float fs = nms == ms ? 1.0f : exp2_hw(ms - nms);
+        mt = nmt;
+        ms = nms;
+        float pa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool kept = key[i] >= tau;
+            pt[i] = kept ? exp2_hw(__builtin_fmaf(tv[i], c, -mt)) : 0.0f;
+            ps[i] = kept ? exp2_hw(__builtin_fmaf(sv[i], c, -ms)) : 0.0f;
+            pa = kept ? __builtin_fmaf(pt[i], tv[i] - sv[i], pa) : pa;
+        }
+        zt = zt * ft + sum8(pt);
+        at = at * ft + pa;
+        zs = zs * fs + sum8(ps);
+    });
+    const Stats row_st = group_merge<kTopThreads>(Stats{mt, zt, at, ms, zs}, sh.part);
+    if (tid == 0)
+        a.row_loss[row] = (row_st.at / row_st.zt) * inv_t -
+                          kLn2 * ((row_st.mt - row_st.ms) + log2f(row_st.zt / row_st.zs));
+    if constexpr (GRAD != 0) {
+        const float wt = gmul / row_st.zt, ws = gmul / row_st.zs;
+        for_ts([&](const Unit<BF16_IN>& both, bool valid, int64_t u) {
+            if (!valid) return;
+            uint32_t key[8];
+            teacher_keys<BF16_IN>(both, key);
+            float tv[8], sv[8], g[8];
+            both.values(tv, sv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
+                const float eq = exp2_hw(__builtin_fmaf(sv[i], c, -row_st.ms));
+                g[i] = key[i] >= tau ? __builtin_fmaf(eq, ws, -(ep * wt)) : 0.0f;
+            }
+            if constexpr (GRAD == 1) {
+                stnt(a.grad, u, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                                    pack_bf16x2(g[6], g[7])});
+            } else {
+                stnt(a.grad, 2 * u, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
+                stnt(a.grad, 2 * u + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
+            }
+        });
+    }
+}
+
 // clear every tag a launch waits on (the whole records)
 __global__ void zero_records_kernel(uint32_t* rec, int64_t words)
 {
@@ -572,6 +786,37 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
                 else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
 #undef KR
             }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_kl_topk(const KlArgs& a, int64_t k, hipStream_t stream)
+{
+    if (a.tokens > 0 && a.vocab > 0) {
+        const float c = kLog2e / a.temperature;
+        const float inv_t = 1.0f / a.temperature;
+        const float gmul = a.grad_scale / a.temperature;
+        const uint32_t kk = (uint32_t)(k < a.vocab ? k : a.vocab);
+        const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
+        const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+        const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
+        const int64_t batch = (int64_t)1 << 20;  // rows per launch
+        for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+            KlArgs b = a;
+            b.tokens = min(batch, a.tokens - r0);
+            b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
+            b.student = static_cast<const char*>(a.student) + r0 * in_row;
+            b.row_loss = a.row_loss + r0;
+            if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
+            const dim3 grid((unsigned)b.tokens), block(kTopThreads);
+#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
+            if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
+            else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
+#undef KT
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

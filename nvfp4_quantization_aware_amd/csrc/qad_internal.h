@@ -78,5 +78,7 @@ struct KlArgs {
 // scratch of launch_kl: per-row losses, then per-row exchange records
 size_t kl_workspace_bytes(int64_t tokens, int64_t vocab);
 hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);
+// teacher-top-k KL (a.row_loss must hold tokens floats; k >= 1)
+hipError_t launch_kl_topk(const KlArgs& a, int64_t k, hipStream_t stream);
 
 } // namespace qad

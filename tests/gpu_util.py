@@ -40,12 +40,16 @@ def bf16_ulp(a: np.ndarray) -> np.ndarray:
     return np.maximum(2.0 ** (e - 7), 2.0**-133)
 
 
-def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, rel=1e-5):
+def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, rel=1e-5, zero_row_scale=0.0):
     """Gradient rule: per row, |g - g_ref| <= rel * max_row |g_ref| for a
     float32 gradient; for bf16, the bf16 rounding of a value within that band
-    (so additionally half a bf16 ulp)."""
+    (so additionally half a bf16 ulp).  A row whose reference gradient is 0
+    everywhere (p and q equal, e.g. a single kept entry) has no relative
+    scale; there `zero_row_scale` (grad_scale / T, the bound of |q - p| times
+    the factor) stands in for max_row |g_ref|."""
     g_ref = np.asarray(g_ref, np.float64)
-    tol = rel * np.abs(g_ref).max(axis=-1, keepdims=True)
+    row_max = np.abs(g_ref).max(axis=-1, keepdims=True)
+    tol = rel * np.where(row_max > 0, row_max, zero_row_scale)
     if g_dev.dtype == np.uint16:
         g = (g_dev.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         bound = tol + 0.5 * bf16_ulp(np.abs(g_ref) + tol)
@@ -53,7 +57,8 @@ def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, rel=1e-5):
         g = g_dev.astype(np.float64)
         bound = tol
         l2 = np.linalg.norm(g - g_ref, axis=-1)
-        assert np.all(l2 <= rel * np.linalg.norm(g_ref, axis=-1)), l2.max()
+        l2_ref = np.linalg.norm(g_ref, axis=-1)
+        assert np.all(l2 <= rel * np.where(l2_ref > 0, l2_ref, zero_row_scale * np.sqrt(g_ref.shape[-1]))), l2.max()
     err = np.abs(g - g_ref)
     bad = err > bound
     assert not bad.any(), "worst excess %g at %s" % ((err - bound).max(), np.argwhere(bad)[:3])

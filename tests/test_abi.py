@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -77,8 +77,11 @@ def test_workspace_sizes(L):
         rec = ((10 * W + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
         expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
         assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
+    # top-k KL: the per-row losses only
+    for tokens, vocab in ((8192, 131072), (3, 8), (1000, 248320)):
+        assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPK, 1, tokens, vocab) == -(-(tokens * 4) // 256) * 256
     assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
-    for op in range(4):
+    for op in range(5):
         assert L.qad_workspace_bytes(op, 1, 1, 16) % 256 == 0
 
 
@@ -174,6 +177,33 @@ def test_kl_rejects(L):
     assert call(a11=None, a12=0) == WS                # no workspace
     assert call(a12=16) == WS
     assert call(a11=P * 5 + 64) == ALIGN
+
+
+def test_kl_topk_rejects(L):
+    f = L.qad_kl_topk_fwd_bwd
+    good = [P, P * 2, 1, 4, 64, 16, 1.0, 0.25, P * 3, None, P * 4, 1, P * 5, 1 << 16, None]
+
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a2=9) == DTYPE
+    assert call(a11=9) == DTYPE
+    assert call(a4=60) == SHAPE                       # vocab % 8
+    assert call(a3=-1) == SHAPE
+    assert call(a5=0) == INVALID                      # k
+    assert call(a5=-3) == INVALID
+    assert call(a6=0.0) == INVALID                    # temperature
+    assert call(a7=float("nan")) == INVALID
+    assert call(a8=None) == INVALID                   # loss_out
+    assert call(a1=None) == INVALID
+    assert call(a0=P_ODD) == ALIGN
+    assert call(a10=P + 32) == INVALID                # gradient overlaps the teacher
+    assert call(a12=None, a13=0) == WS                # no workspace and no row_loss
+    assert call(a13=16) == WS
+    assert call(a12=P * 5 + 64) == ALIGN
 
 
 def test_check_finite_rejects(L):
