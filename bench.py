@@ -198,6 +198,30 @@ def cpu_baseline(fraction: float):
     }
 
 
+def time_topk(wl, dev, k=4096, iters=10):
+    """Teacher-top-k KL (k = 4096, the pages' run) on the same 8192 x 131072
+    logits, timed on its own after the step (not part of the step's value)."""
+    import torch
+    q = wl.q
+    N5, V5 = wl.shapes["kl"]
+    ws = q.workspace(q.QAD_OP_KL_TOPK, 1, N5, V5, dev)
+    print("[bench] top-k KL", file=sys.stderr, flush=True)
+    for _ in range(2):
+        q.qad_kl_topk_fwd_bwd(wl.t5, wl.s5, k, loss_out=wl.l5, grad=wl.gr5, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.qad_kl_topk_fwd_bwd(wl.t5, wl.s5, k, loss_out=wl.l5, grad=wl.gr5, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 6 * N5 * V5
+    return {"k": k, "ms": round(ms, 4), "tokens_per_s": round(N5 / (ms * 1e-3), 1),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes": nbytes, "iters": iters}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -275,6 +299,7 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
+    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

@@ -203,8 +203,8 @@ qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_
  * Arguments as qad_kl_fwd_bwd, plus
  *   k         : >= 1
  *   workspace : qad_workspace_bytes(QAD_OP_KL_TOPK, 1, tokens, vocab) bytes
- *               (per-row losses when row_loss is NULL; may be NULL then if
- *               row_loss is given) */
+ *               (the qad_kl_fwd_bwd workspace followed by one float per row
+ *               for the thresholds) */
 qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt,
                                  int64_t tokens, int64_t vocab, int64_t k, float temperature,
                                  float grad_scale, float* loss_out, float* row_loss, void* grad_student,

@@ -229,7 +229,7 @@ def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, te
     if grad is None and grad_dtype is not None:
         grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
     gt = _dt(grad) if grad is not None else QAD_BF16
-    if ws is None and rows is None:
+    if ws is None:
         ws = workspace(QAD_OP_KL_TOPK, 1, tokens, vocab, dev)
     _check(lib().qad_kl_topk_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, int(k), temperature,
                                      grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),

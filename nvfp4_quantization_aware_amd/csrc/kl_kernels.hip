@@ -166,8 +166,8 @@ __device__ __forceinline__ int64_t lane_unit(int64_t seg_u0, int k) { return seg
 // arithmetic is the same in every form (a unit past the row end is skipped
 // and a valid one takes the same operations), so all give bit-identical
 // states.
-template <bool BF16, bool UNROLL, bool FULL, class Get>
-__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, Get get)
+template <bool BF16, bool UNROLL, bool FULL, bool TOPK, class Get>
+__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, float tau, Get get)
 {
     constexpr int kUnroll = UNROLL ? kSegUnits : 1;
     float mt = -__builtin_inff(), ms = -__builtin_inff();
@@ -180,9 +180,17 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         if (!valid) continue;
         float tv[8], sv[8], pt[8], ps[8];
         u.values(tv, sv);
+        bool kept[8];
+        float tk[8], sk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kept[i] = !TOPK || tv[i] >= tau;
+            tk[i] = kept[i] ? tv[i] : -__builtin_inff();
+            sk[i] = kept[i] ? sv[i] : -__builtin_inff();
+        }
         // c > 0: the max of the scaled logits is the scaled max
-        const float nmt = maxnan(mt, max8(tv) * c);
-        const float nms = maxnan(ms, max8(sv) * c);
+        const float nmt = maxnan(mt, max8(tk) * c);
+        const float nms = maxnan(ms, max8(sk) * c);
         // equal maxima (also both -inf) need no rescaling
         const float ft = nmt == mt ? 1.0f : exp2_hw(mt - nmt);
         const float fs = nms == ms ? 1.0f : exp2_hw(ms - nms);
@@ -193,6 +201,7 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         for (int i = 0; i < 8; ++i) {
             pt[i] = exp2_hw(__builtin_fmaf(tv[i], c, -mt));
             ps[i] = exp2_hw(__builtin_fmaf(sv[i], c, -ms));
+            if (TOPK) { pt[i] = kept[i] ? pt[i] : 0.0f; ps[i] = kept[i] ? ps[i] : 0.0f; }
             pa = __builtin_fmaf(pt[i], tv[i] - sv[i], pa);
         }
         zt = zt * ft + sum8(pt);
@@ -205,10 +214,10 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
 }
 
 // every lane's state over a segment held in registers
-template <bool BF16, bool FULL, class Regs>
-__device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c)
+template <bool BF16, bool FULL, bool TOPK, class Regs>
+__device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c, float tau)
 {
-    return lane_state<BF16, true, FULL>(seg_u0, units, c, [&](int k, Unit<BF16>& u) { u = m[k]; });
+    return lane_state<BF16, true, FULL, TOPK>(seg_u0, units, c, tau, [&](int k, Unit<BF16>& u) { u = m[k]; });
 }
 
 // per-row exchange record for W segments, in words (whole 128-byte lines)
@@ -292,10 +301,11 @@ __device__ __forceinline__ void seg_load(SegRegs<BF16_IN>& m, const KlArgs& a, i
 }
 
 // pass 1: the segment's state, identical in every lane
-template <bool BF16_IN, bool FULL>
-__device__ __forceinline__ Stats seg_pass1(SegRegs<BF16_IN>& m, int64_t seg_u0, int64_t units, float c, Stats* part)
+template <bool BF16_IN, bool FULL, bool TOPK>
+__device__ __forceinline__ Stats seg_pass1(SegRegs<BF16_IN>& m, int64_t seg_u0, int64_t units, float c, float tau,
+                                           Stats* part)
 {
-    const Stats lane_st = lane_state_regs<BF16_IN, FULL>(m, seg_u0, units, c);
+    const Stats lane_st = lane_state_regs<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau);
     const Stats st = group_merge<kSegThreads>(lane_st, part);
 #pragma unroll
     for (int k = 0; k < kSegUnits; ++k)
@@ -313,9 +323,9 @@ struct SegShared {
 // the row's statistics (exchange + merge), its loss (segment 0) and pass 2:
 // p = 2^(c t - m_row) / Z_row and q alike, times grad_scale / T, written as
 // the gradient from the logits still held in registers
-template <bool BF16_IN, int GRAD, bool FULL>
+template <bool BF16_IN, int GRAD, bool FULL, bool TOPK>
 __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a, int W, int64_t row, int seg,
-                                           const Stats& my_seg, float c, float inv_t, float gmul,
+                                           const Stats& my_seg, float c, float tau, float inv_t, float gmul,
                                            uint32_t* rec_base, SegShared& sh)
 {
     const int64_t units = a.vocab >> 3;
@@ -329,7 +339,7 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {
                 const int64_t o_u0 = s * kSegSpan;
-                const Stats ol = lane_state<BF16_IN, false, false>(o_u0, units, c, [&](int k, Unit<BF16_IN>& u) {
+                const Stats ol = lane_state<BF16_IN, false, false, TOPK>(o_u0, units, c, tau, [&](int k, Unit<BF16_IN>& u) {
                     u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
                 });
                 const Stats os = group_merge<kSegThreads>(ol, sh.part);
@@ -358,6 +368,7 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
                 const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
                 const float eq = exp2_hw(__builtin_fmaf(sv[i], c, -row_st.ms));
                 g[i] = __builtin_fmaf(eq, ws, -(ep * wt));
+                if (TOPK) g[i] = tv[i] >= tau ? g[i] : 0.0f;
             }
             const int64_t u = row_unit0 + lane_unit(seg_u0, k);
             if constexpr (GRAD == 1) {
@@ -376,47 +387,50 @@ __device__ __forceinline__ uint64_t* rec_of(uint32_t* rec_base, int64_t row, int
     return reinterpret_cast<uint64_t*>(rec_base + row * rec_words(W));
 }
 
-template <bool BF16_IN, int GRAD, bool FULL>
+template <bool BF16_IN, int GRAD, bool FULL, bool TOPK>
 __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, int seg, float c, float inv_t, float gmul,
                                          uint32_t* rec_base, SegShared& sh)
 {
     const int64_t units = a.vocab >> 3;
     const int64_t seg_u0 = seg * kSegSpan;
+    const float tau = TOPK ? a.tau[row] : 0.0f;
     SegRegs<BF16_IN> m;
     seg_load<BF16_IN, FULL>(m, a, row * units, seg_u0, units);
-    const Stats st = seg_pass1<BF16_IN, FULL>(m, seg_u0, units, c, sh.part);
+    const Stats st = seg_pass1<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau, sh.part);
     if (W > 1) publish(rec_of(rec_base, row, W), seg, st);
-    seg_finish<BF16_IN, GRAD, FULL>(m, a, W, row, seg, st, c, inv_t, gmul, rec_base, sh);
+    seg_finish<BF16_IN, GRAD, FULL, TOPK>(m, a, W, row, seg, st, c, tau, inv_t, gmul, rec_base, sh);
 }
 
 // One workgroup per segment: load, pass 1, publish, wait, pass 2.  Segments
 // that lie wholly inside the row (all but a ragged last one) take a form
 // without per-unit bounds tests.
-template <bool BF16_IN, int GRAD> // GRAD: 0 none, 1 bf16, 2 fp32
+// TOPK: only the entries whose teacher logit is at least the row's threshold
+// a.tau[row] count (the kept set of the teacher-top-k KL); gradient 0 elsewhere
+template <bool BF16_IN, int GRAD, bool TOPK> // GRAD: 0 none, 1 bf16, 2 fp32
 __device__ __forceinline__ void seg_entry(const KlArgs& a, int W, float c, float inv_t, float gmul, uint32_t* rec_base)
 {
     __shared__ SegShared sh;
     const int64_t row = blockIdx.x / W;
     const int seg = (int)(blockIdx.x - row * W);
     if ((seg + 1) * kSegSpan <= (a.vocab >> 3))
-        seg_body<BF16_IN, GRAD, true>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+        seg_body<BF16_IN, GRAD, true, TOPK>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
     else
-        seg_body<BF16_IN, GRAD, false>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+        seg_body<BF16_IN, GRAD, false, TOPK>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
 }
 
 // bf16 logits: held to 128 VGPRs, four workgroups per CU
-template <int GRAD>
+template <int GRAD, bool TOPK>
 __global__ __launch_bounds__(kSegThreads, 4) void kl_seg_bf16_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
                                                                      uint32_t* rec_base)
 {
-    seg_entry<true, GRAD>(a, W, c, inv_t, gmul, rec_base);
+    seg_entry<true, GRAD, TOPK>(a, W, c, inv_t, gmul, rec_base);
 }
 
-template <int GRAD>
+template <int GRAD, bool TOPK>
 __global__ __launch_bounds__(kSegThreads) void kl_seg_f32_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
                                                                  uint32_t* rec_base)
 {
-    seg_entry<false, GRAD>(a, W, c, inv_t, gmul, rec_base);
+    seg_entry<false, GRAD, TOPK>(a, W, c, inv_t, gmul, rec_base);
 }
 
 // ---------------------------------------------------------------------------
@@ -516,8 +530,10 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, in
 //      scan over the bins picks the digit holding rank k;
 //   2. the online softmax state of the kept entries, teacher and student;
 //   3. the gradient (q~ - p~) grad_scale / T on kept entries, 0 elsewhere.
-// Every step streams the teacher row again (a 1024-lane workgroup cannot hold
-// a 128K-logit row in registers without spilling).
+// Rows of at most kMaxSegments record segments split the work: the threshold
+// kernel below finds the k-th largest teacher logit per row, then the
+// one-pass segment kernels run masked by it (TOPK).  Longer rows take
+// kl_topk_kernel, one workgroup per row that streams the row in every step.
 // ---------------------------------------------------------------------------
 constexpr int kTopThreads = 1024;
 constexpr int kDigitBits = 12;
@@ -717,6 +733,48 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t
     }
 }
 
+// the value whose key is `key` (inverse of key16 / key32)
+template <bool BF16>
+__device__ __forceinline__ float value_of_key(uint32_t key)
+{
+    if constexpr (BF16) {
+        const uint32_t h = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xFFFFu);
+        return as_f(h << 16);
+    } else {
+        return as_f((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+    }
+}
+
+// Threshold of the teacher-top-k KL for the segment kernels: tau_out[row] =
+// the k-th largest teacher logit of the row (the radix select above), the
+// teacher row streamed once per round.  (Holding a 128K-logit row in
+// registers allows one 1024-lane workgroup per CU and measured slower than
+// two streaming ones, whose loads and LDS histograms overlap.)
+template <bool BF16>
+__global__ __launch_bounds__(kTopThreads) void kl_topk_tau_kernel(const void* teacher, int64_t vocab, uint32_t k,
+                                                                  float* tau_out)
+{
+    __shared__ TopShared sh;
+    constexpr int V = Unit<BF16>::V;
+    const int64_t row = blockIdx.x;
+    const int64_t units = vocab >> 3;
+    const int64_t ubase = row * units;
+    const int UL = (int)((units + kTopThreads - 1) / kTopThreads);
+    const int tid = threadIdx.x;
+    auto for_t = [&](auto f) {
+#pragma unroll 4
+        for (int j = 0; j < UL; ++j) {
+            const int64_t u = (int64_t)j * kTopThreads + tid;
+            Unit<BF16> un;
+#pragma unroll
+            for (int q = 0; q < V; ++q) un.t[q] = u < units ? ldnt(teacher, V * (ubase + u) + q) : v4u{0u, 0u, 0u, 0u};
+            f(un, u < units);
+        }
+    };
+    const uint32_t key = kth_largest_key<BF16>(k, for_t, sh);
+    if (tid == 0) tau_out[row] = value_of_key<BF16>(key);
+}
+
 // clear every tag a launch waits on (the whole records)
 __global__ void zero_records_kernel(uint32_t* rec, int64_t words)
 {
@@ -741,84 +799,122 @@ size_t kl_workspace_bytes(int64_t tokens, int64_t vocab)
     return ((rows + 255) & ~(size_t)255) + recs;
 }
 
+namespace {
+
+// the one-pass segment kernels (rows of at most kMaxSegments record segments)
+// or the two-pass row kernel; TOPK: masked by a.tau
+hipError_t launch_rows(const KlArgs& a, void* workspace, bool topk, hipStream_t stream)
+{
+    const float c = kLog2e / a.temperature;
+    const float inv_t = 1.0f / a.temperature;
+    const float gmul = a.grad_scale / a.temperature;
+    const int W = segments(a.vocab);
+    const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
+    uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
+    if (W > 1 && W <= kMaxSegments) {
+        const int64_t n = a.tokens * rec_words(W);
+        hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)min((n + 255) / 256, (int64_t)65536)), dim3(256), 0,
+                           stream, rec, n);
+    }
+    // rows in batches, so that no grid exceeds 2^22 workgroups
+    const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+    const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
+    const int64_t batch = W <= kMaxSegments ? ((int64_t)1 << 22) / W : (int64_t)1 << 20;
+    for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+        KlArgs b = a;
+        b.tokens = min(batch, a.tokens - r0);
+        b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
+        b.student = static_cast<const char*>(a.student) + r0 * in_row;
+        b.row_loss = a.row_loss + r0;
+        if (a.tau) b.tau = a.tau + r0;
+        if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
+        if (W <= kMaxSegments) {
+            uint32_t* brec = rec + r0 * rec_words(W);
+            const dim3 grid((unsigned)(b.tokens * W)), block(kSegThreads);
+#define KS(K, GM, TK) hipLaunchKernelGGL((K<GM, TK>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
+#define KS3(K, TK) { if (gmode == 0) KS(K, 0, TK); else if (gmode == 1) KS(K, 1, TK); else KS(K, 2, TK); }
+            if (a.bf16_in) { if (topk) KS3(kl_seg_bf16_kernel, true) else KS3(kl_seg_bf16_kernel, false) }
+            else { if (topk) KS3(kl_seg_f32_kernel, true) else KS3(kl_seg_f32_kernel, false) }
+#undef KS3
+#undef KS
+        } else {
+            const dim3 grid((unsigned)b.tokens), block(kRowThreads);
+#define KR(BF, GM) hipLaunchKernelGGL((kl_row_kernel<BF, GM>), grid, block, 0, stream, b, c, inv_t, gmul)
+            if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
+            else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
+#undef KR
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+} // namespace
+
 hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
 {
     if (a.tokens > 0 && a.vocab > 0) {
-        const float c = kLog2e / a.temperature;
-        const float inv_t = 1.0f / a.temperature;
-        const float gmul = a.grad_scale / a.temperature;
-        const int W = segments(a.vocab);
-        const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
-        uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                    (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
-        if (W > 1 && W <= kMaxSegments) {
-            const int64_t n = a.tokens * rec_words(W);
-            hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)min((n + 255) / 256, (int64_t)65536)), dim3(256), 0,
-                               stream, rec, n);
-        }
-        // rows in batches, so that no grid exceeds 2^22 workgroups
-        const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
-        const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
-        const int64_t batch = W <= kMaxSegments ? ((int64_t)1 << 22) / W : (int64_t)1 << 20;
-        for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
-            KlArgs b = a;
-            b.tokens = min(batch, a.tokens - r0);
-            b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
-            b.student = static_cast<const char*>(a.student) + r0 * in_row;
-            b.row_loss = a.row_loss + r0;
-            if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
-            if (W <= kMaxSegments) {
-                uint32_t* brec = rec + r0 * rec_words(W);
-                const dim3 grid((unsigned)(b.tokens * W)), block(kSegThreads);
-#define KS(K, GM) hipLaunchKernelGGL((K<GM>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
-                if (a.bf16_in) {
-                    if (gmode == 0) KS(kl_seg_bf16_kernel, 0); else if (gmode == 1) KS(kl_seg_bf16_kernel, 1);
-                    else KS(kl_seg_bf16_kernel, 2);
-                } else {
-                    if (gmode == 0) KS(kl_seg_f32_kernel, 0); else if (gmode == 1) KS(kl_seg_f32_kernel, 1);
-                    else KS(kl_seg_f32_kernel, 2);
-                }
-#undef KS
-            } else {
-                const dim3 grid((unsigned)b.tokens), block(kRowThreads);
-#define KR(BF, GM) hipLaunchKernelGGL((kl_row_kernel<BF, GM>), grid, block, 0, stream, b, c, inv_t, gmul)
-                if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
-                else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
-#undef KR
-            }
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+        KlArgs b = a;
+        b.tau = nullptr;
+        hipError_t e = launch_rows(b, workspace, false, stream);
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
     return hipGetLastError();
 }
 
-hipError_t launch_kl_topk(const KlArgs& a, int64_t k, hipStream_t stream)
+size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab)
+{
+    return kl_workspace_bytes(tokens, vocab) + (((size_t)tokens * 4 + 255) & ~(size_t)255);
+}
+
+hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream_t stream)
 {
     if (a.tokens > 0 && a.vocab > 0) {
-        const float c = kLog2e / a.temperature;
-        const float inv_t = 1.0f / a.temperature;
-        const float gmul = a.grad_scale / a.temperature;
         const uint32_t kk = (uint32_t)(k < a.vocab ? k : a.vocab);
-        const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
-        const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
-        const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
-        const int64_t batch = (int64_t)1 << 20;  // rows per launch
-        for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+        if (segments(a.vocab) <= kMaxSegments) {
+            // thresholds, then the one-pass segment kernels masked by them
+            float* tau = reinterpret_cast<float*>(static_cast<char*>(workspace) + kl_workspace_bytes(a.tokens, a.vocab));
+            const int64_t batch = (int64_t)1 << 20;
+            const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+            for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+                const dim3 grid((unsigned)min(batch, a.tokens - r0)), block(kTopThreads);
+                const void* t = static_cast<const char*>(a.teacher) + r0 * in_row;
+                if (a.bf16_in) hipLaunchKernelGGL((kl_topk_tau_kernel<true>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
+                else hipLaunchKernelGGL((kl_topk_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
             KlArgs b = a;
-            b.tokens = min(batch, a.tokens - r0);
-            b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
-            b.student = static_cast<const char*>(a.student) + r0 * in_row;
-            b.row_loss = a.row_loss + r0;
-            if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
-            const dim3 grid((unsigned)b.tokens), block(kTopThreads);
-#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
-            if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
-            else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
-#undef KT
-            hipError_t e = hipGetLastError();
+            b.tau = tau;
+            hipError_t e = launch_rows(b, workspace, true, stream);
             if (e != hipSuccess) return e;
+        } else {
+            // very long rows: one workgroup per row streams it in every step
+            const float c = kLog2e / a.temperature;
+            const float inv_t = 1.0f / a.temperature;
+            const float gmul = a.grad_scale / a.temperature;
+            const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
+            const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+            const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
+            const int64_t batch = (int64_t)1 << 20;
+            for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+                KlArgs b = a;
+                b.tokens = min(batch, a.tokens - r0);
+                b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
+                b.student = static_cast<const char*>(a.student) + r0 * in_row;
+                b.row_loss = a.row_loss + r0;
+                if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
+                const dim3 grid((unsigned)b.tokens), block(kTopThreads);
+#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
+                if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
+                else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
+#undef KT
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
         }
     }
     hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);

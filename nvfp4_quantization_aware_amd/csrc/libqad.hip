@@ -123,7 +123,7 @@ size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
     case QAD_OP_QUANTIZE:
     case QAD_OP_MSE_CALIBRATE: return record_bytes(B, R * C);
     case QAD_OP_KL: return round256(qad::kl_workspace_bytes(R, C));
-    case QAD_OP_KL_TOPK: return round256((size_t)R * 4);
+    case QAD_OP_KL_TOPK: return round256(qad::kl_topk_workspace_bytes(R, C));
     }
     return 0;
 }
@@ -269,7 +269,7 @@ qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_d
         if (ranges_overlap(teacher, ib, grad_student, gb) || ranges_overlap(student, ib, grad_student, gb))
             return QAD_ERR_INVALID_ARG;
     }
-    if (tokens > 0 && !row_loss) {
+    if (tokens > 0) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_KL_TOPK, 1, tokens, vocab)) return QAD_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
     }
@@ -285,7 +285,7 @@ qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_d
     a.loss_out = loss_out;
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
-    return hip_status(qad::launch_kl_topk(a, k, hs(stream)));
+    return hip_status(qad::launch_kl_topk(a, k, workspace, hs(stream)));
 }
 
 qad_status_t qad_check_finite(const float* values, int64_t n, qad_stream_t stream)

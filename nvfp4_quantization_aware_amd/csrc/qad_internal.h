@@ -74,11 +74,13 @@ struct KlArgs {
     float* loss_out;
     void* grad;                // null: forward only
     bool grad_bf16;
+    const float* tau = nullptr;  // teacher-top-k thresholds per row (null: full vocabulary)
 };
 // scratch of launch_kl: per-row losses, then per-row exchange records
 size_t kl_workspace_bytes(int64_t tokens, int64_t vocab);
 hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);
-// teacher-top-k KL (a.row_loss must hold tokens floats; k >= 1)
-hipError_t launch_kl_topk(const KlArgs& a, int64_t k, hipStream_t stream);
+// teacher-top-k KL (k >= 1): the KL workspace followed by per-row thresholds
+size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab);
+hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream_t stream);
 
 } // namespace qad

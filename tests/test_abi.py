@@ -77,9 +77,10 @@ def test_workspace_sizes(L):
         rec = ((10 * W + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
         expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
         assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
-    # top-k KL: the per-row losses only
-    for tokens, vocab in ((8192, 131072), (3, 8), (1000, 248320)):
-        assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPK, 1, tokens, vocab) == -(-(tokens * 4) // 256) * 256
+    # top-k KL: the KL workspace, then one float per row (thresholds)
+    for tokens, vocab in ((8192, 131072), (3, 8), (1000, 248320), (3, 1 << 22)):
+        kl = L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab)
+        assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPK, 1, tokens, vocab) == kl + -(-(tokens * 4) // 256) * 256
     assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
     for op in range(5):
         assert L.qad_workspace_bytes(op, 1, 1, 16) % 256 == 0
@@ -201,7 +202,7 @@ def test_kl_topk_rejects(L):
     assert call(a1=None) == INVALID
     assert call(a0=P_ODD) == ALIGN
     assert call(a10=P + 32) == INVALID                # gradient overlaps the teacher
-    assert call(a12=None, a13=0) == WS                # no workspace and no row_loss
+    assert call(a12=None, a13=0) == WS                # no workspace
     assert call(a13=16) == WS
     assert call(a12=P * 5 + 64) == ALIGN
 

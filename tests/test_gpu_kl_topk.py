@@ -67,6 +67,7 @@ def run_and_check(dev, orc, t, s, k, T, g_dt, label, grad_scale=None):
     (3, 8, 3, 1.0, torch.bfloat16, torch.bfloat16),
     (4, 131072, 4096, 1.0, torch.bfloat16, torch.bfloat16),
     (3, 24584, 300, 1.0, torch.float32, torch.bfloat16),
+    (2, (1 << 20) + 8, 4096, 1.0, torch.bfloat16, torch.bfloat16),  # past 64 record segments: one workgroup per row
 ])
 def test_topk_small(dev, orc, tokens, vocab, k, T, in_dt, g_dt):
     t, s = synth.logits_bf16(tokens=tokens, vocab=vocab, seed=tokens * 11 + vocab + k)
