@@ -296,7 +296,7 @@ def main():
         "parts": parts,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("kl_seg_bf16_kernel<1>") if dom == "kl_fwd_bwd" else None},
+                     "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
     out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev)}
