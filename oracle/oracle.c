@@ -240,6 +240,36 @@ void orc_nvfp4_quantize_blocks(const void* x, int dtype, int64_t nblocks, float 
 }
 
 /* ------------------------------------------------------------------------
+ * FP8 (E4M3) per-tensor simulated quantization.  [Qwen] section "3. QAD"
+ * (the table of quantized components: attention projections FP8 W8A8, KV
+ * cache FP8) and [Nano] "NVFP4-Format und warum es wichtig ist?" (FP8 KV
+ * cache) name the format but not its scaling; the reading taken is one
+ * FP32 scale per tensor mapping the tensor amax onto the E4M3 maximum:
+ *   s    = amax/448 (1 for an all-zero tensor), or a given (frozen) s;
+ *   code = signbit(x)<<7 | E4M3(fl(|x|/s))   (nearest even, saturating);
+ *   y    = bf16(fl(dec(code) * s)).
+ * ---------------------------------------------------------------------- */
+void orc_fp8_quantize(const void* x, int dtype, int64_t n, const float* tscale_in,
+                      uint8_t* codes, float* tscale, uint16_t* y)
+{
+    float s;
+    if (tscale_in) {
+        s = *tscale_in;
+    } else {
+        const float amax = orc_amax(x, dtype, n);
+        s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    if (tscale) *tscale = s;
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = load_x(x, dtype, i);
+        const float q = fabsf(v) / s;
+        const uint8_t c = (uint8_t)(orc_e4m3_encode(q) | (signbit(v) ? 0x80 : 0x00));
+        if (codes) codes[i] = c;
+        if (y) y[i] = orc_bf16_from_f32(orc_e4m3_decode(c) * s);
+    }
+}
+
+/* ------------------------------------------------------------------------
  * MSE calibration (frozen-scale variant, [Lightning] section "量化尺度处理策略":
  * the MSE search is too expensive to redo every step, so its scales are
  * calibrated once and then kept fixed while only the weights train).

@@ -97,6 +97,13 @@ void orc_mse_calibrate_blocks(const float* blocks, int64_t nblocks, float s_g,
                               uint8_t* scales, float* err_out,
                               uint8_t* cand_codes, float* cand_err);
 
+/* ---- FP8 (E4M3) per-tensor QDQ ---------------------------------------------
+ * x: n elements of dtype.  tscale_in NULL: dynamic s = amax/448 (1 for an
+ * all-zero tensor); else s = *tscale_in (> 0).  Optional codes[n] (E4M3 with
+ * the sign of x in bit 7), tscale[1], y[n] (bf16 bits).                    */
+void orc_fp8_quantize(const void* x, int dtype, int64_t n, const float* tscale_in,
+                      uint8_t* codes, float* tscale, uint16_t* y);
+
 /* ---- KL(teacher || student) ---------------------------------------------
  * teacher, student: [rows][V] in dtype (0 fp32, 1 bf16).
  * Writes row_kl[rows] (binary64, nats), optional grad[rows][V] (binary64) =

@@ -61,6 +61,7 @@ def _load():
             "orc_mse_kgrid": (None, [i32, f32, f32, vp]),
             "orc_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
             "orc_mse_calibrate_blocks": (None, [vp, i64, f32, i32, f32, f32, vp, vp, vp, vp]),
+            "orc_fp8_quantize": (None, [vp, i32, i64, vp, vp, vp, vp]),
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
             "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
         }
@@ -214,6 +215,22 @@ def mse_calibrate_blocks(blocks: np.ndarray, s_g: float, n_cand: int = 64,
     return scales, err
 
 
+def fp8_quantize(x: np.ndarray, tscale: float | None = None):
+    """FP8 (E4M3) per-tensor QDQ of one tensor (any shape).
+
+    Returns (codes u8 like x, tensor scale f32, y bf16 bits u16 like x).
+    tscale None: dynamic amax/448; else the given (frozen) scale.
+    """
+    x = np.ascontiguousarray(x)
+    n = x.size
+    codes = np.empty(x.shape, np.uint8)
+    y = np.empty(x.shape, np.uint16)
+    ts = np.empty(1, np.float32)
+    tin = None if tscale is None else np.array([tscale], np.float32)
+    _load().orc_fp8_quantize(_ptr(x), _dtype_code(x), n, _ptr(tin), _ptr(codes), _ptr(ts), _ptr(y))
+    return codes, float(ts[0]), y
+
+
 # ---- KL ---------------------------------------------------------------------
 def kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0,
                grad_scale: float | None = None, want_grad: bool = True):
@@ -264,5 +281,5 @@ __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
-    "kl_topk_fwd_bwd",
+    "kl_topk_fwd_bwd", "fp8_quantize",
 ]
