@@ -222,6 +222,32 @@ def time_topk(wl, dev, k=4096, iters=10):
             "bytes": nbytes, "iters": iters}
 
 
+def time_fp8(wl, iters=10):
+    """FP8 (E4M3) per-tensor QDQ forward with dynamic scales on the MoE weight
+    batch (one pass, per-expert scales) and on the activation tensor (amax
+    pass first), timed on their own after the step."""
+    import torch
+    q = wl.q
+    res = {}
+    for name, x, y, ws in (("fp8_qdq_fwd_moe", wl.w2, wl.y2, wl.ws2), ("fp8_qdq_fwd_act", wl.x3, wl.y3, wl.ws3)):
+        B = x.shape[0] if x.dim() == 3 else 1
+        ts = torch.empty(B, dtype=torch.float32, device=x.device)
+        for _ in range(2):
+            q.fp8_quantize(x, codes=None, y=y, tscale_out=ts, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            q.fp8_quantize(x, codes=None, y=y, tscale_out=ts, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        nbytes = 4 * x.numel()
+        res[name] = {"shape": list(x.shape), "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,7 +325,7 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
-    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev)}
+    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

@@ -172,6 +172,25 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
                                  uint8_t* scales_out, float* tscale_out,
                                  void* workspace, size_t ws_bytes, qad_stream_t stream);
 
+/* FP8 (OCP E4M3FN) per-tensor simulated quantization ([Qwen] "3. QAD": the
+ * attention projections are kept in FP8 W8A8 and the KV cache in FP8; [Nano]:
+ * FP8 KV cache).  The pages give no scaling rule; the one taken here is one
+ * FP32 scale per tensor: s = amax/448 (1 for an all-zero tensor), or the
+ * given frozen / static scale; code = sign(x) << 7 | E4M3(|x|/s) with the
+ * quotient correctly rounded, nearest even, saturating at 448;
+ * y = bf16(dec(code) * s).  The straight-through backward is nvfp4_qdq_bwd.
+ *   x          : device, dtype xt, B tensors of R x C, C % 8 == 0
+ *   tscale_in  : device float[B] frozen scales (> 0, finite), or NULL for
+ *                dynamic scales (computed from each tensor's amax)
+ *   codes      : device u8[B][R][C] (8-byte aligned), or NULL
+ *   tscale_out : device float[B] scales used, or NULL
+ *   y          : device bf16[B][R][C], or NULL (at least one output)
+ *   workspace  : qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C) bytes for
+ *                dynamic scales; unused (may be NULL) with tscale_in */
+qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                          const float* tscale_in, uint8_t* codes, float* tscale_out, void* y,
+                          void* workspace, size_t ws_bytes, qad_stream_t stream);
+
 /* Fused KL(teacher || student) forward + backward over the full vocabulary
  * ([Nano] "Von QAT zu QAD"; [Qwen] "3. QAD").
  *   teacher, student : device, dtype lt, [tokens][vocab] row-major, 16-byte

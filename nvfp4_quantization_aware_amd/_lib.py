@@ -33,6 +33,7 @@ SIGNATURES = {
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "fp8_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_topk_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz,
                                    _vp]),
     "qad_check_finite": (_int, [_vp, _i64, _vp]),
@@ -207,6 +208,26 @@ def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: fl
                                 grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
                                 0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_fwd_bwd")
     return loss_out, rows, grad
+
+
+def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=True, y=True,
+                 tscale_out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """FP8 (E4M3) per-tensor QDQ of x ([R, C] or [B, R, C]).  Dynamic scales
+    (amax/448) unless tscale_in (float[B]) is given.  Returns (codes u8 like x
+    or None, tscale f32[B], y bf16 like x or None)."""
+    B, R, Cc = _brc(x)
+    dev = x.device
+    cd = torch.empty(x.shape, dtype=torch.uint8, device=dev) if codes is True else (
+        codes if isinstance(codes, torch.Tensor) else None)
+    yy = torch.empty(x.shape, dtype=torch.bfloat16, device=dev) if y is True else (
+        y if isinstance(y, torch.Tensor) else None)
+    if tscale_out is None:
+        tscale_out = torch.empty(B, dtype=torch.float32, device=dev)
+    if ws is None and tscale_in is None:
+        ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, dev)
+    _check(lib().fp8_quantize(_p(x), _dt(x), B, R, Cc, _p(tscale_in), _p(cd), _p(tscale_out), _p(yy), _p(ws),
+                              0 if ws is None else ws.numel(), _stream(dev)), "fp8_quantize")
+    return cd, tscale_out, yy
 
 
 def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, temperature: float = 1.0,

@@ -11,7 +11,10 @@ using qad::QuantizeArgs;
 
 namespace {
 
-constexpr int64_t kMaxElems = (int64_t)1 << 46; // keeps every byte offset far from int64 overflow
+// 2^36 elements (128 GiB of bf16, 256 GiB of fp32: any tensor that fits in a
+// GPU's memory) keeps byte offsets far from int64 overflow and every grid
+// below 2^32 lanes
+constexpr int64_t kMaxElems = (int64_t)1 << 36;
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -48,26 +51,29 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
+// fp8: per-tensor E4M3 (no block scales; frozen iff tscale_in is given;
+// codes one byte per element, 8-byte aligned); otherwise NVFP4
 qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
                            const uint8_t* scales_in, const float* tscale_in, uint8_t* codes,
                            uint8_t* scales_out, float* tscale_out, void* y, void* workspace,
-                           size_t ws_bytes, qad_stream_t stream)
+                           size_t ws_bytes, qad_stream_t stream, bool fp8 = false)
 {
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
-    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (n < 0 || C % (fp8 ? 8 : 16) != 0) return QAD_ERR_SHAPE;
     if (!codes && !scales_out && !tscale_out && !y) return QAD_ERR_INVALID_ARG;
-    if ((scales_in == nullptr) != (tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
+    if (!fp8 && (scales_in == nullptr) != (tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
     if (n == 0) return QAD_OK;
     if (!x) return QAD_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || (y && !aligned(y, 16)) || (codes && !aligned(codes, 4)) ||
+    if (!aligned(x, 16) || (y && !aligned(y, 16)) || (codes && !aligned(codes, fp8 ? 8 : 4)) ||
         (tscale_in && !aligned(tscale_in, 4)) || (tscale_out && !aligned(tscale_out, 4)))
         return QAD_ERR_ALIGNMENT;
     const size_t xbytes = (size_t)n * esize(xt);
-    if ((y && ranges_overlap(x, xbytes, y, (size_t)n * 2)) || (codes && ranges_overlap(x, xbytes, codes, (size_t)n / 2)) ||
+    if ((y && ranges_overlap(x, xbytes, y, (size_t)n * 2)) ||
+        (codes && ranges_overlap(x, xbytes, codes, fp8 ? (size_t)n : (size_t)n / 2)) ||
         (scales_out && ranges_overlap(x, xbytes, scales_out, (size_t)n / 16)))
         return QAD_ERR_INVALID_ARG;
-    const bool frozen = scales_in != nullptr;
+    const bool frozen = fp8 ? tscale_in != nullptr : scales_in != nullptr;
     if (!frozen) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C)) return QAD_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
@@ -84,10 +90,11 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     a.scales_out = scales_out;
     a.tscale_out = tscale_out;
     a.y = static_cast<uint16_t*>(y);
+    a.fp8 = fp8;
     if (frozen) return hip_status(qad::launch_quantize(a, qad::QUANT_FROZEN, nullptr, s));
     // dynamic scales: one pass when every chunk of a tensor can be resident at
     // once, otherwise an amax pass first
-    if (qad::quantize_one_pass_ok(a.bf16, B, a.elems))
+    if (qad::quantize_one_pass_ok(a.bf16, fp8, B, a.elems))
         return hip_status(qad::launch_quantize(a, qad::QUANT_ONE_PASS, ws_words(workspace), s));
     hipError_t e = qad::launch_amax(x, a.bf16, B, a.elems, ws_words(workspace), s);
     if (e != hipSuccess) return QAD_ERR_HIP;
@@ -164,6 +171,14 @@ qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     if (!y) return QAD_ERR_INVALID_ARG;
     return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, nullptr, nullptr, nullptr, y, workspace, ws_bytes,
                          stream);
+}
+
+qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C, const float* tscale_in,
+                          uint8_t* codes, float* tscale_out, void* y, void* workspace, size_t ws_bytes,
+                          qad_stream_t stream)
+{
+    return quantize_impl(x, xt, B, R, C, nullptr, tscale_in, codes, nullptr, tscale_out, y, workspace, ws_bytes,
+                         stream, true);
 }
 
 qad_status_t nvfp4_qdq_bwd(const void* grad_y, void* grad_x, qad_dtype_t gt, int64_t n, qad_stream_t stream)

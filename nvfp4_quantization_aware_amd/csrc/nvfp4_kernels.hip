@@ -35,6 +35,8 @@ constexpr uint64_t kWaitTicks = 2000000;
 __device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
 __device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
 __device__ __forceinline__ void stnt32(void* p, int64_t i, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p) + i); }
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void stnt64(void* p, int64_t i, uint32_t lo, uint32_t hi) { __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u*>(p) + i); }
 
 // ---- agent-scope atomics used by the one-pass protocol ---------------------
 __device__ __forceinline__ uint32_t a_load(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -118,6 +120,13 @@ __device__ __forceinline__ float tensor_scale_of(uint32_t amax_bits)
 {
     const float amax = as_f(amax_bits);
     return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+// FP8 (E4M3) per-tensor scale: the amax onto the E4M3 maximum 448
+__device__ __forceinline__ float fp8_scale_of(uint32_t amax_bits)
+{
+    const float amax = as_f(amax_bits);
+    return amax > 0.0f ? amax / 448.0f : 1.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -238,9 +247,30 @@ __device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t 
     return sb;
 }
 
+// FP8 (E4M3) per-tensor QDQ of one unit of 8 elements ([Qwen] "3. QAD":
+// attention projections FP8 W8A8, KV cache FP8): code = sign | E4M3(|x|/s),
+// nearest even, saturating at 448; y = bf16(dec(code) * s).  Codes are the 8
+// bytes of the unit in element order.
+template <bool FAST>
+__device__ __forceinline__ void fp8_unit(const float (&e)[8], float s, float r, uint32_t (&code)[2], uint32_t (&yw)[4])
+{
+    uint32_t c[8];
+    float g[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t mag = e4m3_encode(quotient_pos<FAST>(__builtin_fabsf(e[i]), s, r));
+        c[i] = mag | ((as_u(e[i]) >> 24) & 0x80u);
+        g[i] = __builtin_copysignf(e4m3_decode(mag) * s, e[i]);
+    }
+    code[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    code[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) yw[i >> 1] = pack_bf16x2(g[i], g[i + 1]);
+}
+
 enum { MODE_FROZEN = 0, MODE_AMAX = 1, MODE_ONEPASS = 2 };
 
-template <bool BF16, int MODE, bool FAST>
+template <bool BF16, int MODE, bool FAST, bool FP8>
 __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16> (&raw)[Chunk<BF16>::U],
                                            const uint32_t (&unit_max)[Chunk<BF16>::U], int64_t ubase, int64_t u0,
                                            int64_t units, const ScaleTable& tab, float s_g)
@@ -253,6 +283,15 @@ __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16
         const bool valid = u < units;
         float e[8];
         unpack<BF16>(raw[k], e);
+        if constexpr (FP8) {
+            uint32_t code[2], yw[4];
+            fp8_unit<FAST>(e, s_g, rcp_g, code, yw);
+            if (valid) {
+                if (a.y) stnt(a.y, ubase + u, v4u{yw[0], yw[1], yw[2], yw[3]});
+                if (a.codes) stnt64(a.codes, ubase + u, code[0], code[1]);
+            }
+            continue;
+        }
         uint32_t frozen_code = 0;
         if constexpr (MODE == MODE_FROZEN) frozen_code = valid ? a.scales_in[(ubase + u) >> 1] : 0u;
         uint32_t code, yw[4];
@@ -292,7 +331,7 @@ __device__ uint32_t scan_amax(const void* x, int64_t ubase, int64_t units, uint3
 // resident or finished.  The wait is nevertheless bounded; on time-out the
 // workgroup computes the amax itself (exact, so the result is unchanged).
 // ---------------------------------------------------------------------------
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, bool FP8>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int64_t P, uint32_t* ws)
 {
     using CH = Chunk<BF16>;
@@ -321,7 +360,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
     if constexpr (MODE == MODE_FROZEN) {
         s_g = a.tscale_in[b];
     } else if constexpr (MODE == MODE_AMAX) {
-        s_g = tensor_scale_of(Record(ws, b, P).w[0]); // written by amax_kernel (same chunking)
+        const uint32_t am = Record(ws, b, P).w[0]; // written by amax_kernel (same chunking)
+        s_g = FP8 ? fp8_scale_of(am) : tensor_scale_of(am);
     } else {
         const Record rec(ws, b, P);
         uint32_t m = 0;
@@ -345,13 +385,13 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         __syncthreads();
         uint32_t am = sh_amax;
         if (!(am & 0x80000000u)) am = scan_amax<BF16>(a.x, ubase, units, red); // timed out
-        s_g = tensor_scale_of(am & 0x7FFFFFFFu);
+        s_g = FP8 ? fp8_scale_of(am & 0x7FFFFFFFu) : tensor_scale_of(am & 0x7FFFFFFFu);
     }
-    build_table(tab, s_g);
+    if (!FP8) build_table(tab, s_g);
     if (j == 0 && t == 0 && a.tscale_out) a.tscale_out[b] = s_g;
     __syncthreads();
-    if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true>(a, raw, unit_max, ubase, u0, units, tab, s_g);
-    else code_chunk<BF16, MODE, false>(a, raw, unit_max, ubase, u0, units, tab, s_g);
+    if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true, FP8>(a, raw, unit_max, ubase, u0, units, tab, s_g);
+    else code_chunk<BF16, MODE, false, FP8>(a, raw, unit_max, ubase, u0, units, tab, s_g);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,7 +600,7 @@ __global__ __launch_bounds__(kQThreads) void mse_kernel(MseArgs a, int64_t group
 }
 
 // resident workgroups of a kernel on the current device (cached per device)
-template <bool BF16>
+template <bool BF16, bool FP8>
 int64_t resident_groups()
 {
     static int64_t cache[64];
@@ -568,7 +608,7 @@ int64_t resident_groups()
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     int64_t v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
     if (v) return v;
-    auto kernel = quantize_kernel<BF16, MODE_ONEPASS>;
+    auto kernel = quantize_kernel<BF16, MODE_ONEPASS, FP8>;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kQThreads, 0) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -624,10 +664,11 @@ hipError_t launch_amax_out(const uint32_t* ws, int64_t B, int64_t elems, bool bf
     return hipGetLastError();
 }
 
-bool quantize_one_pass_ok(bool bf16, int64_t B, int64_t elems)
+bool quantize_one_pass_ok(bool bf16, bool fp8, int64_t B, int64_t elems)
 {
     const int64_t P = quantize_chunks(bf16, elems);
-    const int64_t resident = bf16 ? resident_groups<true>() : resident_groups<false>();
+    const int64_t resident = fp8 ? (bf16 ? resident_groups<true, true>() : resident_groups<false, true>())
+                                 : (bf16 ? resident_groups<true, false>() : resident_groups<false, false>());
     (void)B;
     return P >= 1 && resident > 0 && P <= resident / 2;
 }
@@ -642,14 +683,16 @@ hipError_t launch_quantize(const QuantizeArgs& a, int mode, uint32_t* ws, hipStr
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)(a.B * P)), block(kQThreads);
-#define QK(BF, M) hipLaunchKernelGGL((quantize_kernel<BF, M>), grid, block, 0, stream, a, P, ws)
+#define QK(BF, M, F8) hipLaunchKernelGGL((quantize_kernel<BF, M, F8>), grid, block, 0, stream, a, P, ws)
+#define QK2(M, F8) { if (a.bf16) QK(true, M, F8); else QK(false, M, F8); }
     if (mode == MODE_ONEPASS) {
-        if (a.bf16) QK(true, MODE_ONEPASS); else QK(false, MODE_ONEPASS);
+        if (a.fp8) QK2(MODE_ONEPASS, true) else QK2(MODE_ONEPASS, false)
     } else if (mode == MODE_AMAX) {
-        if (a.bf16) QK(true, MODE_AMAX); else QK(false, MODE_AMAX);
+        if (a.fp8) QK2(MODE_AMAX, true) else QK2(MODE_AMAX, false)
     } else {
-        if (a.bf16) QK(true, MODE_FROZEN); else QK(false, MODE_FROZEN);
+        if (a.fp8) QK2(MODE_FROZEN, true) else QK2(MODE_FROZEN, false)
     }
+#undef QK2
 #undef QK
     return hipGetLastError();
 }

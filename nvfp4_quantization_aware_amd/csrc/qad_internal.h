@@ -35,17 +35,18 @@ struct QuantizeArgs {
     const void* x;
     bool bf16;
     int64_t B;
-    int64_t elems;             // R * C per tensor, multiple of 16
+    int64_t elems;             // R * C per tensor, multiple of 16 (NVFP4) or 8 (FP8)
     const uint8_t* scales_in;  // frozen block scales or null (dynamic)
     const float* tscale_in;    // frozen tensor scales
     uint8_t* codes;
     uint8_t* scales_out;
     float* tscale_out;
     uint16_t* y;
+    bool fp8 = false;          // FP8 (E4M3) per-tensor QDQ: no block scales, codes one byte per element
 };
 enum { QUANT_FROZEN = 0, QUANT_AMAX_GIVEN = 1, QUANT_ONE_PASS = 2 };
 // whether every chunk of one tensor can be resident at once with room to spare
-bool quantize_one_pass_ok(bool bf16, int64_t B, int64_t elems);
+bool quantize_one_pass_ok(bool bf16, bool fp8, int64_t B, int64_t elems);
 // QUANT_AMAX_GIVEN expects launch_amax's records in ws; QUANT_ONE_PASS
 // zeroes and uses them itself; QUANT_FROZEN ignores ws.
 hipError_t launch_quantize(const QuantizeArgs& a, int mode, uint32_t* ws, hipStream_t stream);

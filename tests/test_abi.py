@@ -29,12 +29,12 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qad_\w+|nvfp4_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qad_\w+|nvfp4_\w+|fp8_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -113,6 +113,19 @@ def test_quantize_rejects(L):
     assert f(P, 1, 1, 4, 32, None, None, None, None, None, P + 16, P * 3, ws, None) == INVALID
     # empty tensor: nothing to do
     assert f(P, 1, 0, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == OK
+
+
+def test_fp8_quantize_rejects(L):
+    f = L.fp8_quantize
+    ws = 1 << 16
+    assert f(P, 1, 1, 4, 12, None, None, None, P * 2, P * 3, ws, None) == SHAPE    # C % 8
+    assert f(P, 7, 1, 4, 16, None, None, None, P * 2, P * 3, ws, None) == DTYPE
+    assert f(P, 1, 1, 4, 16, None, None, None, None, P * 3, ws, None) == INVALID   # no output
+    assert f(None, 1, 1, 4, 16, None, None, None, P * 2, P * 3, ws, None) == INVALID
+    assert f(P, 1, 1, 4, 16, None, P * 4 + 4, None, None, P * 3, ws, None) == ALIGN  # codes 8-byte aligned
+    assert f(P, 1, 1, 4, 16, None, None, None, P * 2, None, 0, None) == WS           # dynamic needs workspace
+    assert f(P, 1, 1, 4, 16, None, None, None, P + 16, P * 3, ws, None) == INVALID   # y overlaps x
+    assert f(P, 1, 0, 4, 16, None, None, None, P * 2, None, 0, None) == OK           # empty
 
 
 def test_qdq_fwd_bwd_reject(L):
