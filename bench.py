@@ -248,6 +248,42 @@ def time_fp8(wl, iters=10):
     return res
 
 
+def time_linear(wl, dev, iters=10):
+    """W4A4 fake-quant linear of one MoE expert's projection: 8192 tokens of the
+    activation workload (x [8192, 4096]) times expert 0 of the MoE weights
+    (w [2048, 4096]); forward (both QDQ passes + the bf16 MFMA product) and
+    straight-through backward (two products), timed on their own."""
+    import torch
+    q = wl.q
+    x = wl.x3[0, :8192]
+    w = wl.w2[0]
+    M, K = x.shape
+    N = w.shape[0]
+    ws = q.workspace(q.QAD_OP_W4A4_LINEAR, M, N, K, dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    gy = torch.empty((M, N), dtype=torch.bfloat16, device=dev).normal_(0, 1e-3)
+    gx, gw = torch.empty_like(xq), torch.empty_like(wq)
+    res = {"shape_MNK": [M, N, K], "peak_TFLOPs_bf16": 2500.0}
+    for name, f, flops in (("fwd", lambda: q.qad_w4a4_linear_fwd(x, w, y=y, xq=xq, wq=wq, ws=ws), 2 * M * N * K),
+                           ("bwd", lambda: q.qad_w4a4_linear_bwd(gy, xq, wq, grad_x=gx, grad_w=gw, ws=ws),
+                            4 * M * N * K)):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        res[name] = {"ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -325,7 +361,7 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
-    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl)}
+    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

@@ -92,7 +92,8 @@ typedef enum {
     QAD_OP_QUANTIZE = 1,      /* nvfp4_quantize and nvfp4_qdq_fwd             */
     QAD_OP_MSE_CALIBRATE = 2, /* nvfp4_mse_calibrate                          */
     QAD_OP_KL = 3,            /* qad_kl_fwd_bwd: B = 1, R = tokens, C = vocab */
-    QAD_OP_KL_TOPK = 4        /* qad_kl_topk_fwd_bwd: B = 1, R = tokens, C = vocab */
+    QAD_OP_KL_TOPK = 4,       /* qad_kl_topk_fwd_bwd: B = 1, R = tokens, C = vocab */
+    QAD_OP_W4A4_LINEAR = 5    /* qad_w4a4_linear_fwd / _bwd: B = M, R = N, C = K */
 } qad_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -190,6 +191,33 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
 qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
                           const float* tscale_in, uint8_t* codes, float* tscale_out, void* y,
                           void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* W4A4 NVFP4 fake-quant linear layer ([Qwen] "3. QAD": the student is the
+ * W4A4 NVFP4 model, weights and activations both NVFP4; [Lightning]
+ * "QAD的工作原理": simulated quantization in every student forward).
+ *   forward : y[M][N] = QDQ(x)[M][K] * QDQ(w)[N][K]^T, where QDQ is
+ *             nvfp4_qdq_fwd with dynamic scales (one tensor scale for x, one
+ *             for w; blocks of 16 along K); bf16 product of the bf16 QDQ
+ *             values with fp32 accumulation (MFMA, hipBLASLt)
+ *   x, w    : device, dtype dt, row-major, 16-byte aligned; K > 0, K % 16 == 0
+ *   y       : device bf16 [M][N]; xq, wq: device bf16 [M][K], [N][K]
+ *             receive QDQ(x), QDQ(w) (kept for the backward); no output may
+ *             overlap another or an input
+ *   workspace : qad_workspace_bytes(QAD_OP_W4A4_LINEAR, M, N, K) bytes
+ * The library keeps one hipBLASLt handle per device, created on first use;
+ * hipBLASLt's scratch comes from the workspace. */
+qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, int64_t M, int64_t N, int64_t K,
+                                 void* y, void* xq, void* wq, void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Backward of qad_w4a4_linear_fwd with the straight-through estimator through
+ * both quantizers: grad_x[M][K] = grad_y[M][N] * wq[N][K] and
+ * grad_w[N][K] = grad_y^T * xq[M][K] (bf16, fp32 accumulation).
+ *   grad_y : device bf16 [M][N]; xq, wq: the forward's QDQ outputs
+ *   grad_x, grad_w : device bf16 outputs, either may be NULL (not both)
+ *   workspace : as for the forward
+ * M == 0 or N == 0 writes zeros to the other gradient. */
+qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void* wq, int64_t M, int64_t N, int64_t K,
+                                 void* grad_x, void* grad_w, void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* Fused KL(teacher || student) forward + backward over the full vocabulary
  * ([Nano] "Von QAT zu QAD"; [Qwen] "3. QAD").

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libqad.so")
 
 QAD_F32, QAD_BF16 = 0, 1
-QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL, QAD_OP_KL_TOPK = 0, 1, 2, 3, 4
+QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL, QAD_OP_KL_TOPK, QAD_OP_W4A4_LINEAR = 0, 1, 2, 3, 4, 5
 STATUS = {0: "QAD_OK", 1: "QAD_ERR_INVALID_ARG", 2: "QAD_ERR_SHAPE", 3: "QAD_ERR_DTYPE",
           4: "QAD_ERR_ALIGNMENT", 5: "QAD_ERR_WORKSPACE", 6: "QAD_ERR_NONFINITE", 7: "QAD_ERR_HIP"}
 
@@ -33,6 +33,8 @@ SIGNATURES = {
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qad_w4a4_linear_fwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qad_w4a4_linear_bwd": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fp8_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_topk_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz,
                                    _vp]),
@@ -228,6 +230,39 @@ def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=T
     _check(lib().fp8_quantize(_p(x), _dt(x), B, R, Cc, _p(tscale_in), _p(cd), _p(tscale_out), _p(yy), _p(ws),
                               0 if ws is None else ws.numel(), _stream(dev)), "fp8_quantize")
     return cd, tscale_out, yy
+
+
+def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=None, ws: torch.Tensor | None = None):
+    """y = QDQ(x) QDQ(w)^T (bf16) for x [M, K], w [N, K].  Returns (y, xq, wq)."""
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1] or x.dtype != w.dtype:
+        raise ValueError("x [M, K] and w [N, K] of one dtype")
+    (M, K), N = x.shape, w.shape[0]
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if xq is None else xq
+    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if wq is None else wq
+    if ws is None:
+        ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
+    _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(y), _p(xq), _p(wq), _p(ws), ws.numel(),
+                                     _stream(dev)), "qad_w4a4_linear_fwd")
+    return y, xq, wq
+
+
+def qad_w4a4_linear_bwd(grad_y: torch.Tensor, xq: torch.Tensor, wq: torch.Tensor, grad_x=True, grad_w=True,
+                        ws: torch.Tensor | None = None):
+    """Straight-through backward: returns (grad_x [M, K] or None, grad_w [N, K] or None)."""
+    M, N = grad_y.shape
+    K = xq.shape[1]
+    dev = grad_y.device
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if grad_x is True else (
+        grad_x if isinstance(grad_x, torch.Tensor) else None)
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if grad_w is True else (
+        grad_w if isinstance(grad_w, torch.Tensor) else None)
+    if ws is None:
+        ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
+    _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), _p(ws), ws.numel(),
+                                     _stream(dev)), "qad_w4a4_linear_bwd")
+    return gx, gw
 
 
 def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, temperature: float = 1.0,

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libqad.so")
-SOURCES = ["libqad.hip", "nvfp4_kernels.hip", "kl_kernels.hip"]
+SOURCES = ["libqad.hip", "nvfp4_kernels.hip", "kl_kernels.hip", "linear.hip"]
+LIBS = ["-lhipblaslt"]
 ARCH = "gfx950"
 
 
@@ -36,7 +37,7 @@ def compile_flags():
 def build(verbose: bool = False) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + compile_flags() + ["-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc()] + compile_flags() + ["-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + LIBS
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

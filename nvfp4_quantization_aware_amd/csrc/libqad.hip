@@ -131,6 +131,7 @@ size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
     case QAD_OP_MSE_CALIBRATE: return record_bytes(B, R * C);
     case QAD_OP_KL: return round256(qad::kl_workspace_bytes(R, C));
     case QAD_OP_KL_TOPK: return round256(qad::kl_topk_workspace_bytes(R, C));
+    case QAD_OP_W4A4_LINEAR: return round256(qad::linear_workspace_bytes(B, R, C));
     }
     return 0;
 }

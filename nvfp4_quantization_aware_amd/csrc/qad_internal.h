@@ -84,4 +84,7 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);
 size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab);
 hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream_t stream);
 
+// W4A4 linear: the QDQ records of the larger operand, then the GEMM scratch
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 } // namespace qad

@@ -231,6 +231,25 @@ def fp8_quantize(x: np.ndarray, tscale: float | None = None):
     return codes, float(ts[0]), y
 
 
+def w4a4_linear_fwd(x: np.ndarray, w: np.ndarray):
+    """W4A4 fake-quant linear: y = QDQ(x) QDQ(w)^T in binary64 (numpy matmul of
+    the oracle's NVFP4 QDQ outputs).  Returns (y f64 [M][N], xq bf16 bits,
+    wq bf16 bits)."""
+    _, _, _, xq = nvfp4_quantize(x)
+    _, _, _, wq = nvfp4_quantize(w)
+    xf = (xq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wf = (wq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return xf @ wf.T, xq, wq
+
+
+def w4a4_linear_bwd(grad_y: np.ndarray, xq: np.ndarray, wq: np.ndarray):
+    """Straight-through backward in binary64: grad_x = grad_y wq, grad_w =
+    grad_y^T xq (bf16 bit inputs)."""
+    f = lambda b: (np.asarray(b).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g = f(grad_y)
+    return g @ f(wq), g.T @ f(xq)
+
+
 # ---- KL ---------------------------------------------------------------------
 def kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0,
                grad_scale: float | None = None, want_grad: bool = True):
@@ -281,5 +300,5 @@ __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
-    "kl_topk_fwd_bwd", "fp8_quantize",
+    "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd",
 ]

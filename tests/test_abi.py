@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -82,7 +82,7 @@ def test_workspace_sizes(L):
         kl = L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab)
         assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPK, 1, tokens, vocab) == kl + -(-(tokens * 4) // 256) * 256
     assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
-    for op in range(5):
+    for op in range(6):
         assert L.qad_workspace_bytes(op, 1, 1, 16) % 256 == 0
 
 
@@ -126,6 +126,31 @@ def test_fp8_quantize_rejects(L):
     assert f(P, 1, 1, 4, 16, None, None, None, P * 2, None, 0, None) == WS           # dynamic needs workspace
     assert f(P, 1, 1, 4, 16, None, None, None, P + 16, P * 3, ws, None) == INVALID   # y overlaps x
     assert f(P, 1, 0, 4, 16, None, None, None, P * 2, None, 0, None) == OK           # empty
+
+
+def test_w4a4_linear_rejects(L):
+    fw, bw = L.qad_w4a4_linear_fwd, L.qad_w4a4_linear_bwd
+    ws = L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, 64, 32, 128)
+    assert ws >= 64 << 20 and ws % 256 == 0
+    a = lambda **kw: [kw.get("x", P), kw.get("w", P * 2), kw.get("dt", 1), kw.get("M", 64), kw.get("N", 32),
+                      kw.get("K", 128), kw.get("y", P * 3), kw.get("xq", P * 4), kw.get("wq", P * 5),
+                      kw.get("ws", P * 6), kw.get("wsb", ws), None]
+    assert fw(*a(dt=5)) == DTYPE
+    assert fw(*a(K=24)) == SHAPE and fw(*a(K=0)) == SHAPE and fw(*a(M=-1)) == SHAPE
+    assert fw(*a(y=None)) == INVALID and fw(*a(x=None)) == INVALID
+    assert fw(*a(xq=P * 4 + 8)) == ALIGN
+    assert fw(*a(wsb=ws - 256)) == WS and fw(*a(ws=None)) == WS
+    assert fw(*a(ws=P * 6 + 128)) == ALIGN
+    assert fw(*a(y=P * 4)) == INVALID                 # y overlaps xq
+    assert fw(*a(M=0)) == OK                          # nothing to do
+    b = lambda **kw: [kw.get("gy", P), kw.get("xq", P * 2), kw.get("wq", P * 3), kw.get("M", 64), kw.get("N", 32),
+                      kw.get("K", 128), kw.get("gx", P * 4), kw.get("gw", P * 5), kw.get("ws", P * 6),
+                      kw.get("wsb", ws), None]
+    assert bw(*b(gx=None, gw=None)) == INVALID
+    assert bw(*b(K=8)) == SHAPE
+    assert bw(*b(wq=None)) == INVALID                 # grad_x needs wq
+    assert bw(*b(gx=P)) == INVALID                    # grad_x overlaps grad_y
+    assert bw(*b(wsb=16)) == WS
 
 
 def test_qdq_fwd_bwd_reject(L):
