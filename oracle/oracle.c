@@ -240,6 +240,38 @@ void orc_nvfp4_quantize_blocks(const void* x, int dtype, int64_t nblocks, float 
 }
 
 /* ------------------------------------------------------------------------
+ * Clipped straight-through backward.  [Lightning] section "量化尺度处理策略":
+ * with frozen scales only the weights train, the scales stay fixed.  The
+ * pages print no clipping rule; the reading taken is the usual one for a
+ * saturating quantizer: the gradient passes where the element lies inside the
+ * range its block can represent, |x| <= 6 * s_eff, and is +0 where the
+ * quantizer saturates.  s_eff = fl(dec(s_b) * s_g) is the forward's binary32
+ * effective scale; the comparison is exact (6 * s_eff needs at most 26
+ * significant bits, so the binary64 product is exact).  The scales are the
+ * ones the forward used (frozen, or the dynamic ones it reported).
+ * ---------------------------------------------------------------------- */
+void orc_nvfp4_qdq_bwd_clipped(const void* grad_y, int gdtype, const void* x, int xdtype,
+                               int64_t nblocks, const uint8_t* scales, float s_g,
+                               void* grad_x, int64_t* n_clipped)
+{
+    int64_t clipped = 0;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const float s_eff = orc_e4m3_decode(scales[b]) * s_g;
+        const double lim = 6.0 * (double)s_eff;
+        for (int j = 0; j < 16; ++j) {
+            const int64_t i = b * 16 + j;
+            const int pass = fabs((double)load_x(x, xdtype, i)) <= lim;
+            clipped += !pass;
+            if (gdtype == 1)
+                ((uint16_t*)grad_x)[i] = pass ? ((const uint16_t*)grad_y)[i] : 0;
+            else
+                ((float*)grad_x)[i] = pass ? ((const float*)grad_y)[i] : 0.0f;
+        }
+    }
+    if (n_clipped) *n_clipped = clipped;
+}
+
+/* ------------------------------------------------------------------------
  * FP8 (E4M3) per-tensor simulated quantization.  [Qwen] section "3. QAD"
  * (the table of quantized components: attention projections FP8 W8A8, KV
  * cache FP8) and [Nano] "NVFP4-Format und warum es wichtig ist?" (FP8 KV

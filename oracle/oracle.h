@@ -97,6 +97,15 @@ void orc_mse_calibrate_blocks(const float* blocks, int64_t nblocks, float s_g,
                               uint8_t* scales, float* err_out,
                               uint8_t* cand_codes, float* cand_err);
 
+/* ---- clipped straight-through backward --------------------------------
+ * One tensor of nblocks 16-element blocks with the forward's block scales
+ * and tensor scale s_g: grad_x = grad_y where |x| <= 6 * dec(s_b) * s_g
+ * (exact), +0 elsewhere.  grad in gdtype, x in xdtype (0 fp32, 1 bf16).
+ * Optional n_clipped: number of zeroed elements.                          */
+void orc_nvfp4_qdq_bwd_clipped(const void* grad_y, int gdtype, const void* x, int xdtype,
+                               int64_t nblocks, const uint8_t* scales, float s_g,
+                               void* grad_x, int64_t* n_clipped);
+
 /* ---- FP8 (E4M3) per-tensor QDQ ---------------------------------------------
  * x: n elements of dtype.  tscale_in NULL: dynamic s = amax/448 (1 for an
  * all-zero tensor); else s = *tscale_in (> 0).  Optional codes[n] (E4M3 with

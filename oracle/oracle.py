@@ -62,6 +62,7 @@ def _load():
             "orc_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
             "orc_mse_calibrate_blocks": (None, [vp, i64, f32, i32, f32, f32, vp, vp, vp, vp]),
             "orc_fp8_quantize": (None, [vp, i32, i64, vp, vp, vp, vp]),
+            "orc_nvfp4_qdq_bwd_clipped": (None, [vp, i32, vp, i32, i64, vp, f32, vp, vp]),
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
             "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
         }
@@ -231,6 +232,24 @@ def fp8_quantize(x: np.ndarray, tscale: float | None = None):
     return codes, float(ts[0]), y
 
 
+def nvfp4_qdq_bwd_clipped(grad_y: np.ndarray, x: np.ndarray, scales: np.ndarray, tscale: float):
+    """Clipped straight-through backward of one tensor (x.size % 16 == 0):
+    grad_y where |x| <= 6 * dec(scale) * tscale, +0 elsewhere.  grad_y and x
+    are float32 or raw-bf16 uint16 arrays of the same size; scales holds one
+    E4M3 code per 16 consecutive elements.  Returns (grad_x like grad_y,
+    number of clipped elements)."""
+    g = np.ascontiguousarray(grad_y)
+    x = np.ascontiguousarray(x)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    if g.size != x.size or x.size % 16 or sc.size != x.size // 16:
+        raise ValueError("grad_y, x and scales sizes do not match")
+    out = np.empty_like(g)
+    nc = np.zeros(1, np.int64)
+    _load().orc_nvfp4_qdq_bwd_clipped(_ptr(g), _dtype_code(g), _ptr(x), _dtype_code(x), x.size // 16,
+                                      _ptr(sc), float(tscale), _ptr(out), _ptr(nc))
+    return out, int(nc[0])
+
+
 def w4a4_linear_fwd(x: np.ndarray, w: np.ndarray):
     """W4A4 fake-quant linear: y = QDQ(x) QDQ(w)^T in binary64 (numpy matmul of
     the oracle's NVFP4 QDQ outputs).  Returns (y f64 [M][N], xq bf16 bits,
@@ -300,5 +319,5 @@ __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
-    "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd",
+    "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd", "nvfp4_qdq_bwd_clipped",
 ]
