@@ -248,6 +248,30 @@ def time_fp8(wl, iters=10):
     return res
 
 
+def time_clipped_ste(wl, iters=10):
+    """Clipped straight-through backward on the MoE weight batch with the
+    forward's dynamic scales (taken once before timing): reads grad_y and x
+    (2 B each per element) and the block scales (1/16 B), writes grad_x
+    (2 B), timed on its own after the step."""
+    import torch
+    q = wl.q
+    w, g, gx = wl.w2, wl.g2, wl.gx2
+    _, scales, ts, _ = q.nvfp4_quantize(w, codes=False, y=False, ws=wl.ws2)
+    for _ in range(2):
+        q.nvfp4_qdq_bwd_clipped(g, w, scales, ts, grad_x=gx)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.nvfp4_qdq_bwd_clipped(g, w, scales, ts, grad_x=gx)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 6 * w.numel() + w.numel() // 16
+    return {"shape": list(w.shape), "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+
 def time_linear(wl, dev, iters=10):
     """W4A4 fake-quant linear of one MoE expert's projection: 8192 tokens of the
     activation workload (x [8192, 4096]) times expert 0 of the MoE weights
@@ -361,7 +385,8 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
-    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev)}
+    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
+                         "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

@@ -151,6 +151,24 @@ qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
 qad_status_t nvfp4_qdq_bwd(const void* grad_y, void* grad_x, qad_dtype_t gt, int64_t n,
                            qad_stream_t stream);
 
+/* Clipped straight-through backward ([Lightning] "量化尺度处理策略": with
+ * frozen scales only the weights train; the pages print no clipping rule).
+ * grad_x = grad_y bit for bit where |x| <= 6 * s_eff, the range the element's
+ * block can represent, and +0 where the forward saturated; s_eff =
+ * fl(dec(s_b) * s_g) is the forward's binary32 effective scale and the
+ * comparison is exact.  The scales are the ones the forward used: the frozen
+ * ones, or scales_out / tscale_out of a dynamic nvfp4_quantize.
+ *   grad_y     : device, dtype gt, [B][R][C], 16-byte aligned
+ *   x          : device, dtype xt, [B][R][C], 16-byte aligned (the forward input)
+ *   scales     : device u8 [B][R][C/16] E4M3 block scale codes (0..126)
+ *   tscale     : device float[B] tensor scales (positive, finite), 4-byte aligned
+ *   grad_x     : device, dtype gt, [B][R][C], 16-byte aligned; grad_x == grad_y
+ *                is allowed (in place); any other overlap with an input is not
+ * C % 16 == 0.  Other scale codes or tensor scales give unspecified results. */
+qad_status_t nvfp4_qdq_bwd_clipped(const void* grad_y, qad_dtype_t gt, const void* x, qad_dtype_t xt,
+                                   int64_t B, int64_t R, int64_t C, const uint8_t* scales,
+                                   const float* tscale, void* grad_x, qad_stream_t stream);
+
 /* MSE calibration of the frozen block scales ([Lightning] "量化尺度处理策略":
  * the MSE scale search runs once, before training, because it is too costly
  * per step).  For each block the candidates are amax_b * k_i / 6 with k_i the

@@ -31,6 +31,7 @@ SIGNATURES = {
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_fwd": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
+    "nvfp4_qdq_bwd_clipped": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
     "qad_w4a4_linear_fwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -166,6 +167,28 @@ def nvfp4_qdq_bwd(grad_y: torch.Tensor, grad_x: torch.Tensor | None = None) -> t
         grad_x = torch.empty_like(grad_y)
     _check(lib().nvfp4_qdq_bwd(_p(grad_y), _p(grad_x), _dt(grad_y), grad_y.numel(),
                                _stream(grad_y.device)), "nvfp4_qdq_bwd")
+    return grad_x
+
+
+def nvfp4_qdq_bwd_clipped(grad_y: torch.Tensor, x: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+                          grad_x: torch.Tensor | None = None) -> torch.Tensor:
+    """Clipped straight-through backward with the forward's scales: grad_y
+    where |x| <= 6 * s_eff, +0 elsewhere.  grad_y and x share the shape
+    [R, C] or [B, R, C]; scales [.., C/16] u8, tscale [B] float32."""
+    B, R, Cc = _brc(x)
+    if tuple(grad_y.shape) != tuple(x.shape):
+        raise ValueError("grad_y and x shapes differ")
+    for t in (grad_y, scales, tscale):
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+    if scales.dtype != torch.uint8 or scales.numel() != B * R * (Cc // 16):
+        raise ValueError("scales must be uint8 with one code per 16 elements")
+    if tscale.dtype != torch.float32 or tscale.numel() != B:
+        raise ValueError("tscale must be float32 with one scale per tensor")
+    if grad_x is None:
+        grad_x = torch.empty_like(grad_y)
+    _check(lib().nvfp4_qdq_bwd_clipped(_p(grad_y), _dt(grad_y), _p(x), _dt(x), B, R, Cc, _p(scales), _p(tscale),
+                                       _p(grad_x), _stream(x.device)), "nvfp4_qdq_bwd_clipped")
     return grad_x
 
 

@@ -194,6 +194,37 @@ qad_status_t nvfp4_qdq_bwd(const void* grad_y, void* grad_x, qad_dtype_t gt, int
     return hip_status(qad::launch_copy(grad_y, grad_x, (int64_t)bytes, hs(stream)));
 }
 
+qad_status_t nvfp4_qdq_bwd_clipped(const void* grad_y, qad_dtype_t gt, const void* x, qad_dtype_t xt,
+                                   int64_t B, int64_t R, int64_t C, const uint8_t* scales,
+                                   const float* tscale, void* grad_x, qad_stream_t stream)
+{
+    if (!valid_dtype(gt) || !valid_dtype(xt)) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(B, R, C);
+    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (n == 0) return QAD_OK;
+    if (B > (int64_t)INT32_MAX / qad::clip_chunks(R * C)) return QAD_ERR_SHAPE;
+    if (!grad_y || !x || !scales || !tscale || !grad_x) return QAD_ERR_INVALID_ARG;
+    if (!aligned(grad_y, 16) || !aligned(x, 16) || !aligned(grad_x, 16) || !aligned(tscale, 4))
+        return QAD_ERR_ALIGNMENT;
+    const size_t gbytes = (size_t)n * esize(gt);
+    if ((grad_x != grad_y && ranges_overlap(grad_y, gbytes, grad_x, gbytes)) ||
+        ranges_overlap(x, (size_t)n * esize(xt), grad_x, gbytes) ||
+        ranges_overlap(scales, (size_t)n / 16, grad_x, gbytes) ||
+        ranges_overlap(tscale, (size_t)B * 4, grad_x, gbytes))
+        return QAD_ERR_INVALID_ARG;
+    qad::ClipArgs a;
+    a.grad_y = grad_y;
+    a.gbf16 = gt == QAD_BF16;
+    a.x = x;
+    a.xbf16 = xt == QAD_BF16;
+    a.B = B;
+    a.elems = R * C;
+    a.scales = scales;
+    a.tscale = tscale;
+    a.grad_x = grad_x;
+    return hip_status(qad::launch_qdq_bwd_clipped(a, hs(stream)));
+}
+
 qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64_t R, int64_t C,
                                  int32_t n_candidates, float k_min, float k_max, uint8_t* scales_out,
                                  float* tscale_out, void* workspace, size_t ws_bytes, qad_stream_t stream)

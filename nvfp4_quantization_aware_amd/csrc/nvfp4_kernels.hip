@@ -463,6 +463,66 @@ __global__ __launch_bounds__(kQThreads) void copy_kernel(const void* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Clipped straight-through backward ([Lightning] "量化尺度处理策略": with
+// frozen scales only the weights train).  grad_x = grad_y where the element
+// lies inside the range its block represents, |x| <= 6 * s_eff, and +0 where
+// the quantizer saturates; s_eff = dec(s_b) * s_g as in the forward.  The
+// test is exact: fma(-6, s_eff, |x|) rounds |x| - 6 * s_eff once, and both
+// terms are multiples of 2^-149, so a nonzero difference never rounds to 0
+// and the sign is the exact one.  One lane per unit of 8 elements (half a
+// block), kClipUnits units per lane strided by the workgroup width, one
+// tensor per group of workgroups (uniform tensor scale).
+// ---------------------------------------------------------------------------
+constexpr int kClipUnits = 4;
+
+template <bool GBF16, bool XBF16>
+__global__ __launch_bounds__(kQThreads) void clip_ste_kernel(ClipArgs a, int64_t P)
+{
+    const int64_t b = blockIdx.x / P;
+    const int64_t u0 = (blockIdx.x - b * P) * ((int64_t)kQThreads * kClipUnits);
+    const int64_t upt = a.elems >> 3;
+    const float s_g = a.tscale[b];
+    const void* gy = (const char*)a.grad_y + b * a.elems * (GBF16 ? 2 : 4);
+    const void* x = (const char*)a.x + b * a.elems * (XBF16 ? 2 : 4);
+    void* gx = (char*)a.grad_x + b * a.elems * (GBF16 ? 2 : 4);
+    const uint8_t* sc = a.scales + b * (a.elems >> 4);
+    Raw<GBF16> g[kClipUnits];
+    Raw<XBF16> xr[kClipUnits];
+    uint32_t code[kClipUnits];
+#pragma unroll
+    for (int k = 0; k < kClipUnits; ++k) {
+        const int64_t u = u0 + k * kQThreads + threadIdx.x;
+        const bool valid = u < upt;
+        g[k] = load_raw<GBF16>(gy, u, valid);
+        xr[k] = load_raw<XBF16>(x, u, valid);
+        code[k] = valid ? sc[u >> 1] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kClipUnits; ++k) {
+        const int64_t u = u0 + k * kQThreads + threadIdx.x;
+        if (u >= upt) continue;
+        float e[8];
+        unpack<XBF16>(xr[k], e);
+        const float s = e4m3_decode(code[k] & 127u) * s_g;
+        bool keep[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) keep[i] = __builtin_fmaf(-6.0f, s, __builtin_fabsf(e[i])) <= 0.0f;
+        if constexpr (GBF16) {
+            uint32_t w[4] = {g[k].a.x, g[k].a.y, g[k].a.z, g[k].a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = (keep[2 * i] ? w[i] & 0xFFFFu : 0u) | (keep[2 * i + 1] ? w[i] & 0xFFFF0000u : 0u);
+            stnt(gx, u, v4u{w[0], w[1], w[2], w[3]});
+        } else {
+            stnt(gx, 2 * u, v4u{keep[0] ? g[k].a.x : 0u, keep[1] ? g[k].a.y : 0u, keep[2] ? g[k].a.z : 0u,
+                                keep[3] ? g[k].a.w : 0u});
+            stnt(gx, 2 * u + 1, v4u{keep[4] ? g[k].b.x : 0u, keep[5] ? g[k].b.y : 0u, keep[6] ? g[k].b.z : 0u,
+                                    keep[7] ? g[k].b.w : 0u});
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // MSE calibration of the frozen block scales ([Lightning] "量化尺度处理策略").
 // One lane per 16-element block.  The candidates amax_b * k_i / 6 rounded to
 // E4M3 are non-decreasing in i and, for grids no coarser than k_min/16 per
@@ -707,6 +767,27 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream, src, dst, vecs,
                        (const uint16_t*)((const char*)src + vecs * 16), (uint16_t*)((char*)dst + vecs * 16),
                        tail_halves);
+    return hipGetLastError();
+}
+
+int64_t clip_chunks(int64_t elems)
+{
+    const int64_t per = (int64_t)kQThreads * kClipUnits;
+    return ((elems >> 3) + per - 1) / per;
+}
+
+hipError_t launch_qdq_bwd_clipped(const ClipArgs& a, hipStream_t stream)
+{
+    if (a.B <= 0 || a.elems <= 0) return hipSuccess;
+    const int64_t P = clip_chunks(a.elems);
+    const dim3 grid((unsigned)(a.B * P)), block(kQThreads);
+#define CK(G, X) hipLaunchKernelGGL((clip_ste_kernel<G, X>), grid, block, 0, stream, a, P)
+    if (a.gbf16) {
+        if (a.xbf16) CK(true, true); else CK(true, false);
+    } else {
+        if (a.xbf16) CK(false, true); else CK(false, false);
+    }
+#undef CK
     return hipGetLastError();
 }
 

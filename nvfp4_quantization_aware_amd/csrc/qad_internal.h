@@ -53,6 +53,21 @@ hipError_t launch_quantize(const QuantizeArgs& a, int mode, uint32_t* ws, hipStr
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+struct ClipArgs {
+    const void* grad_y;
+    bool gbf16;
+    const void* x;             // the forward's input
+    bool xbf16;
+    int64_t B;
+    int64_t elems;             // R * C per tensor, multiple of 16
+    const uint8_t* scales;     // [B][elems/16] block scale codes the forward used
+    const float* tscale;       // [B] tensor scales the forward used
+    void* grad_x;              // dtype of grad_y
+};
+// workgroups per tensor of the clipped backward
+int64_t clip_chunks(int64_t elems);
+hipError_t launch_qdq_bwd_clipped(const ClipArgs& a, hipStream_t stream);
+
 struct MseArgs {
     const void* w;
     bool bf16;

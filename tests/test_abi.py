@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -163,6 +163,31 @@ def test_qdq_fwd_bwd_reject(L):
     # in place and empty are no-ops
     assert L.nvfp4_qdq_bwd(P, P, 1, 100, None) == OK
     assert L.nvfp4_qdq_bwd(P, P * 2, 1, 0, None) == OK
+
+
+def test_qdq_bwd_clipped_rejects(L):
+    f = L.nvfp4_qdq_bwd_clipped
+    Q = 1 << 24   # far-apart fake addresses: grad_y, x, scales, tscale, grad_x
+
+    def a(gy=P, gt=1, x=P + Q, xt=1, B=2, R=4, C=32, sc=P + 2 * Q, ts=P + 3 * Q, gx=P + 4 * Q):
+        return gy, gt, x, xt, B, R, C, sc, ts, gx, None
+
+    assert f(*a(gt=7)) == DTYPE
+    assert f(*a(xt=7)) == DTYPE
+    assert f(*a(C=24)) == SHAPE                      # C % 16
+    assert f(*a(B=-1)) == SHAPE
+    assert f(*a(B=1 << 31, R=1, C=16)) == SHAPE      # grid beyond 2^31 workgroups
+    assert f(*a(x=None)) == INVALID
+    assert f(*a(sc=None)) == INVALID
+    assert f(*a(ts=None)) == INVALID
+    assert f(*a(gx=None)) == INVALID
+    assert f(*a(x=P_ODD)) == ALIGN
+    assert f(*a(gx=P_ODD + 4 * Q)) == ALIGN
+    assert f(*a(ts=P + 3 * Q + 2)) == ALIGN
+    assert f(*a(gx=P + 64)) == INVALID               # partial overlap with grad_y
+    assert f(*a(gx=P + Q)) == INVALID                # grad_x over x
+    assert f(*a(gx=P + 2 * Q)) == INVALID            # grad_x over the scales
+    assert f(*a(R=0)) == OK                          # empty: nothing launched
 
 
 def test_amax_rejects(L):
