@@ -248,6 +248,31 @@ def time_fp8(wl, iters=10):
     return res
 
 
+def time_topp(wl, dev, top_p=0.9, iters=10):
+    """Teacher-top-p (nucleus) KL on the same 8192 x 131072 logits: thresholds
+    (three streaming reads of the teacher) then the masked one-pass KL, timed
+    on its own after the step."""
+    import torch
+    q = wl.q
+    N5, V5 = wl.shapes["kl"]
+    ws = q.workspace(q.QAD_OP_KL_TOPP, 1, N5, V5, dev)
+    print("[bench] top-p KL", file=sys.stderr, flush=True)
+    for _ in range(2):
+        q.qad_kl_topp_fwd_bwd(wl.t5, wl.s5, top_p, loss_out=wl.l5, grad=wl.gr5, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.qad_kl_topp_fwd_bwd(wl.t5, wl.s5, top_p, loss_out=wl.l5, grad=wl.gr5, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 6 * N5 * V5
+    return {"top_p": top_p, "ms": round(ms, 4), "tokens_per_s": round(N5 / (ms * 1e-3), 1),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes": nbytes, "iters": iters}
+
+
 def time_clipped_ste(wl, iters=10):
     """Clipped straight-through backward on the MoE weight batch with the
     forward's dynamic scales (taken once before timing): reads grad_y and x
@@ -385,7 +410,7 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
-    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
+    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), "kl_topp_fwd_bwd": time_topp(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
                          "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -93,7 +93,8 @@ typedef enum {
     QAD_OP_MSE_CALIBRATE = 2, /* nvfp4_mse_calibrate                          */
     QAD_OP_KL = 3,            /* qad_kl_fwd_bwd: B = 1, R = tokens, C = vocab */
     QAD_OP_KL_TOPK = 4,       /* qad_kl_topk_fwd_bwd: B = 1, R = tokens, C = vocab */
-    QAD_OP_W4A4_LINEAR = 5    /* qad_w4a4_linear_fwd / _bwd: B = M, R = N, C = K */
+    QAD_OP_W4A4_LINEAR = 5,   /* qad_w4a4_linear_fwd / _bwd: B = M, R = N, C = K */
+    QAD_OP_KL_TOPP = 6        /* qad_kl_topp_fwd_bwd: B = 1, R = tokens, C = vocab */
 } qad_op_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -274,6 +275,27 @@ qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_d
                                  int64_t tokens, int64_t vocab, int64_t k, float temperature,
                                  float grad_scale, float* loss_out, float* row_loss, void* grad_student,
                                  qad_dtype_t gt, void* workspace, size_t ws_bytes, qad_stream_t stream);
+
+/* Teacher-top-p (nucleus) KL forward + backward ([Qwen] "3. QAD" names top-p
+ * as the variant to try after the top-k run; no definition is printed).  Per
+ * token row, with p = softmax(teacher/T) over the whole row:
+ *   tau = the largest teacher value at which the teacher mass of the entries
+ *         at or above it reaches top_p (top_p >= 1: the smallest value);
+ *   S   = { v : teacher_v >= tau } (ties with tau kept; -0 equals +0);
+ *   then exactly as qad_kl_topk_fwd_bwd on S.
+ * The masses are the exponentials the KL kernels use, summed exactly in
+ * 64-bit fixed point (2^-40 of the row's largest weight), so the choice is
+ * deterministic; where the accumulated mass lies within about 1e-6 of top_p
+ * it may differ from an exact-arithmetic choice by one group of tied values.
+ *   top_p            : > 0 and finite
+ *   tau_out          : device float[tokens] thresholds, or NULL; must not
+ *                      overlap any other argument
+ *   workspace        : qad_workspace_bytes(QAD_OP_KL_TOPP, 1, tokens, vocab)
+ * Other arguments, layouts and errors as qad_kl_topk_fwd_bwd. */
+qad_status_t qad_kl_topp_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt, int64_t tokens,
+                                 int64_t vocab, float top_p, float temperature, float grad_scale, float* loss_out,
+                                 float* row_loss, void* grad_student, qad_dtype_t gt, float* tau_out,
+                                 void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* Synchronises `stream`, copies n floats from device memory `values` (an
  * amax_out or tscale_out array) and returns QAD_ERR_NONFINITE if any is a NaN

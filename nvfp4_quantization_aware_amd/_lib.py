@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libqad.so")
 
 QAD_F32, QAD_BF16 = 0, 1
-QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL, QAD_OP_KL_TOPK, QAD_OP_W4A4_LINEAR = 0, 1, 2, 3, 4, 5
+QAD_OP_AMAX, QAD_OP_QUANTIZE, QAD_OP_MSE_CALIBRATE, QAD_OP_KL, QAD_OP_KL_TOPK, QAD_OP_W4A4_LINEAR, QAD_OP_KL_TOPP = \
+    0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "QAD_OK", 1: "QAD_ERR_INVALID_ARG", 2: "QAD_ERR_SHAPE", 3: "QAD_ERR_DTYPE",
           4: "QAD_ERR_ALIGNMENT", 5: "QAD_ERR_WORKSPACE", 6: "QAD_ERR_NONFINITE", 7: "QAD_ERR_HIP"}
 
@@ -39,6 +40,8 @@ SIGNATURES = {
     "fp8_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_topk_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz,
                                    _vp]),
+    "qad_kl_topp_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _f32, _vp, _vp, _vp, _int, _vp, _vp,
+                                   _sz, _vp]),
     "qad_check_finite": (_int, [_vp, _i64, _vp]),
 }
 
@@ -314,6 +317,37 @@ def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, te
                                      grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
                                      0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topk_fwd_bwd")
     return loss_out, rows, grad
+
+
+def qad_kl_topp_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, top_p: float, temperature: float = 1.0,
+                        grad_scale: float | None = None, grad_dtype=torch.bfloat16, row_loss=False, tau=False,
+                        loss_out: torch.Tensor | None = None, grad: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None):
+    """KL over the teacher's nucleus of each row: the entries at or above the
+    largest teacher value at which the teacher mass reaches top_p (ties
+    kept), both softmaxes renormalised over them.  Returns (loss f32[1],
+    row_loss f32[tokens] or None, grad or None, tau f32[tokens] or None)."""
+    if teacher.shape != student.shape or teacher.dim() != 2:
+        raise ValueError("teacher and student must both be [tokens, vocab]")
+    tokens, vocab = teacher.shape
+    dev = teacher.device
+    if grad_scale is None:
+        grad_scale = 1.0 / tokens if tokens else 0.0
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
+        row_loss if isinstance(row_loss, torch.Tensor) else None)
+    taus = torch.empty(tokens, dtype=torch.float32, device=dev) if tau is True else (
+        tau if isinstance(tau, torch.Tensor) else None)
+    if grad is None and grad_dtype is not None:
+        grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
+    gt = _dt(grad) if grad is not None else QAD_BF16
+    if ws is None:
+        ws = workspace(QAD_OP_KL_TOPP, 1, tokens, vocab, dev)
+    _check(lib().qad_kl_topp_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, float(top_p),
+                                     temperature, grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(taus),
+                                     _p(ws), 0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topp_fwd_bwd")
+    return loss_out, rows, grad, taus
 
 
 def qad_check_finite(values: torch.Tensor) -> bool:

@@ -641,6 +641,13 @@ __device__ uint32_t kth_largest_key(uint32_t k, ForT for_t, TopShared& sh)
     return prefix;
 }
 
+// the key of a logit value (the value is a bf16 value when BF16)
+template <bool BF16>
+__device__ __forceinline__ uint32_t key_of_value(float v)
+{
+    return BF16 ? key16(as_u(v) >> 16) : key32(as_u(v));
+}
+
 template <bool BF16_IN, int GRAD>
 __global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t k, float c, float inv_t, float gmul)
 {
@@ -661,7 +668,8 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t
             f(un, u < units);
         }
     };
-    const uint32_t tau = kth_largest_key<BF16_IN>(k, for_t, sh);
+    // the threshold key: given (a.tau, as a logit value) or selected here
+    const uint32_t tau = a.tau ? key_of_value<BF16_IN>(a.tau[row]) : kth_largest_key<BF16_IN>(k, for_t, sh);
 
     // f(teacher and student unit, valid, unit index) over the lane's units
     auto for_ts = [&](auto f) {
@@ -775,6 +783,184 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_tau_kernel(const void* te
     if (tid == 0) tau_out[row] = value_of_key<BF16>(key);
 }
 
+// ---------------------------------------------------------------------------
+// Teacher-top-p (nucleus) threshold ([Qwen] "3. QAD" names top-p as the
+// variant to try after the top-k run).  tau_out[row] = the largest teacher
+// value at which the teacher mass of the entries at or above it reaches
+// top_p; top_p >= 1 keeps every entry (tau = the smallest value).  Masses are
+// p_v up to the row's common factor: w_v = 2^(c t_v - m), m = RN(c max t),
+// exactly the exponentials of the KL kernels, taken in fixed point
+// (floor(w 2^40) in 64-bit integers) so that every sum is exact and
+// independent of the order of the LDS atomics:
+//   0. the row's largest key (integer max), hence m;
+//   1. a radix round over the top 12 key bits: an LDS histogram sums the
+//      fixed-point masses per digit; its total is Z, the target is
+//      ceil(top_p Z), and a scan from the top finds the digit at which the
+//      accumulated mass reaches it;
+//   2. further rounds resolve the remaining key bits inside that digit.
+// Weights below 2^-40 of the largest count as 0 (at most vocab * 2^-40 of the
+// mass).  The teacher row is streamed once per step: three times for bf16,
+// four for fp32.
+// ---------------------------------------------------------------------------
+struct TopPShared {
+    unsigned long long hist[1 << kDigitBits];
+    unsigned long long wave_tot[kTopThreads / 64];
+    unsigned long long above, target;
+    uint32_t digit;
+    uint32_t wave_key[kTopThreads / 64];
+};
+
+__device__ __forceinline__ unsigned long long block_incl_scan64(unsigned long long v, unsigned long long* wave_tot)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long n = __shfl_up(v, o, 64);
+        if (lane >= o) v += n;
+    }
+    if (lane == 63) wave_tot[w] = v;
+    __syncthreads();
+    unsigned long long off = 0;
+    for (int i = 0; i < w; ++i) off += wave_tot[i];
+    __syncthreads();
+    return v + off;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void teacher_values(const Unit<BF16>& u, float (&tv)[8])
+{
+    if constexpr (BF16) {
+        unpack8(u.t[0], tv);
+    } else {
+        tv[0] = as_f(u.t[0].x); tv[1] = as_f(u.t[0].y); tv[2] = as_f(u.t[0].z); tv[3] = as_f(u.t[0].w);
+        tv[4] = as_f(u.t[1].x); tv[5] = as_f(u.t[1].y); tv[6] = as_f(u.t[1].z); tv[7] = as_f(u.t[1].w);
+    }
+}
+
+// largest (MAX) or smallest key of the row, in every lane
+template <bool BF16, bool MAX, class ForT>
+__device__ uint32_t extreme_key(ForT for_t, uint32_t* wave_key)
+{
+    uint32_t e = MAX ? 0u : 0xFFFFFFFFu;
+    for_t([&](const Unit<BF16>& u, bool valid) {
+        if (!valid) return;
+        uint32_t key[8];
+        teacher_keys<BF16>(u, key);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e = MAX ? umax(e, key[i]) : min(e, key[i]);
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t n = __shfl_xor(e, o, 64);
+        e = MAX ? umax(e, n) : min(e, n);
+    }
+    if ((threadIdx.x & 63) == 0) wave_key[threadIdx.x >> 6] = e;
+    __syncthreads();
+    e = wave_key[0];
+    for (int i = 1; i < kTopThreads / 64; ++i) e = MAX ? umax(e, wave_key[i]) : min(e, wave_key[i]);
+    __syncthreads();
+    return e;
+}
+
+// the key of the nucleus threshold (0 < top_p < 1); m = RN(c max t)
+template <bool BF16, class ForT>
+__device__ uint32_t nucleus_key(float top_p, float c, float m, ForT for_t, TopPShared& sh)
+{
+    constexpr int KB = BF16 ? 16 : 32;
+    uint32_t prefix = 0;
+    unsigned long long remaining = 0;
+    for (int used = 0; used < KB;) {
+        const int d = KB - used < kDigitBits ? KB - used : kDigitBits;
+        const int nb = 1 << d, shift = KB - used - d;
+        for (int i = threadIdx.x; i < nb; i += kTopThreads) sh.hist[i] = 0ull;
+        __syncthreads();
+        for_t([&](const Unit<BF16>& u, bool valid) {
+            if (!valid) return;
+            uint32_t key[8];
+            float tv[8];
+            teacher_keys<BF16>(u, key);
+            teacher_values<BF16>(u, tv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (used == 0 || (key[i] >> (KB - used)) == prefix) {
+                    const unsigned long long w =
+                        (unsigned long long)(exp2_hw(__builtin_fmaf(tv[i], c, -m)) * 0x1p40f);
+                    if (w) atomicAdd(&sh.hist[(key[i] >> shift) & (nb - 1)], w);
+                }
+            }
+        });
+        __syncthreads();
+        // lane l sums the g bins below nb - l g (from the top), then a scan
+        // gives every group the mass above it
+        const int g = nb >= kTopThreads ? nb / kTopThreads : 1;
+        const int groups = nb / g;
+        const int top = nb - 1 - (int)threadIdx.x * g;
+        unsigned long long local = 0;
+        if ((int)threadIdx.x < groups)
+            for (int b = 0; b < g; ++b) local += sh.hist[top - b];
+        const unsigned long long incl = block_incl_scan64(local, sh.wave_tot);
+        if (used == 0) {
+            // the last lane's inclusive sum is the row's total mass Z
+            if (threadIdx.x == kTopThreads - 1) {
+                unsigned long long t = (unsigned long long)ceil((double)top_p * (double)incl);
+                t = t > incl ? incl : t;
+                sh.target = t < 1ull ? 1ull : t;
+            }
+            __syncthreads();
+            remaining = sh.target;
+        }
+        if ((int)threadIdx.x < groups && incl - local < remaining && remaining <= incl) {
+            unsigned long long cum = incl - local;
+            for (int b = 0; b < g; ++b) {
+                const unsigned long long h = sh.hist[top - b];
+                if (remaining <= cum + h) {
+                    sh.digit = (uint32_t)(top - b);
+                    sh.above = cum;
+                    break;
+                }
+                cum += h;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << d) | sh.digit;
+        remaining -= sh.above;
+        used += d;
+        __syncthreads();  // hist, digit and above are rewritten next round
+    }
+    return prefix;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kTopThreads) void kl_topp_tau_kernel(const void* teacher, int64_t vocab, float top_p,
+                                                                  float c, float* tau_out)
+{
+    __shared__ TopPShared sh;
+    constexpr int V = Unit<BF16>::V;
+    const int64_t row = blockIdx.x;
+    const int64_t units = vocab >> 3;
+    const int64_t ubase = row * units;
+    const int UL = (int)((units + kTopThreads - 1) / kTopThreads);
+    const int tid = threadIdx.x;
+    auto for_t = [&](auto f) {
+#pragma unroll 4
+        for (int j = 0; j < UL; ++j) {
+            const int64_t u = (int64_t)j * kTopThreads + tid;
+            Unit<BF16> un;
+#pragma unroll
+            for (int q = 0; q < V; ++q) un.t[q] = u < units ? ldnt(teacher, V * (ubase + u) + q) : v4u{0u, 0u, 0u, 0u};
+            f(un, u < units);
+        }
+    };
+    uint32_t key;
+    if (top_p >= 1.0f) {
+        key = extreme_key<BF16, false>(for_t, sh.wave_key);
+    } else {
+        const float m = value_of_key<BF16>(extreme_key<BF16, true>(for_t, sh.wave_key)) * c;
+        key = nucleus_key<BF16>(top_p, c, m, for_t, sh);
+    }
+    if (tid == 0) tau_out[row] = value_of_key<BF16>(key);
+}
+
 // clear every tag a launch waits on (the whole records)
 __global__ void zero_records_kernel(uint32_t* rec, int64_t words)
 {
@@ -870,10 +1056,47 @@ size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab)
     return kl_workspace_bytes(tokens, vocab) + (((size_t)tokens * 4 + 255) & ~(size_t)255);
 }
 
+namespace {
+
+// rows longer than kMaxSegments record segments: one workgroup per row
+// streams it in every step (threshold from a.tau when given, else the k-th
+// largest teacher logit)
+hipError_t launch_topk_long_rows(const KlArgs& a, uint32_t kk, hipStream_t stream)
+{
+    const float c = kLog2e / a.temperature;
+    const float inv_t = 1.0f / a.temperature;
+    const float gmul = a.grad_scale / a.temperature;
+    const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
+    const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+    const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
+    const int64_t batch = (int64_t)1 << 20;
+    for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+        KlArgs b = a;
+        b.tokens = min(batch, a.tokens - r0);
+        b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
+        b.student = static_cast<const char*>(a.student) + r0 * in_row;
+        b.row_loss = a.row_loss + r0;
+        if (a.tau) b.tau = a.tau + r0;
+        if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
+        const dim3 grid((unsigned)b.tokens), block(kTopThreads);
+#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
+        if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
+        else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
+#undef KT
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+} // namespace
+
 hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream_t stream)
 {
     if (a.tokens > 0 && a.vocab > 0) {
         const uint32_t kk = (uint32_t)(k < a.vocab ? k : a.vocab);
+        KlArgs b = a;
+        b.tau = nullptr;
         if (segments(a.vocab) <= kMaxSegments) {
             // thresholds, then the one-pass segment kernels masked by them
             float* tau = reinterpret_cast<float*>(static_cast<char*>(workspace) + kl_workspace_bytes(a.tokens, a.vocab));
@@ -887,35 +1110,40 @@ hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream
                 hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
-            KlArgs b = a;
             b.tau = tau;
             hipError_t e = launch_rows(b, workspace, true, stream);
             if (e != hipSuccess) return e;
         } else {
-            // very long rows: one workgroup per row streams it in every step
-            const float c = kLog2e / a.temperature;
-            const float inv_t = 1.0f / a.temperature;
-            const float gmul = a.grad_scale / a.temperature;
-            const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
-            const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
-            const size_t g_row = (size_t)a.vocab * (a.grad_bf16 ? 2 : 4);
-            const int64_t batch = (int64_t)1 << 20;
-            for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
-                KlArgs b = a;
-                b.tokens = min(batch, a.tokens - r0);
-                b.teacher = static_cast<const char*>(a.teacher) + r0 * in_row;
-                b.student = static_cast<const char*>(a.student) + r0 * in_row;
-                b.row_loss = a.row_loss + r0;
-                if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
-                const dim3 grid((unsigned)b.tokens), block(kTopThreads);
-#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
-                if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
-                else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
-#undef KT
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-            }
+            hipError_t e = launch_topk_long_rows(b, kk, stream);
+            if (e != hipSuccess) return e;
         }
+    }
+    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_kl_topp(const KlArgs& a, float top_p, float* tau_out, void* workspace, hipStream_t stream)
+{
+    if (a.tokens > 0 && a.vocab > 0) {
+        // thresholds (into tau_out when given), then the masked KL
+        float* tau = tau_out ? tau_out
+                             : reinterpret_cast<float*>(static_cast<char*>(workspace) + kl_workspace_bytes(a.tokens, a.vocab));
+        const float c = kLog2e / a.temperature;
+        const int64_t batch = (int64_t)1 << 20;
+        const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
+        for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
+            const dim3 grid((unsigned)min(batch, a.tokens - r0)), block(kTopThreads);
+            const void* t = static_cast<const char*>(a.teacher) + r0 * in_row;
+            if (a.bf16_in) hipLaunchKernelGGL((kl_topp_tau_kernel<true>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
+            else hipLaunchKernelGGL((kl_topp_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        KlArgs b = a;
+        b.tau = tau;
+        hipError_t e = segments(a.vocab) <= kMaxSegments ? launch_rows(b, workspace, true, stream)
+                                                         : launch_topk_long_rows(b, 1u, stream);
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
     return hipGetLastError();

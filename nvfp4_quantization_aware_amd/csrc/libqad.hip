@@ -130,7 +130,8 @@ size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
     case QAD_OP_QUANTIZE:
     case QAD_OP_MSE_CALIBRATE: return record_bytes(B, R * C);
     case QAD_OP_KL: return round256(qad::kl_workspace_bytes(R, C));
-    case QAD_OP_KL_TOPK: return round256(qad::kl_topk_workspace_bytes(R, C));
+    case QAD_OP_KL_TOPK:
+    case QAD_OP_KL_TOPP: return round256(qad::kl_topk_workspace_bytes(R, C));
     case QAD_OP_W4A4_LINEAR: return round256(qad::linear_workspace_bytes(B, R, C));
     }
     return 0;
@@ -333,6 +334,52 @@ qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_d
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
     return hip_status(qad::launch_kl_topk(a, k, workspace, hs(stream)));
+}
+
+qad_status_t qad_kl_topp_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt, int64_t tokens,
+                                 int64_t vocab, float top_p, float temperature, float grad_scale, float* loss_out,
+                                 float* row_loss, void* grad_student, qad_dtype_t gt, float* tau_out,
+                                 void* workspace, size_t ws_bytes, qad_stream_t stream)
+{
+    if (!valid_dtype(lt) || (grad_student && !valid_dtype(gt))) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(1, tokens, vocab);
+    if (n < 0 || vocab % 8 != 0 || tokens > 0x7FFFFFFFll || vocab > 0x7FFFFFFFll) return QAD_ERR_SHAPE;
+    if (tokens > 0 && vocab == 0) return QAD_ERR_SHAPE;
+    if (!(top_p > 0.0f) || !isfinite(top_p)) return QAD_ERR_INVALID_ARG;
+    if (!(temperature > 0.0f) || !isfinite(temperature) || !isfinite(grad_scale)) return QAD_ERR_INVALID_ARG;
+    if (!loss_out) return QAD_ERR_INVALID_ARG;
+    if (n > 0 && (!teacher || !student)) return QAD_ERR_INVALID_ARG;
+    if (!aligned(teacher, 16) || !aligned(student, 16) || (grad_student && !aligned(grad_student, 16)) ||
+        !aligned(loss_out, 4) || (row_loss && !aligned(row_loss, 4)) || (tau_out && !aligned(tau_out, 4)))
+        return QAD_ERR_ALIGNMENT;
+    const size_t ib = (size_t)n * esize(lt), gb = grad_student ? (size_t)n * esize(gt) : 0;
+    if (grad_student && (ranges_overlap(teacher, ib, grad_student, gb) || ranges_overlap(student, ib, grad_student, gb)))
+        return QAD_ERR_INVALID_ARG;
+    if (tau_out && tokens > 0) {
+        const size_t tb = (size_t)tokens * 4;
+        if (ranges_overlap(tau_out, tb, teacher, ib) || ranges_overlap(tau_out, tb, student, ib) ||
+            (grad_student && ranges_overlap(tau_out, tb, grad_student, gb)) ||
+            ranges_overlap(tau_out, tb, loss_out, 4) || (row_loss && ranges_overlap(tau_out, tb, row_loss, tb)))
+            return QAD_ERR_INVALID_ARG;
+    }
+    if (tokens > 0) {
+        if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_KL_TOPP, 1, tokens, vocab)) return QAD_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
+        if (tau_out && ranges_overlap(tau_out, (size_t)tokens * 4, workspace, ws_bytes)) return QAD_ERR_INVALID_ARG;
+    }
+    qad::KlArgs a;
+    a.teacher = teacher;
+    a.student = student;
+    a.bf16_in = lt == QAD_BF16;
+    a.tokens = tokens;
+    a.vocab = vocab;
+    a.temperature = temperature;
+    a.grad_scale = grad_scale;
+    a.row_loss = row_loss ? row_loss : static_cast<float*>(workspace);
+    a.loss_out = loss_out;
+    a.grad = grad_student;
+    a.grad_bf16 = gt == QAD_BF16;
+    return hip_status(qad::launch_kl_topp(a, top_p, tau_out, workspace, hs(stream)));
 }
 
 qad_status_t qad_check_finite(const float* values, int64_t n, qad_stream_t stream)

@@ -98,6 +98,9 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);
 // teacher-top-k KL (k >= 1): the KL workspace followed by per-row thresholds
 size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab);
 hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream_t stream);
+// teacher-top-p (nucleus) KL; thresholds into tau_out when non-null, else into
+// the workspace slot of the top-k layout (kl_topk_workspace_bytes)
+hipError_t launch_kl_topp(const KlArgs& a, float top_p, float* tau_out, void* workspace, hipStream_t stream);
 
 // W4A4 linear: the QDQ records of the larger operand, then the GEMM scratch
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);

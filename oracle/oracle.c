@@ -461,6 +461,44 @@ static int cmp_desc(const void* a, const void* b)
     return x < y ? 1 : x > y ? -1 : 0;
 }
 
+/* KL of one row restricted to S = { v : t_v >= tau }, both softmaxes
+ * renormalised over S; gradient 0 outside S.  Returns the row loss. */
+static double kl_kept_row(const void* teacher, const void* student, int dtype, int64_t o, int64_t V,
+                          double tau, double T, double grad_scale, double* grad, int64_t* count_out)
+{
+    double mt = -INFINITY, ms = -INFINITY;
+    int64_t count = 0;
+    for (int64_t v = 0; v < V; ++v) {
+        const double tv = load_d(teacher, dtype, o + v);
+        if (!(tv >= tau)) continue;
+        ++count;
+        const double t = tv / T, s = load_d(student, dtype, o + v) / T;
+        if (t > mt) mt = t;
+        if (s > ms) ms = s;
+    }
+    double zt = 0.0, zs = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        if (!(load_d(teacher, dtype, o + v) >= tau)) continue;
+        zt += exp(load_d(teacher, dtype, o + v) / T - mt);
+        zs += exp(load_d(student, dtype, o + v) / T - ms);
+    }
+    const double lse_t = mt + log(zt), lse_s = ms + log(zs);
+    double kl = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        const double tv = load_d(teacher, dtype, o + v);
+        if (!(tv >= tau)) {
+            if (grad) grad[o + v] = 0.0;
+            continue;
+        }
+        const double logp = tv / T - lse_t, logq = load_d(student, dtype, o + v) / T - lse_s;
+        const double p = exp(logp);
+        kl += p * (logp - logq);
+        if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
+    }
+    if (count_out) *count_out = count;
+    return kl;
+}
+
 double orc_kl_topk_fwd_bwd(const void* teacher, const void* student, int dtype,
                            int64_t rows, int64_t V, int64_t k, double T, double grad_scale,
                            double* row_kl, double* grad, int64_t* row_count)
@@ -474,37 +512,66 @@ double orc_kl_topk_fwd_bwd(const void* teacher, const void* student, int dtype,
         for (int64_t v = 0; v < V; ++v) sorted[v] = load_d(teacher, dtype, o + v);
         qsort(sorted, (size_t)V, sizeof(double), cmp_desc);
         const double tau = sorted[kk - 1];
-        double mt = -INFINITY, ms = -INFINITY;
-        int64_t count = 0;
-        for (int64_t v = 0; v < V; ++v) {
-            const double tv = load_d(teacher, dtype, o + v);
-            if (!(tv >= tau)) continue;
-            ++count;
-            const double t = tv / T, s = load_d(student, dtype, o + v) / T;
-            if (t > mt) mt = t;
-            if (s > ms) ms = s;
-        }
-        double zt = 0.0, zs = 0.0;
-        for (int64_t v = 0; v < V; ++v) {
-            if (!(load_d(teacher, dtype, o + v) >= tau)) continue;
-            zt += exp(load_d(teacher, dtype, o + v) / T - mt);
-            zs += exp(load_d(student, dtype, o + v) / T - ms);
-        }
-        const double lse_t = mt + log(zt), lse_s = ms + log(zs);
-        double kl = 0.0;
-        for (int64_t v = 0; v < V; ++v) {
-            const double tv = load_d(teacher, dtype, o + v);
-            if (!(tv >= tau)) {
-                if (grad) grad[o + v] = 0.0;
-                continue;
-            }
-            const double logp = tv / T - lse_t, logq = load_d(student, dtype, o + v) / T - lse_s;
-            const double p = exp(logp);
-            kl += p * (logp - logq);
-            if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
-        }
+        const double kl = kl_kept_row(teacher, student, dtype, o, V, tau, T, grad_scale, grad,
+                                      row_count ? row_count + r : NULL);
         if (row_kl) row_kl[r] = kl;
-        if (row_count) row_count[r] = count;
+        total += kl;
+    }
+    free(sorted);
+    return rows > 0 ? total / (double)rows : 0.0;
+}
+
+/* ------------------------------------------------------------------------
+ * Teacher-top-p (nucleus) KL.  [Qwen] "3. QAD" names top-p as the variant to
+ * try after the top-k run, without defining it; the reading taken is the
+ * usual nucleus of the teacher distribution:
+ *   p = softmax(t/T) over the whole row;
+ *   walking the distinct teacher values from the largest down, accumulate
+ *   the mass of every entry equal to each; tau = the first value at which
+ *   the accumulated mass reaches top_p (top_p >= 1: every entry);
+ *   S = { v : t_v >= tau } (ties with tau kept), then exactly as top-k.
+ * Optional row_tau[rows]; row_mass[2*rows] = (mass strictly above tau, mass
+ * at or above tau), which bound the decision's margin.
+ * ---------------------------------------------------------------------- */
+double orc_kl_topp_fwd_bwd(const void* teacher, const void* student, int dtype,
+                           int64_t rows, int64_t V, double top_p, double T, double grad_scale,
+                           double* row_kl, double* grad, int64_t* row_count, double* row_tau,
+                           double* row_mass)
+{
+    double total = 0.0;
+    double* sorted = (double*)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    if (!sorted) return NAN;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t o = r * V;
+        double mt = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            sorted[v] = load_d(teacher, dtype, o + v);
+            if (sorted[v] / T > mt) mt = sorted[v] / T;
+        }
+        double zt = 0.0;
+        for (int64_t v = 0; v < V; ++v) zt += exp(sorted[v] / T - mt);
+        qsort(sorted, (size_t)V, sizeof(double), cmp_desc);
+        double tau = sorted[V - 1], above = 0.0, incl = 0.0;
+        if (top_p < 1.0) {
+            int64_t i = 0;
+            while (i < V) {
+                const double val = sorted[i];
+                double m = 0.0;
+                while (i < V && sorted[i] == val) m += exp(sorted[i++] / T - mt) / zt;
+                above = incl;
+                incl += m;
+                tau = val;
+                if (incl >= top_p) break;
+            }
+        } else {
+            for (int64_t v = 0; v < V; ++v) incl += exp(sorted[v] / T - mt) / zt;
+            above = incl - exp(sorted[V - 1] / T - mt) / zt;
+        }
+        const double kl = kl_kept_row(teacher, student, dtype, o, V, tau, T, grad_scale, grad,
+                                      row_count ? row_count + r : NULL);
+        if (row_kl) row_kl[r] = kl;
+        if (row_tau) row_tau[r] = tau;
+        if (row_mass) { row_mass[2 * r] = above; row_mass[2 * r + 1] = incl; }
         total += kl;
     }
     free(sorted);

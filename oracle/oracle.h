@@ -129,6 +129,16 @@ double orc_kl_topk_fwd_bwd(const void* teacher, const void* student, int dtype,
                            int64_t rows, int64_t V, int64_t k, double T, double grad_scale,
                            double* row_kl, double* grad, int64_t* row_count);
 
+/* ---- teacher-top-p (nucleus) KL -------------------------------------------
+ * As orc_kl_topk_fwd_bwd with tau = the largest teacher value at which the
+ * teacher mass of the entries at or above it reaches top_p (ties kept;
+ * top_p >= 1: every entry).  Optional row_tau[rows] (the threshold) and
+ * row_mass[2*rows] (mass strictly above tau, mass at or above tau).        */
+double orc_kl_topp_fwd_bwd(const void* teacher, const void* student, int dtype,
+                           int64_t rows, int64_t V, double top_p, double T, double grad_scale,
+                           double* row_kl, double* grad, int64_t* row_count, double* row_tau,
+                           double* row_mass);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,7 @@ def _load():
             "orc_nvfp4_qdq_bwd_clipped": (None, [vp, i32, vp, i32, i64, vp, f32, vp, vp]),
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
             "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
+            "orc_kl_topp_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, f64, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -315,9 +316,38 @@ def kl_topk_fwd_bwd(teacher: np.ndarray, student: np.ndarray, k: int, T: float =
     return float(loss), row, g, cnt
 
 
+def kl_topp_fwd_bwd(teacher: np.ndarray, student: np.ndarray, top_p: float, T: float = 1.0,
+                    grad_scale: float | None = None, want_grad: bool = True):
+    """Binary64 KL restricted to the teacher's nucleus of each row: the
+    entries at or above tau, the largest teacher value at which the teacher
+    mass of the entries at or above it reaches top_p (ties kept); both
+    softmaxes renormalised over that set, gradient 0 outside it.
+
+    Returns (mean loss, row losses f64[rows], gradient f64[rows, V] or None,
+    set sizes i64[rows], tau f64[rows], masses f64[rows, 2] = (mass strictly
+    above tau, mass at or above tau)).
+    """
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    assert t.shape == s.shape and t.dtype == s.dtype and top_p > 0
+    V = t.shape[-1]
+    rows = t.size // V if V else 0
+    if grad_scale is None:
+        grad_scale = 1.0 / rows if rows else 0.0
+    row = np.empty(rows, np.float64)
+    cnt = np.empty(rows, np.int64)
+    tau = np.empty(rows, np.float64)
+    mass = np.empty((rows, 2), np.float64)
+    g = np.empty((rows, V), np.float64) if want_grad else None
+    loss = _load().orc_kl_topp_fwd_bwd(_ptr(t), _ptr(s), _dtype_code(t), rows, V, float(top_p), float(T),
+                                       float(grad_scale), _ptr(row), _ptr(g), _ptr(cnt), _ptr(tau), _ptr(mass))
+    return float(loss), row, g, cnt, tau, mass
+
+
 __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
     "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd", "nvfp4_qdq_bwd_clipped",
+    "kl_topp_fwd_bwd",
 ]

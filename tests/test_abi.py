@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -81,8 +81,9 @@ def test_workspace_sizes(L):
     for tokens, vocab in ((8192, 131072), (3, 8), (1000, 248320), (3, 1 << 22)):
         kl = L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab)
         assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPK, 1, tokens, vocab) == kl + -(-(tokens * 4) // 256) * 256
+        assert L.qad_workspace_bytes(q.QAD_OP_KL_TOPP, 1, tokens, vocab) == kl + -(-(tokens * 4) // 256) * 256
     assert L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, -1, 2, 16) == 0
-    for op in range(6):
+    for op in range(7):
         assert L.qad_workspace_bytes(op, 1, 1, 16) % 256 == 0
 
 
@@ -268,6 +269,39 @@ def test_kl_topk_rejects(L):
     assert call(a12=None, a13=0) == WS                # no workspace
     assert call(a13=16) == WS
     assert call(a12=P * 5 + 64) == ALIGN
+
+
+def test_kl_topp_rejects(L):
+    f = L.qad_kl_topp_fwd_bwd
+    good = [P, P * 2, 1, 4, 64, 0.9, 1.0, 0.25, P * 3, None, P * 4, 1, P * 6, P * 5, 1 << 16, None]
+
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a2=9) == DTYPE
+    assert call(a11=9) == DTYPE
+    assert call(a4=60) == SHAPE                       # vocab % 8
+    assert call(a3=-1) == SHAPE
+    assert call(a3=2, a4=0) == SHAPE                  # rows without a vocabulary
+    assert call(a5=0.0) == INVALID                    # top_p
+    assert call(a5=-0.5) == INVALID
+    assert call(a5=float("nan")) == INVALID
+    assert call(a5=float("inf")) == INVALID
+    assert call(a6=0.0) == INVALID                    # temperature
+    assert call(a7=float("nan")) == INVALID
+    assert call(a8=None) == INVALID                   # loss_out
+    assert call(a1=None) == INVALID
+    assert call(a0=P_ODD) == ALIGN
+    assert call(a12=P * 6 + 2) == ALIGN               # tau_out
+    assert call(a10=P + 32) == INVALID                # gradient overlaps the teacher
+    assert call(a12=P + 64) == INVALID                # thresholds over the teacher
+    assert call(a12=P * 5 + 256) == INVALID           # thresholds inside the workspace
+    assert call(a13=None, a14=0) == WS                # no workspace
+    assert call(a14=16) == WS
+    assert call(a13=P * 5 + 64) == ALIGN
 
 
 def test_check_finite_rejects(L):
