@@ -26,8 +26,6 @@ constexpr float kRcp6 = 0x1.555556p-3f;
 // range); smaller ones take IEEE division everywhere.
 constexpr float kFastMinScale = 0x1p-80f;
 constexpr int kQThreads = 256;
-// candidate codes the unrolled MSE walk covers (k in [0.5, 1] spans <= 9)
-constexpr int kMseCodes = 9;
 // A bounded wait: after this many wall-clock ticks (20 ms at the 100 MHz
 // counter) a workgroup stops waiting and computes what it waited for itself.
 constexpr uint64_t kWaitTicks = 2000000;
@@ -213,7 +211,8 @@ __device__ __forceinline__ float quotient_pos(float x, float s, float r)
 template <bool FAST>
 __device__ __forceinline__ float quotient(float x, float s, float r)
 {
-    return __builtin_copysignf(quotient_pos<FAST>(__builtin_fabsf(x), s, r), x);
+    if constexpr (FAST) return div_rcp_signed(x, s, r);
+    else return __builtin_copysignf(quotient_pos<FAST>(__builtin_fabsf(x), s, r), x);
 }
 
 // Code one unit (half a block; the lane pair owns the block).  Returns the
@@ -229,8 +228,20 @@ __device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t 
     sb &= 127u;
     const float s = tab.seff[sb], r = tab.rcp[sb];
     float q[8];
+    if constexpr (FROZEN && FAST) {
+        // A frozen scale may be far below an element: x r would overflow and
+        // the reciprocal scheme turn it into NaN.  Every quotient >= 8
+        // saturates to the same code, so x is first clamped to +-8 s (exact;
+        // signed zeros and everything below the bound pass unchanged).  A
+        // dynamic scale keeps every quotient below 12, and IEEE division
+        // (small tensor scales) saturates by itself.
+        const float lim = s > 0.0f ? 8.0f * s : 0x1.fffffep127f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quotient<FAST>(e[i], s, r);
+        for (int i = 0; i < 8; ++i) q[i] = quotient<FAST>(__builtin_amdgcn_fmed3f(e[i], -lim, lim), s, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = quotient<FAST>(e[i], s, r);
+    }
     uint32_t c = 0;
     c = fp4_encode_pair<0>(c, q[0], q[1]);
     c = fp4_encode_pair<1>(c, q[2], q[3]);
@@ -607,40 +618,28 @@ __device__ __forceinline__ void calibrate_tensor(const MseArgs& a, int64_t b, in
         // candidate whose largest element alone already costs more than the
         // best error so far cannot win; once the largest element is clipped
         // (6 s <= amax_b) that cost only grows for smaller codes, so stop.
+        // Each lane skips its own pruned candidates before every full
+        // evaluation, so a wave runs as many evaluations as its busiest lane
+        // needs, not one per candidate position any lane evaluates.
         uint32_t best = c_hi;
         float best_err = __builtin_inff();
-        if (c_hi - c_lo < (uint32_t)kMseCodes) {
-            // the usual case (k in [0.5, 1] spans at most 9 codes): a fixed,
-            // unrolled walk whose table reads are all issued up front
-            float sv[kMseCodes], rv[kMseCodes];
-#pragma unroll
-            for (int j = 0; j < kMseCodes; ++j) {
-                const int cc = max((int)c_hi - j, 0);
-                sv[j] = tab.seff[cc];
-                rv[j] = tab.rcp[cc];
+        const int n = (int)(c_hi - c_lo) + 1;
+        int j = 0;
+        for (;;) {
+            float sj = 0.0f, rj = 0.0f;
+            bool done = false;
+            for (;;) {
+                if (j >= n) { done = true; break; }
+                sj = tab.seff[c_hi - j];
+                rj = tab.rcp[c_hi - j];
+                if (!(max_term<FAST>(amax_b, sj, rj) > best_err)) break;
+                if (6.0f * sj <= amax_b) { done = true; break; }
+                ++j;
             }
-            bool live = true;
-#pragma unroll
-            for (int j = 0; j < kMseCodes; ++j) {
-                live = live && (int)c_hi - j >= (int)c_lo;
-                if (!live) continue;
-                if (max_term<FAST>(amax_b, sv[j], rv[j]) > best_err) {
-                    live = !(6.0f * sv[j] <= amax_b);
-                    continue;
-                }
-                const float err = block_error<FAST>(e, sv[j], rv[j]);
-                if (err <= best_err) { best_err = err; best = c_hi - (uint32_t)j; }
-            }
-        } else {
-            for (int cc = (int)c_hi; cc >= (int)c_lo; --cc) {
-                const float s = tab.seff[cc], r = tab.rcp[cc];
-                if (max_term<FAST>(amax_b, s, r) > best_err) {
-                    if (6.0f * s <= amax_b) break;
-                    continue;
-                }
-                const float err = block_error<FAST>(e, s, r);
-                if (err <= best_err) { best_err = err; best = (uint32_t)cc; }
-            }
+            if (done) break;
+            const float err = block_error<FAST>(e, sj, rj);
+            if (err <= best_err) { best_err = err; best = c_hi - (uint32_t)j; }
+            ++j;
         }
         a.scales_out[gb] = (uint8_t)best;
     }

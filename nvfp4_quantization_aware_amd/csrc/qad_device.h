@@ -74,6 +74,20 @@ __device__ __forceinline__ float div_rcp(float x, float s, float r)
     return __builtin_fmaf(e1, r, q1);
 }
 
+// The same quotient with x's sign on every result, signed zeros included: the
+// steps of div_rcp with each residual negated (s q - x, then multiplied by
+// -r).  Negation is exact and rounding to nearest is symmetric, so every
+// nonzero result equals div_rcp's, while a zero quotient (x = +-0, or r = 0
+// for s = 0) keeps the sign of x instead of becoming +0.
+__device__ __forceinline__ float div_rcp_signed(float x, float s, float r)
+{
+    const float q0 = x * r;
+    const float e0 = __builtin_fmaf(s, q0, -x);
+    const float q1 = __builtin_fmaf(e0, -r, q0);
+    const float e1 = __builtin_fmaf(s, q1, -x);
+    return __builtin_fmaf(e1, -r, q1);
+}
+
 // ---------------------------------------------------------------------------
 // gfx950 FP4 conversions with unit scale.  Encoding rounds to the nearest
 // E2M1 value with ties to the even code and saturates, taking the code's sign

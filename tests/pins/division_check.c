@@ -17,7 +17,14 @@
  *   - random binary32 x with |x/s| in [2^-12, 2^10],
  * for divisors: 6, every E4M3 value times assorted tensor scales, plus random
  * binary32 in [2^-89, 2^100].
- * Prints: exact-range-checked, exact-range-mismatches, code-mismatches.
+ * The signed form the quantizer uses (residuals negated: e = s*q - x, then
+ * q + e*(-y)) must equal copysign(quot(|x|), x) bit for bit on every input
+ * above whose quotient does not overflow (x*y = inf turns both forms into
+ * NaN; the quantizer never lets that happen: dynamic scales keep quotients
+ * below 12 and frozen ones see x clamped to +-8 s first), and on +-0 for
+ * every divisor and for s = 0 (y = 0).
+ * Prints: exact-range-checked, exact-range-mismatches, code-mismatches,
+ * signed-form-mismatches.
  */
 #include <math.h>
 #include <stdint.h>
@@ -50,6 +57,15 @@ static float quot(float x, float s, float y)
     return fmaf(r1, y, q1);
 }
 
+static float quot_signed(float x, float s, float y)
+{
+    float q0 = x * y;
+    float r0 = fmaf(s, q0, -x);
+    float q1 = fmaf(r0, -y, q0);
+    float r1 = fmaf(s, q1, -x);
+    return fmaf(r1, -y, q1);
+}
+
 int main(void)
 {
     enum { ND = 4000 };
@@ -72,8 +88,22 @@ int main(void)
         divs[nd++] = u2f((ex << 23) | (uint32_t)(st & 0x7FFFFF));
     }
     const float MID[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    unsigned long long exact_checked = 0, exact_bad = 0, code_bad = 0;
-#pragma omp parallel for reduction(+ : exact_checked, exact_bad, code_bad) schedule(dynamic, 8)
+    unsigned long long exact_checked = 0, exact_bad = 0, code_bad = 0, signed_bad = 0;
+    /* zeros: every divisor, and a zero divisor with y = 0 */
+    for (int i = 0; i <= ND; ++i) {
+        float s = i < ND ? divs[i] : 0.0f, y = i < ND ? 1.0f / s : 0.0f;
+        for (int sg = 0; sg < 2; ++sg) {
+            float z = sg ? -0.0f : 0.0f;
+            signed_bad += f2u(quot_signed(z, s, y)) != f2u(copysignf(quot(0.0f, s, y), z));
+        }
+        if (i == ND)
+            for (uint32_t h = 1; h < 0x7F80; ++h) {
+                float x = u2f(h << 16);
+                signed_bad += f2u(quot_signed(x, 0.0f, 0.0f)) != f2u(0.0f);
+                signed_bad += f2u(quot_signed(-x, 0.0f, 0.0f)) != f2u(-0.0f);
+            }
+    }
+#pragma omp parallel for reduction(+ : exact_checked, exact_bad, code_bad, signed_bad) schedule(dynamic, 8)
     for (int i = 0; i < ND; ++i) {
         float s = divs[i], y = 1.0f / s;
         float xs[2];
@@ -86,6 +116,9 @@ int main(void)
                 exact_bad += f2u(q_) != f2u(ref_);                               \
             }                                                                    \
             code_bad += (nearest_code(q_) & 7) != (nearest_code(ref_) & 7);    \
+            if (!isinf(x_ * y))                                                  \
+                signed_bad += f2u(quot_signed(x_, s, y)) !=                      \
+                              f2u(copysignf(quot(fabsf(x_), s, y), x_));         \
         } while (0)
         for (uint32_t h = 1; h < 0x7F80; ++h) {
             xs[0] = u2f(h << 16);
@@ -109,6 +142,6 @@ int main(void)
             CHECK(r * s);
         }
     }
-    printf("%llu %llu %llu\n", exact_checked, exact_bad, code_bad);
+    printf("%llu %llu %llu %llu\n", exact_checked, exact_bad, code_bad, signed_bad);
     return 0;
 }

@@ -163,6 +163,27 @@ def test_frozen_scales(dev, orc):
     check_quantize(orc, x3.to(dev), "frozen-tiny-scale", frozen=(rs3, np.array([1e-28], np.float32)))
 
 
+def test_frozen_quotient_overflow(dev, orc):
+    # frozen scales far below the elements: x / s_eff exceeds the binary32
+    # range (the oracle's quotient is inf and saturates to +-6); tensor scale
+    # 2^-80 (reciprocal division) and 2^-81 (IEEE division), signed zeros and
+    # ordinary values in the same blocks
+    x = torch.empty((2, 4, 64), dtype=torch.float32)
+    g = torch.Generator().manual_seed(12)
+    x.copy_(torch.randn((2, 4, 64), generator=g) * 1e30)
+    x[:, :, ::7] = 3.0e38
+    x[:, :, 1::7] = -3.0e38
+    x[:, :, 2::7] = -0.0
+    x[:, :, 3::7] = 0.0
+    x[:, :, 4::7] = 1e-30
+    x[:, 0, :16] = 2.0 ** -88                      # an ordinary block under the tiny scale
+    rs = np.full((2, 4, 4), 1, np.uint8)          # E4M3 code 1: 2^-9
+    rs[:, :, 3] = 0                               # s_eff = 0: signed zeros
+    rs[:, 1, 2] = 0x7E                            # 448
+    for ts in (2.0 ** -80, 2.0 ** -81):
+        check_quantize(orc, x.to(dev), "frozen-overflow ts=%g" % ts, frozen=(rs, np.array([ts, ts], np.float32)))
+
+
 def test_qdq_fwd_equals_quantize_y(dev, orc):
     w, _ = synth.moe_weights_bf16(experts=2, rows=128, cols=256, seed=21, with_grad=False)
     w = w.to(dev)
