@@ -758,11 +758,12 @@ __device__ __forceinline__ float value_of_key(uint32_t key)
 // teacher row streamed once per round.  (Holding a 128K-logit row in
 // registers allows one 1024-lane workgroup per CU and measured slower than
 // two streaming ones, whose loads and LDS histograms overlap.)
-template <bool BF16>
+template <bool BF16, bool REDO = false>
 __global__ __launch_bounds__(kTopThreads) void kl_topk_tau_kernel(const void* teacher, int64_t vocab, uint32_t k,
                                                                   float* tau_out)
 {
     __shared__ TopShared sh;
+    if (REDO && !__builtin_isnan(tau_out[blockIdx.x])) return;   // only rows the count kernel left NaN
     constexpr int V = Unit<BF16>::V;
     const int64_t row = blockIdx.x;
     const int64_t units = vocab >> 3;
@@ -802,6 +803,17 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_tau_kernel(const void* te
 // mass).  The teacher row is streamed once per step: three times for bf16,
 // four for fp32.
 // ---------------------------------------------------------------------------
+// floor(w 2^40) as a 64-bit integer, w in [0, 2]: w 2^40 is an exact float
+// with at most 24 significant bits, split exactly into its high and low
+// 32-bit parts (the same value as a plain truncating conversion)
+__device__ __forceinline__ unsigned long long fix40(float w)
+{
+    const float x = w * 0x1p40f;
+    const uint32_t hi = (uint32_t)(x * 0x1p-32f);
+    const uint32_t lo = (uint32_t)__builtin_fmaf((float)hi, -0x1p32f, x);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
 struct TopPShared {
     unsigned long long hist[1 << kDigitBits];
     unsigned long long wave_tot[kTopThreads / 64];
@@ -883,8 +895,7 @@ __device__ uint32_t nucleus_key(float top_p, float c, float m, ForT for_t, TopPS
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if (used == 0 || (key[i] >> (KB - used)) == prefix) {
-                    const unsigned long long w =
-                        (unsigned long long)(exp2_hw(__builtin_fmaf(tv[i], c, -m)) * 0x1p40f);
+                    const unsigned long long w = fix40(exp2_hw(__builtin_fmaf(tv[i], c, -m)));
                     if (w) atomicAdd(&sh.hist[(key[i] >> shift) & (nb - 1)], w);
                 }
             }
@@ -930,11 +941,12 @@ __device__ uint32_t nucleus_key(float top_p, float c, float m, ForT for_t, TopPS
     return prefix;
 }
 
-template <bool BF16>
+template <bool BF16, bool REDO = false>
 __global__ __launch_bounds__(kTopThreads) void kl_topp_tau_kernel(const void* teacher, int64_t vocab, float top_p,
                                                                   float c, float* tau_out)
 {
     __shared__ TopPShared sh;
+    if (REDO && !__builtin_isnan(tau_out[blockIdx.x])) return;   // only rows the count kernel left NaN
     constexpr int V = Unit<BF16>::V;
     const int64_t row = blockIdx.x;
     const int64_t units = vocab >> 3;
@@ -959,6 +971,199 @@ __global__ __launch_bounds__(kTopThreads) void kl_topp_tau_kernel(const void* te
         key = nucleus_key<BF16>(top_p, c, m, for_t, sh);
     }
     if (tid == 0) tau_out[row] = value_of_key<BF16>(key);
+}
+
+// ---------------------------------------------------------------------------
+// Thresholds of bf16 rows in one read of the teacher.  A bf16 logit is one of
+// 65536 keys and equal keys are equal values, so the count of every key
+// determines the k-th largest value exactly, and, since the entries of one
+// key share one fixed-point weight floor(2^(c v - m) 2^40), the nucleus too
+// (the same integer sums as the radix rounds above, so the same choice).  The
+// counts live in LDS as 16-bit halves of 32768 words (128 KiB; ds_add without
+// return).  A half that passes 65535 carries into its neighbour or out of
+// the word, which can only lower the sum of all halves, so a sum different
+// from the row length (more than 65535 equal logits in the row) sends the
+// workgroup to the streaming radix rounds instead.
+// ---------------------------------------------------------------------------
+constexpr int kSelWords = 32768;        // two 16-bit counters per word
+constexpr int kSelKeysPerLane = 65536 / kTopThreads;
+
+struct alignas(16) SelShared {
+    struct {
+        uint32_t hist[kSelWords];
+        unsigned long long wave_tot64[kTopThreads / 64];
+        uint32_t wave_tot[kTopThreads / 64];
+        uint32_t wave_key[kTopThreads / 64];
+        unsigned long long total64, target, rem64;
+        uint32_t total, key, lane, rem;
+    } c;
+};
+
+__device__ __forceinline__ uint32_t sel_count(const uint32_t* hist, uint32_t key)
+{
+    return (hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
+}
+
+// TOPP: nucleus of mass top_p (top_p >= 1: the smallest key); else the k-th
+// largest.  Returns the threshold key of the row.
+// count the 16 teacher keys of two units into the histogram
+__device__ __forceinline__ void sel_count_unit(uint32_t* hist, const v4u& v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t k0 = key16(w[i] & 0xFFFFu), k1 = key16(w[i] >> 16);
+        atomicAdd(&hist[k0 >> 1], 1u << ((k0 & 1u) * 16u));
+        atomicAdd(&hist[k1 >> 1], 1u << ((k1 & 1u) * 16u));
+    }
+}
+
+// The threshold key of a row from its counted histogram (TOPP: the nucleus of
+// mass top_p, top_p >= 1 the smallest key; else the k-th largest), or
+// 0xFFFFFFFF when a counter overflowed.
+template <bool TOPP>
+__device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, SelShared& sh)
+{
+    const int tid = threadIdx.x;
+    // lane l owns the kSelKeysPerLane keys below 65536 - kSelKeysPerLane l
+    // (32 words); order-free passes over them start at a lane-dependent word
+    // so that the lanes of a wave read different LDS banks
+    constexpr int kWordsPerLane = kSelKeysPerLane / 2;
+    const uint32_t hi = 65535u - (uint32_t)tid * kSelKeysPerLane;
+    const uint32_t whi = hi >> 1;
+    auto word_at = [&](int b) { return whi - (uint32_t)((b + tid) & (kWordsPerLane - 1)); };
+    uint32_t local = 0;
+#pragma unroll 8
+    for (int b = 0; b < kWordsPerLane; ++b) {
+        const uint32_t w = sh.c.hist[word_at(b)];
+        local += (w & 0xFFFFu) + (w >> 16);
+    }
+    const uint32_t incl = block_incl_scan(local, sh.c.wave_tot);
+    if (tid == kTopThreads - 1) sh.c.total = incl;
+    __syncthreads();
+    if ((int64_t)sh.c.total != vocab) return 0xFFFFFFFFu;   // a counter overflowed
+    if constexpr (!TOPP) {
+        // the lane whose keys hold rank k, then its 64 keys across wave 0
+        if (incl - local < k && k <= incl) { sh.c.lane = (uint32_t)tid; sh.c.rem = k - (incl - local); }
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t key = 65535u - sh.c.lane * kSelKeysPerLane - (uint32_t)tid;
+            uint32_t v = sel_count(sh.c.hist, key);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t n = __shfl_up(v, o, 64);
+                if (tid >= o) v += n;
+            }
+            const unsigned long long hit = __ballot(v >= sh.c.rem);
+            if (tid == 0) sh.c.key = 65535u - sh.c.lane * kSelKeysPerLane - (uint32_t)__builtin_ctzll(hit);
+        }
+        __syncthreads();
+        return sh.c.key;
+    } else {
+        // the largest (smallest for top_p >= 1) key present
+        const bool want_min = top_p >= 1.0f;
+        uint32_t e = want_min ? 0xFFFFFFFFu : 0u;
+#pragma unroll 4
+        for (int b = 0; b < kWordsPerLane; ++b) {
+            const uint32_t wi = word_at(b), w = sh.c.hist[wi];
+            if (w & 0xFFFFu) e = want_min ? min(e, 2u * wi) : umax(e, 2u * wi);
+            if (w >> 16) e = want_min ? min(e, 2u * wi + 1u) : umax(e, 2u * wi + 1u);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint32_t n = __shfl_xor(e, o, 64);
+            e = want_min ? min(e, n) : umax(e, n);
+        }
+        if ((tid & 63) == 0) sh.c.wave_key[tid >> 6] = e;
+        __syncthreads();
+        e = sh.c.wave_key[0];
+        for (int i = 1; i < kTopThreads / 64; ++i) e = want_min ? min(e, sh.c.wave_key[i]) : umax(e, sh.c.wave_key[i]);
+        if (want_min) return e;
+        const float m = value_of_key<true>(e) * c;
+        // fixed-point mass of each key: count x floor(2^(c v - m) 2^40)
+        auto key_mass = [&](uint32_t key, uint32_t n) {
+            return fix40(exp2_hw(__builtin_fmaf(value_of_key<true>(key), c, -m))) * n;
+        };
+        unsigned long long lm = 0;
+#pragma unroll 2
+        for (int b = 0; b < kWordsPerLane; ++b) {
+            const uint32_t wi = word_at(b), w = sh.c.hist[wi];
+            lm += key_mass(2u * wi, w & 0xFFFFu) + key_mass(2u * wi + 1u, w >> 16);
+        }
+        const unsigned long long incl64 = block_incl_scan64(lm, sh.c.wave_tot64);
+        if (tid == kTopThreads - 1) {
+            unsigned long long t = (unsigned long long)ceil((double)top_p * (double)incl64);
+            t = t > incl64 ? incl64 : t;
+            sh.c.target = t < 1ull ? 1ull : t;
+        }
+        __syncthreads();
+        const unsigned long long target = sh.c.target;
+        if (incl64 - lm < target && target <= incl64) { sh.c.lane = (uint32_t)tid; sh.c.rem64 = target - (incl64 - lm); }
+        __syncthreads();
+        if (tid < 64) {
+            const uint32_t key = 65535u - sh.c.lane * kSelKeysPerLane - (uint32_t)tid;
+            unsigned long long v = key_mass(key, sel_count(sh.c.hist, key));
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const unsigned long long n = __shfl_up(v, o, 64);
+                if (tid >= o) v += n;
+            }
+            const unsigned long long hit = __ballot(v >= sh.c.rem64);
+            if (tid == 0) sh.c.key = 65535u - sh.c.lane * kSelKeysPerLane - (uint32_t)__builtin_ctzll(hit);
+        }
+        __syncthreads();
+        return sh.c.key;
+    }
+}
+
+// bf16 teacher rows: thresholds by the key counts (a row whose counters
+// overflow is left NaN for the radix kernels).  One workgroup per CU (the histogram fills the LDS) walks rows
+// r = blockIdx.x, + gridDim.x, ...; a lane streams its units in batches of
+// kSelBatch with the next batch (the next row's first, across rows) in
+// flight while it counts the current one and while the row is scanned.
+constexpr int kSelBatch = 4;
+
+template <bool TOPP>
+__global__ __launch_bounds__(kTopThreads) void kl_sel16_kernel(const void* teacher, int64_t rows, int64_t vocab,
+                                                               uint32_t k, float top_p, float c, float* tau_out)
+{
+    __shared__ SelShared sh;
+    const int64_t units = vocab >> 3;
+    const int tid = threadIdx.x;
+    const int64_t per_batch = (int64_t)kSelBatch * kTopThreads;
+    const int nbatch = (int)((units + per_batch - 1) / per_batch);
+    auto load_batch = [&](int64_t row, int bi, v4u (&v)[kSelBatch]) {
+#pragma unroll
+        for (int q = 0; q < kSelBatch; ++q) {
+            const int64_t u = (int64_t)bi * per_batch + (int64_t)q * kTopThreads + tid;
+            v[q] = row < rows && u < units ? ldnt(teacher, row * units + u) : v4u{0u, 0u, 0u, 0u};
+        }
+    };
+    v4u cur[kSelBatch], nxt[kSelBatch];
+    int64_t row = blockIdx.x;
+    load_batch(row, 0, cur);
+    for (int i = tid; i < kSelWords / 4; i += kTopThreads) reinterpret_cast<v4u*>(sh.c.hist)[i] = v4u{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (; row < rows; row += gridDim.x) {
+        for (int bi = 0; bi < nbatch; ++bi) {
+            if (bi + 1 < nbatch) load_batch(row, bi + 1, nxt);
+            else load_batch(row + gridDim.x, 0, nxt);
+#pragma unroll 1
+            for (int q = 0; q < kSelBatch; ++q)
+                if ((int64_t)bi * per_batch + (int64_t)q * kTopThreads + tid < units) sel_count_unit(sh.c.hist, cur[q]);
+#pragma unroll
+            for (int q = 0; q < kSelBatch; ++q) cur[q] = nxt[q];
+        }
+        __syncthreads();
+        const uint32_t key = sel16_key<TOPP>(vocab, k, top_p, c, sh);
+        // a counter overflowed (more than 65535 equal logits): NaN marks the
+        // row for the streaming radix kernels launched after this one
+        if (tid == 0) tau_out[row] = key == 0xFFFFFFFFu ? __builtin_nanf("") : value_of_key<true>(key);
+        __syncthreads();
+        for (int i = tid; i < kSelWords / 4; i += kTopThreads)
+            reinterpret_cast<v4u*>(sh.c.hist)[i] = v4u{0u, 0u, 0u, 0u};
+        __syncthreads();
+    }
 }
 
 // clear every tag a launch waits on (the whole records)
@@ -1058,6 +1263,21 @@ size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab)
 
 namespace {
 
+// workgroups of the persistent bf16 threshold kernel: one per CU (cached per
+// device), never more than rows
+dim3 sel_grid(int64_t rows)
+{
+    static int cache[64];
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        cus = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+        if (!cus && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            __atomic_store_n(&cache[dev], cus, __ATOMIC_RELAXED);
+    }
+    if (cus <= 0) cus = 256;
+    return dim3((unsigned)max((int64_t)1, min(rows, (int64_t)cus)));
+}
+
 // rows longer than kMaxSegments record segments: one workgroup per row
 // streams it in every step (threshold from a.tau when given, else the k-th
 // largest teacher logit)
@@ -1105,8 +1325,11 @@ hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream
             for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
                 const dim3 grid((unsigned)min(batch, a.tokens - r0)), block(kTopThreads);
                 const void* t = static_cast<const char*>(a.teacher) + r0 * in_row;
-                if (a.bf16_in) hipLaunchKernelGGL((kl_topk_tau_kernel<true>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
-                else hipLaunchKernelGGL((kl_topk_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
+                if (a.bf16_in) {
+                    hipLaunchKernelGGL((kl_sel16_kernel<false>), sel_grid(min(batch, a.tokens - r0)), block, 0, stream, t,
+                                       min(batch, a.tokens - r0), a.vocab, kk, 1.0f, 0.0f, tau + r0);
+                    hipLaunchKernelGGL((kl_topk_tau_kernel<true, true>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
+                } else hipLaunchKernelGGL((kl_topk_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, kk, tau + r0);
                 hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
@@ -1134,8 +1357,11 @@ hipError_t launch_kl_topp(const KlArgs& a, float top_p, float* tau_out, void* wo
         for (int64_t r0 = 0; r0 < a.tokens; r0 += batch) {
             const dim3 grid((unsigned)min(batch, a.tokens - r0)), block(kTopThreads);
             const void* t = static_cast<const char*>(a.teacher) + r0 * in_row;
-            if (a.bf16_in) hipLaunchKernelGGL((kl_topp_tau_kernel<true>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
-            else hipLaunchKernelGGL((kl_topp_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
+            if (a.bf16_in) {
+                hipLaunchKernelGGL((kl_sel16_kernel<true>), sel_grid(min(batch, a.tokens - r0)), block, 0, stream, t,
+                                   min(batch, a.tokens - r0), a.vocab, 1u, top_p, c, tau + r0);
+                hipLaunchKernelGGL((kl_topp_tau_kernel<true, true>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
+            } else hipLaunchKernelGGL((kl_topp_tau_kernel<false>), grid, block, 0, stream, t, a.vocab, top_p, c, tau + r0);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
