@@ -62,7 +62,15 @@ struct PlanKey {
     }
 };
 
-bool make_plan(hipblasLtHandle_t h, const PlanKey& key, GemmPlan& p)
+// The heuristic's candidates (up to kGemmCandidates) are timed on the first
+// call's own operands and the fastest is kept: the heuristic's first choice
+// runs some of these shapes at two thirds of the best candidate's rate.
+// Timing synchronizes the stream once per plan; under graph capture (where
+// that is not allowed) the first candidate is taken untimed.
+constexpr int kGemmCandidates = 16;
+
+bool make_plan(hipblasLtHandle_t h, const PlanKey& key, GemmPlan& p, const void* A, const void* B, void* D, void* ws,
+               hipStream_t stream)
 {
     if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) return false;
     const int32_t opa = key.ta ? HIPBLAS_OP_T : HIPBLAS_OP_N, opb = key.tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
@@ -79,17 +87,46 @@ bool make_plan(hipblasLtHandle_t h, const PlanKey& key, GemmPlan& p)
     hipblasLtMatmulPreference_t pref = nullptr;
     if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
     const uint64_t wsb = kGemmWorkspace;
-    hipblasLtMatmulHeuristicResult_t res[1];
+    hipblasLtMatmulHeuristicResult_t res[kGemmCandidates];
     int found = 0;
     const bool ok =
         hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) ==
             HIPBLAS_STATUS_SUCCESS &&
-        hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.ld, p.ld, pref, 1, res, &found) ==
+        hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.la, p.lb, p.ld, p.ld, pref, kGemmCandidates, res, &found) ==
             HIPBLAS_STATUS_SUCCESS &&
         found >= 1;
     hipblasLtMatmulPreferenceDestroy(pref);
-    if (ok) p.algo = res[0].algo;
-    return ok;
+    if (!ok) return false;
+    p.algo = res[0].algo;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (found == 1 || hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return true;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return true;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return true;
+    }
+    const float alpha = 1.0f, beta = 0.0f;
+    float best = 0.0f;
+    for (int i = 0; i < found; ++i) {
+        if (res[i].workspaceSize > kGemmWorkspace) continue;
+        auto run = [&]() {
+            return hipblasLtMatmul(h, p.desc, &alpha, A, p.la, B, p.lb, &beta, D, p.ld, D, p.ld, &res[i].algo, ws,
+                                   kGemmWorkspace, stream) == HIPBLAS_STATUS_SUCCESS;
+        };
+        if (!run()) continue;   // warm-up (and a check that the candidate runs)
+        bool good = hipEventRecord(e0, stream) == hipSuccess;
+        for (int r = 0; r < 3 && good; ++r) good = run();
+        good = good && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0.0f;
+        if (good && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && (best == 0.0f || ms < best)) {
+            best = ms;
+            p.algo = res[i].algo;
+        }
+    }
+    (void)hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    return true;
 }
 
 void free_plan(GemmPlan& p)
@@ -118,7 +155,7 @@ qad_status_t gemm_bf16(bool ta, bool tb, int64_t m, int64_t n, int64_t k, const 
         auto it = plans.find(key);
         if (it == plans.end()) {
             GemmPlan p;
-            if (!make_plan(h, key, p)) {
+            if (!make_plan(h, key, p, A, B, D, ws, stream)) {
                 free_plan(p);
                 return QAD_ERR_HIP;
             }
