@@ -34,6 +34,7 @@ __device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin
 __device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
 __device__ __forceinline__ void stnt32(void* p, int64_t i, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p) + i); }
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef short fp8x2_t __attribute__((ext_vector_type(2)));   // two FP8 codes in a 32-bit register half
 __device__ __forceinline__ void stnt64(void* p, int64_t i, uint32_t lo, uint32_t hi) { __builtin_nontemporal_store(v2u{lo, hi}, reinterpret_cast<v2u*>(p) + i); }
 
 // ---- agent-scope atomics used by the one-pass protocol ---------------------
@@ -261,22 +262,33 @@ __device__ __forceinline__ uint32_t quantize_unit(const float (&e)[8], uint32_t 
 // FP8 (E4M3) per-tensor QDQ of one unit of 8 elements ([Qwen] "3. QAD":
 // attention projections FP8 W8A8, KV cache FP8): code = sign | E4M3(|x|/s),
 // nearest even, saturating at 448; y = bf16(dec(code) * s).  Codes are the 8
-// bytes of the unit in element order.
-template <bool FAST>
+// bytes of the unit in element order.  The quotient is clamped to +-448 and
+// converted by gfx950's FP8 instructions with unit scale (nearest even on
+// every input up to 448 in magnitude, signs and subnormals included; beyond
+// 464 they give NaN, hence the clamp); decoding is the reverse instruction.
+// A frozen scale may lie far below an element, where x r overflows: frozen
+// elements are first clamped to +-1024 s (exact), which saturates the same.
+template <bool FAST, bool FROZEN>
 __device__ __forceinline__ void fp8_unit(const float (&e)[8], float s, float r, uint32_t (&code)[2], uint32_t (&yw)[4])
 {
-    uint32_t c[8];
-    float g[8];
+    float q[8];
+    const float lim = FROZEN && FAST ? 1024.0f * s : 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t mag = e4m3_encode(quotient_pos<FAST>(__builtin_fabsf(e[i]), s, r));
-        c[i] = mag | ((as_u(e[i]) >> 24) & 0x80u);
-        g[i] = __builtin_copysignf(e4m3_decode(mag) * s, e[i]);
+        const float x = FROZEN && FAST ? __builtin_amdgcn_fmed3f(e[i], -lim, lim) : e[i];
+        q[i] = __builtin_amdgcn_fmed3f(quotient<FAST>(x, s, r), -448.0f, 448.0f);
     }
-    code[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    code[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) yw[i >> 1] = pack_bf16x2(g[i], g[i + 1]);
+    for (int w = 0; w < 2; ++w) {
+        fp8x2_t lo = {0, 0};
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, q[4 * w], q[4 * w + 1], 1.0f, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, q[4 * w + 2], q[4 * w + 3], 1.0f, true);
+        code[w] = __builtin_bit_cast(uint32_t, lo);
+        const auto g01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code[w], 1.0f, false);
+        const auto g23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code[w], 1.0f, true);
+        yw[2 * w] = pack_bf16x2(g01[0] * s, g01[1] * s);
+        yw[2 * w + 1] = pack_bf16x2(g23[0] * s, g23[1] * s);
+    }
 }
 
 enum { MODE_FROZEN = 0, MODE_AMAX = 1, MODE_ONEPASS = 2 };
@@ -296,7 +308,7 @@ __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16
         unpack<BF16>(raw[k], e);
         if constexpr (FP8) {
             uint32_t code[2], yw[4];
-            fp8_unit<FAST>(e, s_g, rcp_g, code, yw);
+            fp8_unit<FAST, MODE == MODE_FROZEN>(e, s_g, rcp_g, code, yw);
             if (valid) {
                 if (a.y) stnt(a.y, ubase + u, v4u{yw[0], yw[1], yw[2], yw[3]});
                 if (a.codes) stnt64(a.codes, ubase + u, code[0], code[1]);

@@ -6,7 +6,14 @@
 //  * v_cvt_scalef32_pk_f32_fp4 with unit scale: the 16 signed grid values;
 //  * v_cvt_pk_bf16_f32: round to nearest even of the top 16 bits (NaNs
 //    skipped), i.e. (u + 0x7FFF + ((u >> 16) & 1)) >> 16.
-// Prints one line "fp4_mismatch bf16_mismatch decode_ok layout_word".
+//  * v_cvt_scalef32_pk_fp8_f32 with unit scale: OCP E4M3FN code of x =
+//    nearest magnitude of the format (ties to the even code), sign bit
+//    copied, on every input up to 448 in magnitude; inputs beyond are
+//    counted by what they give (the quantizer clamps its quotients to 448);
+//  * v_cvt_scalef32_pk_f32_fp8 with unit scale: every non-NaN code decodes
+//    to its value, in either half of the source word.
+// Prints one line "fp4_mismatch bf16_mismatch decode_ok layout_word
+// fp8_mismatch fp8_decode_ok fp8_layout_word".
 // Built by the package build step; run by tests/test_gpu_cvt_instructions.py.
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -26,6 +33,50 @@ __device__ unsigned ref_e2m1(float r)
     else if (a <= 5.0f) i = 6;
     else i = 7;
     return sign << 3 | i;
+}
+
+typedef short fp8x2_t __attribute__((ext_vector_type(2)));
+
+// E4M3FN magnitude of code c (0..126): 4 exponent bits (bias 7), 3 mantissa
+// bits, exponent 0 subnormal
+__device__ float e4m3_mag(unsigned c)
+{
+    const unsigned e = c >> 3, m = c & 7;
+    return e ? ldexpf(1.0f + m / 8.0f, (int)e - 7) : ldexpf((float)m, -9);
+}
+
+// nearest magnitude code, ties to the even code (the format's 127 values in
+// order; binary search for the largest one <= a)
+__device__ unsigned ref_e4m3(float a)
+{
+    unsigned lo = 0, hi = 126;
+    while (lo < hi) {
+        const unsigned mid = (lo + hi + 1) / 2;
+        if (e4m3_mag(mid) <= a) lo = mid; else hi = mid - 1;
+    }
+    if (lo == 126u) return 126u;
+    const float d0 = a - e4m3_mag(lo), d1 = e4m3_mag(lo + 1) - a;
+    if (d0 < d1) return lo;
+    if (d1 < d0) return lo + 1;
+    return (lo & 1u) ? lo + 1 : lo;
+}
+
+__global__ void check_fp8(unsigned long long* bad)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; // 2^24 threads x 256 inputs
+    unsigned n = 0;
+    for (unsigned k = 0; k < 256; ++k) {
+        const unsigned u = (unsigned)(t * 256 + k);
+        const float f = __uint_as_float(u), a = __builtin_fabsf(f);
+        if (!(a <= 448.0f)) continue;   // NaN, or beyond the range the quantizer feeds
+        fp8x2_t w = {0, 0};
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, f, -f, 1.0f, false);
+        const unsigned ww = __builtin_bit_cast(unsigned, w), want = ref_e4m3(a);
+        n += (ww & 0xFFu) != (((u >> 31) << 7) | want);
+        n += ((ww >> 8) & 0xFFu) != ((((u >> 31) ^ 1u) << 7) | want);
+        n += (ww >> 16) != 0u;
+    }
+    if (n) atomicAdd(bad + 2, (unsigned long long)n);
 }
 
 __global__ void check(unsigned long long* bad)
@@ -73,21 +124,37 @@ __global__ void decode_and_layout(unsigned* out)
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, 6.0f, -0.5f, 1.0f, 3);
     out[0] = ok;
     out[1] = w;
+    unsigned ok8 = 1;
+    for (unsigned c = 0; c < 256; ++c) {
+        if ((c & 0x7Fu) == 0x7Fu) continue;   // NaN codes
+        const float want = (c & 0x80u) ? -e4m3_mag(c & 0x7Fu) : e4m3_mag(c & 0x7Fu);
+        const unsigned lo = c | (c << 8), hi = lo << 16;
+        const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false);
+        const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true);
+        ok8 &= __float_as_uint(a[0]) == __float_as_uint(want) && __float_as_uint(a[1]) == __float_as_uint(want);
+        ok8 &= __float_as_uint(b[0]) == __float_as_uint(want) && __float_as_uint(b[1]) == __float_as_uint(want);
+    }
+    fp8x2_t v = {0, 0};
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, 1.0f, -2.0f, 1.0f, false);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, 448.0f, 0.001953125f, 1.0f, true);
+    out[2] = ok8;
+    out[3] = __builtin_bit_cast(unsigned, v);
 }
 
 int main()
 {
     unsigned long long* bad;
     unsigned* out;
-    if (hipMalloc(&bad, 16) != hipSuccess || hipMalloc(&out, 8) != hipSuccess) return 2;
-    if (hipMemset(bad, 0, 16) != hipSuccess) return 2;
+    if (hipMalloc(&bad, 24) != hipSuccess || hipMalloc(&out, 16) != hipSuccess) return 2;
+    if (hipMemset(bad, 0, 24) != hipSuccess) return 2;
     check<<<65536, 256>>>(bad);
+    check_fp8<<<65536, 256>>>(bad);
     decode_and_layout<<<1, 1>>>(out);
     if (hipDeviceSynchronize() != hipSuccess) return 3;
-    unsigned long long b[2];
-    unsigned o[2];
-    if (hipMemcpy(b, bad, 16, hipMemcpyDeviceToHost) != hipSuccess || hipMemcpy(o, out, 8, hipMemcpyDeviceToHost) != hipSuccess)
+    unsigned long long b[3];
+    unsigned o[4];
+    if (hipMemcpy(b, bad, 24, hipMemcpyDeviceToHost) != hipSuccess || hipMemcpy(o, out, 16, hipMemcpyDeviceToHost) != hipSuccess)
         return 3;
-    printf("%llu %llu %u 0x%08x\n", b[0], b[1], o[0], o[1]);
+    printf("%llu %llu %u 0x%08x %llu %u 0x%08x\n", b[0], b[1], o[0], o[1], b[2], o[2], o[3]);
     return 0;
 }

@@ -53,6 +53,18 @@ def test_fp8_small(dev, orc, shape, dtype):
     check_fp8(orc, x, "small")
 
 
+def test_fp8_frozen_quotient_overflow(dev, orc):
+    # a frozen scale far below the elements: x / s exceeds the binary32 range
+    # (the oracle's quotient is inf and saturates to +-448), with the
+    # reciprocal division (s = 2^-80) and IEEE division (s = 2^-81)
+    x = torch.randn((2, 8, 64), generator=torch.Generator().manual_seed(13)) * 1e30
+    x[:, :, ::5] = 3.0e38
+    x[:, :, 1::5] = -3.0e38
+    x[:, :, 2::5] = -0.0
+    x[:, 0, :] = 2.0 ** -75                      # ordinary quotients in the same tensor
+    check_fp8(orc, x.to(dev), "frozen overflow", tscale=[2.0 ** -80, 2.0 ** -81])
+
+
 def test_fp8_frozen_and_saturation(dev, orc):
     g = torch.Generator().manual_seed(8)
     x = (torch.randn((2, 16, 64), generator=g) * 100).to(torch.bfloat16).to(dev)
