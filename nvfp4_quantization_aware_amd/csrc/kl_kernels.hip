@@ -1032,11 +1032,12 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
     const uint32_t hi = 65535u - (uint32_t)tid * kSelKeysPerLane;
     const uint32_t whi = hi >> 1;
     auto word_at = [&](int b) { return whi - (uint32_t)((b + tid) & (kWordsPerLane - 1)); };
-    uint32_t local = 0;
+    uint32_t local = 0, nz = 0;   // nz: the lane's words holding any count
 #pragma unroll 8
     for (int b = 0; b < kWordsPerLane; ++b) {
         const uint32_t w = sh.c.hist[word_at(b)];
         local += (w & 0xFFFFu) + (w >> 16);
+        nz |= (w != 0u ? 1u : 0u) << b;
     }
     const uint32_t incl = block_incl_scan(local, sh.c.wave_tot);
     if (tid == kTopThreads - 1) sh.c.total = incl;
@@ -1063,9 +1064,8 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
         // the largest (smallest for top_p >= 1) key present
         const bool want_min = top_p >= 1.0f;
         uint32_t e = want_min ? 0xFFFFFFFFu : 0u;
-#pragma unroll 4
-        for (int b = 0; b < kWordsPerLane; ++b) {
-            const uint32_t wi = word_at(b), w = sh.c.hist[wi];
+        for (uint32_t m = nz; m; m &= m - 1u) {   // only the lane's nonzero words
+            const uint32_t wi = word_at(__builtin_ctz(m)), w = sh.c.hist[wi];
             if (w & 0xFFFFu) e = want_min ? min(e, 2u * wi) : umax(e, 2u * wi);
             if (w >> 16) e = want_min ? min(e, 2u * wi + 1u) : umax(e, 2u * wi + 1u);
         }
@@ -1085,9 +1085,8 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
             return fix40(exp2_hw(__builtin_fmaf(value_of_key<true>(key), c, -m))) * n;
         };
         unsigned long long lm = 0;
-#pragma unroll 2
-        for (int b = 0; b < kWordsPerLane; ++b) {
-            const uint32_t wi = word_at(b), w = sh.c.hist[wi];
+        for (uint32_t mk = nz; mk; mk &= mk - 1u) {   // only the lane's nonzero words
+            const uint32_t wi = word_at(__builtin_ctz(mk)), w = sh.c.hist[wi];
             lm += key_mass(2u * wi, w & 0xFFFFu) + key_mass(2u * wi + 1u, w >> 16);
         }
         const unsigned long long incl64 = block_incl_scan64(lm, sh.c.wave_tot64);
