@@ -530,10 +530,12 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, in
 //      scan over the bins picks the digit holding rank k;
 //   2. the online softmax state of the kept entries, teacher and student;
 //   3. the gradient (q~ - p~) grad_scale / T on kept entries, 0 elsewhere.
-// Rows of at most kMaxSegments record segments split the work: the threshold
-// kernel below finds the k-th largest teacher logit per row, then the
-// one-pass segment kernels run masked by it (TOPK).  Longer rows take
-// kl_topk_kernel, one workgroup per row that streams the row in every step.
+// Rows of at most kMaxSegments record segments split the work: a threshold
+// kernel finds the k-th largest teacher logit per row (kl_sel16_kernel from
+// exact key counts for bf16 teachers, kl_topk_tau_kernel by the radix rounds
+// for fp32 ones and for bf16 rows whose counts overflow), then the one-pass
+// segment kernels run masked by it (TOPK).  Longer rows take kl_topk_kernel,
+// one workgroup per row that streams the row in every step.
 // ---------------------------------------------------------------------------
 constexpr int kTopThreads = 1024;
 constexpr int kDigitBits = 12;
@@ -757,7 +759,8 @@ __device__ __forceinline__ float value_of_key(uint32_t key)
 // the k-th largest teacher logit of the row (the radix select above), the
 // teacher row streamed once per round.  (Holding a 128K-logit row in
 // registers allows one 1024-lane workgroup per CU and measured slower than
-// two streaming ones, whose loads and LDS histograms overlap.)
+// two streaming ones, whose loads and LDS histograms overlap.)  REDO: only
+// the rows kl_sel16_kernel left NaN (their key counts overflowed).
 template <bool BF16, bool REDO = false>
 __global__ __launch_bounds__(kTopThreads) void kl_topk_tau_kernel(const void* teacher, int64_t vocab, uint32_t k,
                                                                   float* tau_out)
@@ -941,6 +944,7 @@ __device__ uint32_t nucleus_key(float top_p, float c, float m, ForT for_t, TopPS
     return prefix;
 }
 
+// REDO: only the rows kl_sel16_kernel left NaN (their key counts overflowed)
 template <bool BF16, bool REDO = false>
 __global__ __launch_bounds__(kTopThreads) void kl_topp_tau_kernel(const void* teacher, int64_t vocab, float top_p,
                                                                   float c, float* tau_out)

@@ -83,6 +83,19 @@ def test_topk_many_ties(dev, orc, in_dt):
     run_and_check(dev, orc, t, s, 512, 1.0, torch.float32, "ties")
 
 
+@pytest.mark.parametrize("k", [50, 4096, 90000])
+def test_topk_count_overflow_rows(dev, orc, k):
+    # more than 65535 equal bf16 teacher logits in a row: the one-read key
+    # counts overflow and those rows are redone by the radix rounds; k lands
+    # above, inside and below the tied group
+    rng = np.random.default_rng(k)
+    t = torch.from_numpy(rng.normal(0, 3, (3, 131072))).to(torch.bfloat16)
+    t[0, rng.choice(131072, 70000, replace=False)] = 0.5
+    t[2, rng.choice(131072, 100000, replace=False)] = -1.25
+    s = (t.double() + torch.from_numpy(rng.normal(0, 0.5, (3, 131072)))).to(torch.bfloat16)
+    run_and_check(dev, orc, t, s, k, 1.0, torch.float32, "count overflow")
+
+
 def test_topk_signed_zero_ties(dev, orc):
     # -0 and +0 are equal teacher logits: both are kept when zero is the k-th value
     t = torch.zeros(2, 64, dtype=torch.float32)

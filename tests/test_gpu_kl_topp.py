@@ -121,6 +121,18 @@ def test_topp_many_ties(dev, orc, in_dt):
         run_and_check(dev, orc, t, s, p, 1.0, torch.float32, "ties")
 
 
+@pytest.mark.parametrize("top_p", [0.2, 0.9, 1.0])
+def test_topp_count_overflow_rows(dev, orc, top_p):
+    # more than 65535 equal bf16 teacher logits in a row: the one-read key
+    # counts overflow and those rows are redone by the radix rounds
+    rng = np.random.default_rng(int(top_p * 10))
+    t = torch.from_numpy(rng.normal(0, 3, (3, 131072))).to(torch.bfloat16)
+    t[0, rng.choice(131072, 70000, replace=False)] = 0.5
+    t[2, rng.choice(131072, 100000, replace=False)] = 9.0
+    s = (t.double() + torch.from_numpy(rng.normal(0, 0.5, (3, 131072)))).to(torch.bfloat16)
+    run_and_check(dev, orc, t, s, top_p, 1.0, torch.float32, "count overflow")
+
+
 def test_topp_signed_zero_group(dev, orc):
     # -0 and +0 are one teacher value: kept together when zero is the boundary
     t = torch.full((2, 64), -30.0, dtype=torch.float32)
