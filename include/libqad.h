@@ -215,10 +215,15 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  * W4A4 NVFP4 model, weights and activations both NVFP4; [Lightning]
  * "QAD的工作原理": simulated quantization in every student forward).
  *   forward : y[M][N] = QDQ(x)[M][K] * QDQ(w)[N][K]^T, where QDQ is
- *             nvfp4_qdq_fwd with dynamic scales (one tensor scale for x, one
- *             for w; blocks of 16 along K); bf16 product of the bf16 QDQ
- *             values with fp32 accumulation (MFMA, hipBLASLt)
+ *             nvfp4_qdq_fwd (blocks of 16 along K): dynamic scales for x;
+ *             for w dynamic scales too, or the frozen ones given
+ *             ([Lightning] "量化尺度处理策略": frozen-scale QAD keeps the
+ *             MSE-calibrated weight scales fixed while the weights train);
+ *             bf16 product of the bf16 QDQ values with fp32 accumulation
+ *             (MFMA, hipBLASLt)
  *   x, w    : device, dtype dt, row-major, 16-byte aligned; K > 0, K % 16 == 0
+ *   w_scales_in, w_tscale_in : device u8 [N][K/16] and float[1], frozen
+ *             scales of w (as from nvfp4_mse_calibrate), or both NULL
  *   y       : device bf16 [M][N]; xq, wq: device bf16 [M][K], [N][K]
  *             receive QDQ(x), QDQ(w) (kept for the backward); no output may
  *             overlap another or an input
@@ -226,7 +231,8 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  * The library keeps one hipBLASLt handle per device, created on first use;
  * hipBLASLt's scratch comes from the workspace. */
 qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, int64_t M, int64_t N, int64_t K,
-                                 void* y, void* xq, void* wq, void* workspace, size_t ws_bytes, qad_stream_t stream);
+                                 const uint8_t* w_scales_in, const float* w_tscale_in, void* y, void* xq, void* wq,
+                                 void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* Backward of qad_w4a4_linear_fwd with the straight-through estimator through
  * both quantizers: grad_x[M][K] = grad_y[M][N] * wq[N][K] and

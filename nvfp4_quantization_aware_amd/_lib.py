@@ -35,7 +35,7 @@ SIGNATURES = {
     "nvfp4_qdq_bwd_clipped": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
-    "qad_w4a4_linear_fwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qad_w4a4_linear_fwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qad_w4a4_linear_bwd": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fp8_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_topk_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz,
@@ -258,8 +258,11 @@ def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=T
     return cd, tscale_out, yy
 
 
-def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=None, ws: torch.Tensor | None = None):
-    """y = QDQ(x) QDQ(w)^T (bf16) for x [M, K], w [N, K].  Returns (y, xq, wq)."""
+def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=None, ws: torch.Tensor | None = None,
+                        w_scales_in: torch.Tensor | None = None, w_tscale_in: torch.Tensor | None = None):
+    """y = QDQ(x) QDQ(w)^T (bf16) for x [M, K], w [N, K]; w's scales are
+    dynamic, or the frozen w_scales_in (u8 [N, K/16]) / w_tscale_in (f32 [1]).
+    Returns (y, xq, wq)."""
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1] or x.dtype != w.dtype:
         raise ValueError("x [M, K] and w [N, K] of one dtype")
     (M, K), N = x.shape, w.shape[0]
@@ -269,8 +272,13 @@ def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=No
     wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if wq is None else wq
     if ws is None:
         ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
-    _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(y), _p(xq), _p(wq), _p(ws), ws.numel(),
-                                     _stream(dev)), "qad_w4a4_linear_fwd")
+    if (w_scales_in is None) != (w_tscale_in is None):
+        raise ValueError("frozen weight scales need both w_scales_in and w_tscale_in")
+    if w_scales_in is not None and (w_scales_in.dtype != torch.uint8 or w_scales_in.numel() != N * (K // 16)
+                                    or w_tscale_in.dtype != torch.float32 or w_tscale_in.numel() != 1):
+        raise ValueError("w_scales_in must be uint8 [N, K/16] and w_tscale_in float32 [1]")
+    _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(w_scales_in), _p(w_tscale_in), _p(y), _p(xq),
+                                     _p(wq), _p(ws), ws.numel(), _stream(dev)), "qad_w4a4_linear_fwd")
     return y, xq, wq
 
 

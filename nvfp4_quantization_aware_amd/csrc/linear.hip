@@ -196,11 +196,12 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 extern "C" {
 
 qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, int64_t M, int64_t N, int64_t K,
-                                 void* y, void* xq, void* wq, void* workspace, size_t ws_bytes, qad_stream_t stream)
+                                 const uint8_t* w_scales_in, const float* w_tscale_in, void* y, void* xq, void* wq,
+                                 void* workspace, size_t ws_bytes, qad_stream_t stream)
 {
     if (dt != QAD_BF16 && dt != QAD_F32) return QAD_ERR_DTYPE;
     if (!dims_ok(M, N, K) || K <= 0 || K % 16 != 0) return QAD_ERR_SHAPE;
-    if (!y || !xq || !wq) return QAD_ERR_INVALID_ARG;
+    if (!y || !xq || !wq || (w_scales_in == nullptr) != (w_tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return QAD_OK;
     if (!x || !w) return QAD_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(xq) || !aligned16(wq)) return QAD_ERR_ALIGNMENT;
@@ -214,7 +215,7 @@ qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, i
     const size_t rec = qad::linear_workspace_bytes(M, N, K) - kGemmWorkspace;
     qad_status_t st = nvfp4_qdq_fwd(x, dt, 1, M, K, nullptr, nullptr, xq, workspace, rec, stream);
     if (st != QAD_OK) return st;
-    st = nvfp4_qdq_fwd(w, dt, 1, N, K, nullptr, nullptr, wq, workspace, rec, stream);
+    st = nvfp4_qdq_fwd(w, dt, 1, N, K, w_scales_in, w_tscale_in, wq, workspace, rec, stream);
     if (st != QAD_OK) return st;
     // row-major y[M][N] = xq[M][K] wq[N][K]^T is the column-major N x M
     // product wq^T (K x N stored, transposed) times xq (K x M stored)

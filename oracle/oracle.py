@@ -251,12 +251,13 @@ def nvfp4_qdq_bwd_clipped(grad_y: np.ndarray, x: np.ndarray, scales: np.ndarray,
     return out, int(nc[0])
 
 
-def w4a4_linear_fwd(x: np.ndarray, w: np.ndarray):
+def w4a4_linear_fwd(x: np.ndarray, w: np.ndarray, w_scales: np.ndarray | None = None,
+                    w_tscale: float | None = None):
     """W4A4 fake-quant linear: y = QDQ(x) QDQ(w)^T in binary64 (numpy matmul of
-    the oracle's NVFP4 QDQ outputs).  Returns (y f64 [M][N], xq bf16 bits,
-    wq bf16 bits)."""
+    the oracle's NVFP4 QDQ outputs; w with frozen scales when given).
+    Returns (y f64 [M][N], xq bf16 bits, wq bf16 bits)."""
     _, _, _, xq = nvfp4_quantize(x)
-    _, _, _, wq = nvfp4_quantize(w)
+    _, _, _, wq = nvfp4_quantize(w, w_scales, w_tscale)
     xf = (xq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     wf = (wq.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return xf @ wf.T, xq, wq

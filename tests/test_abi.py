@@ -134,11 +134,12 @@ def test_w4a4_linear_rejects(L):
     ws = L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, 64, 32, 128)
     assert ws >= 64 << 20 and ws % 256 == 0
     a = lambda **kw: [kw.get("x", P), kw.get("w", P * 2), kw.get("dt", 1), kw.get("M", 64), kw.get("N", 32),
-                      kw.get("K", 128), kw.get("y", P * 3), kw.get("xq", P * 4), kw.get("wq", P * 5),
-                      kw.get("ws", P * 6), kw.get("wsb", ws), None]
+                      kw.get("K", 128), kw.get("wsc", None), kw.get("wts", None), kw.get("y", P * 3),
+                      kw.get("xq", P * 4), kw.get("wq", P * 5), kw.get("ws", P * 6), kw.get("wsb", ws), None]
     assert fw(*a(dt=5)) == DTYPE
     assert fw(*a(K=24)) == SHAPE and fw(*a(K=0)) == SHAPE and fw(*a(M=-1)) == SHAPE
     assert fw(*a(y=None)) == INVALID and fw(*a(x=None)) == INVALID
+    assert fw(*a(wsc=P * 7)) == INVALID and fw(*a(wts=P * 8)) == INVALID   # frozen weight scales come in pairs
     assert fw(*a(xq=P * 4 + 8)) == ALIGN
     assert fw(*a(wsb=ws - 256)) == WS and fw(*a(ws=None)) == WS
     assert fw(*a(ws=P * 6 + 128)) == ALIGN

@@ -1,7 +1,7 @@
 """GPU parity of the W4A4 fake-quant linear layer (qad_w4a4_linear_fwd/_bwd).
 
 The quantized operands xq, wq must equal the oracle's NVFP4 QDQ outputs bit
-for bit.  The products are bf16 values of fp32-accumulated sums, compared with
+for bit (dynamic scales, or for w frozen MSE-calibrated scales).  The products are bf16 values of fp32-accumulated sums, compared with
 the binary64 oracle product within the bound that arithmetic allows: half a
 bf16 ulp of the result plus 2 K 2^-24 sum_k |a_k b_k| (fp32 rounding of up to
 K products and partial sums in any order).
@@ -33,16 +33,24 @@ def assert_product_close(got_bits, ref, absprod, K, label):
     assert not bad.any(), (label, np.argwhere(bad)[:3], (np.abs(got - ref) - bound).max())
 
 
-def run_case(dev, orc, M, N, K, dtype, seed):
+def run_case(dev, orc, M, N, K, dtype, seed, frozen=False):
     g = torch.Generator().manual_seed(seed)
     x = (torch.randn((M, K), generator=g) * 2).to(dtype)
     w = (torch.randn((N, K), generator=g) * 0.05).to(dtype)
     gy = (torch.randn((M, N), generator=g) * 1e-3).to(torch.bfloat16)
-    announce("qad_w4a4_linear_fwd/bwd M=%d N=%d K=%d %s" % (M, N, K, dtype))
-    y, xq, wq = q.qad_w4a4_linear_fwd(x.to(dev), w.to(dev))
+    ws_in = wt_in = None
+    if frozen:   # the oracle's MSE-calibrated weight scales, frozen
+        sc, ts = orc.mse_calibrate(host(w))
+        ws_in, wt_in = sc, ts
+    announce("qad_w4a4_linear_fwd/bwd M=%d N=%d K=%d %s frozen=%s" % (M, N, K, dtype, frozen))
+    if frozen:
+        y, xq, wq = q.qad_w4a4_linear_fwd(x.to(dev), w.to(dev), w_scales_in=torch.from_numpy(sc).to(dev),
+                                          w_tscale_in=torch.tensor([ts], dtype=torch.float32, device=dev))
+    else:
+        y, xq, wq = q.qad_w4a4_linear_fwd(x.to(dev), w.to(dev))
     gx, gw = q.qad_w4a4_linear_bwd(gy.to(dev), xq, wq)
     torch.cuda.synchronize()
-    yr, xqr, wqr = orc.w4a4_linear_fwd(host(x), host(w))
+    yr, xqr, wqr = orc.w4a4_linear_fwd(host(x), host(w), ws_in, wt_in)
     assert np.array_equal(host(xq), xqr) and np.array_equal(host(wq), wqr)
     xf, wf, gf = f64(xqr), f64(wqr), f64(host(gy))
     assert_product_close(host(y), yr, np.abs(xf) @ np.abs(wf).T, K, "y")
@@ -55,6 +63,11 @@ def run_case(dev, orc, M, N, K, dtype, seed):
                                          (256, 512, 1024, torch.bfloat16), (1, 1, 16, torch.bfloat16)])
 def test_linear_small(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=M + N + K)
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(64, 32, 128, torch.bfloat16), (40, 24, 256, torch.float32)])
+def test_linear_frozen_weight_scales(dev, orc, M, N, K, dtype):
+    run_case(dev, orc, M, N, K, dtype, seed=7 * M + N, frozen=True)
 
 
 def test_linear_expert_shape_sampled(dev, orc):

@@ -53,3 +53,18 @@ def test_backward_is_the_transposed_products(orc):
     for (j, k) in [(0, 0), (4, 9)]:
         e = np.zeros_like(wf); e[j, k] = h
         assert abs((loss(xf, wf + e) - loss(xf, wf - e)) / (2 * h) - gw[j, k]) < 1e-9
+
+
+def test_frozen_weight_scales_compose(orc):
+    # with frozen weight scales the weight operand is exactly the frozen QDQ
+    # of w (which the NVFP4 pins cover) and the product changes accordingly
+    x = synth.bf16_bits(synth.gaussian_weight_bf16(6, 64, seed=4))
+    w = synth.bf16_bits(synth.gaussian_weight_bf16(5, 64, seed=5))
+    sc, ts = orc.mse_calibrate(w)
+    y, xq, wq = orc.w4a4_linear_fwd(x, w, sc, ts)
+    assert np.array_equal(wq, orc.nvfp4_quantize(w, sc, ts)[3])
+    assert np.array_equal(xq, orc.nvfp4_quantize(x)[3])
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(y, f(xq) @ f(wq).T)
+    yd, _, wqd = orc.w4a4_linear_fwd(x, w)
+    assert not np.array_equal(wqd, wq)   # the calibrated scales differ from the dynamic ones here
