@@ -35,6 +35,15 @@ int64_t tensor_elems(int64_t B, int64_t R, int64_t C)
 
 qad_status_t hip_status(hipError_t e) { return e == hipSuccess ? QAD_OK : QAD_ERR_HIP; }
 
+// the per-tensor kernels launch B times the chunks of one tensor (the fp32
+// chunks, the most numerous) workgroups in one grid; beyond 2^31 - 1 that
+// grid cannot be expressed, so such a batch is a shape error
+bool batch_grid_ok(int64_t B, int64_t rc)
+{
+    const int64_t P = qad::quantize_chunks(false, rc);
+    return B <= 0 || P <= 0 || B <= (int64_t)0x7FFFFFFF / P;
+}
+
 uint32_t* ws_words(void* workspace) { return static_cast<uint32_t*>(workspace); }
 
 // workspace of the tensor records for B tensors of rc elements (sized for
@@ -60,7 +69,7 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
 {
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
-    if (n < 0 || C % (fp8 ? 8 : 16) != 0) return QAD_ERR_SHAPE;
+    if (n < 0 || C % (fp8 ? 8 : 16) != 0 || !batch_grid_ok(B, R * C)) return QAD_ERR_SHAPE;
     if (!codes && !scales_out && !tscale_out && !y) return QAD_ERR_INVALID_ARG;
     if (!fp8 && (scales_in == nullptr) != (tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
     if (n == 0) return QAD_OK;
@@ -142,7 +151,7 @@ qad_status_t nvfp4_amax(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int
 {
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
-    if (n < 0 || (C * esize(xt)) % 16 != 0) return QAD_ERR_SHAPE;
+    if (n < 0 || (C * esize(xt)) % 16 != 0 || !batch_grid_ok(B, R * C)) return QAD_ERR_SHAPE;
     if (B == 0) return QAD_OK;
     if (!amax_out) return QAD_ERR_INVALID_ARG;
     if (n > 0 && !x) return QAD_ERR_INVALID_ARG;
@@ -232,7 +241,7 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
 {
     if (!valid_dtype(wt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
-    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (n < 0 || C % 16 != 0 || !batch_grid_ok(B, R * C)) return QAD_ERR_SHAPE;
     if (n_candidates < 1 || !(k_min > 0.0f) || !(k_max >= k_min) || !isfinite(k_max)) return QAD_ERR_INVALID_ARG;
     // consecutive candidates must not be able to skip an E4M3 value (relative
     // step at most 1/16, below the narrowest E4M3 rounding interval, 1/15)

@@ -116,6 +116,16 @@ def test_quantize_rejects(L):
     assert f(P, 1, 0, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == OK
 
 
+def test_batches_beyond_one_grid_rejected(L):
+    # 2^31 tensors of 16 elements: 2^35 elements (allowed) but one workgroup
+    # per tensor already exceeds a grid's 2^31 - 1 workgroups
+    B = 1 << 31
+    assert L.nvfp4_quantize(P, 1, B, 1, 16, None, None, None, None, None, P * 2, P * 3, 1 << 40, None) == SHAPE
+    assert L.nvfp4_amax(P, 1, B, 1, 16, P * 2, P * 3, 1 << 40, None) == SHAPE
+    assert L.nvfp4_mse_calibrate(P, 1, B, 1, 16, 64, 0.5, 1.0, P * 2, P * 3, P * 4, 1 << 40, None) == SHAPE
+    assert L.fp8_quantize(P, 1, B, 1, 16, None, None, None, P * 2, P * 3, 1 << 40, None) == SHAPE
+
+
 def test_fp8_quantize_rejects(L):
     f = L.fp8_quantize
     ws = 1 << 16
