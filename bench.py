@@ -134,6 +134,19 @@ def measured_traffic(kernel: str):
     return rec["traffic_bytes"]
 
 
+def _host_cpu():
+    """CPU model and logical CPU count of the host the oracle ran on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(fraction: float):
     """The CPU oracle (single-threaded C) on `fraction` of one step: the same
     share of every part, so its GB/s compares directly with the GPU step."""
@@ -187,6 +200,7 @@ def cpu_baseline(fraction: float):
         "value": round(nbytes / secs / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "host": _host_cpu(),
         "kind": "oracle",
         "seconds": round(secs, 2),
         "part_seconds": {k: round(v[0], 3) for k, v in parts.items()},
@@ -402,6 +416,9 @@ def main():
             "parallelism": "single GPU",
         },
         "frac_hbm_step": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        # the same ratio against what a plain copy reaches on this machine (the
+        # straight-through copy of the 2 GiB MoE gradient in the same steps)
+        "frac_of_measured_copy": round(total_bytes / (ms_step * 1e-3) / 1e9 / parts["moe_ste_bwd"]["GB/s"], 4),
         "nvfp4_qdq_GBps": round(qdq_bytes / (qdq_ms * 1e-3) / 1e9, 1),
         "kl_tokens_per_s": round(kl_tokens_s, 1),
         "parts": parts,
