@@ -7,7 +7,10 @@ Tolerances (the oracle is binary64; the kernels accumulate in fp32):
     leaves an absolute floor of a few 1e-7 nats on rows whose KL is near 0;
   * fp32 gradient: per row, max and L2 error <= 1e-5 of the row's max / L2
     norm of the reference;
-  * bf16 gradient: the bf16 rounding of a value inside that fp32 band.
+  * bf16 gradient: the bf16 rounding of a value inside that fp32 band;
+  * on near one-hot rows (low T, wide logits) the gradient q - p is far
+    below the probabilities it is the difference of; there the band is
+    1e-6 of max(p + q) (and of its L2), the fp32 floor of that difference.
 Full-size logits (8192 x 131072) are checked on sampled rows; the mean over
 all rows is checked against the per-row losses the kernel wrote.
 """
@@ -17,7 +20,7 @@ import torch
 
 import nvfp4_quantization_aware_amd as q
 from nvfp4_quantization_aware_amd import synth
-from gpu_util import announce, assert_kl_grad_close, gpu_device, host
+from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +75,21 @@ def test_kl_many_rounds(dev, orc, g_dt):
     _check_rows(rows, ref_rows)
     if g_dt is not None:
         assert_kl_grad_close(g, ref_g)
+
+
+@pytest.mark.parametrize("T,std,vocab", [(0.5, 8.0, 131072), (0.25, 8.0, 16384), (0.5, 5.0, 23744)])
+@pytest.mark.parametrize("g_dt", [torch.float32, torch.bfloat16])
+def test_kl_near_one_hot_rows(dev, orc, T, std, vocab, g_dt):
+    # low temperature and wide logits: both distributions nearly one-hot at
+    # the same entry, so the gradient q - p is many orders of magnitude below
+    # the probabilities; fp32 then reaches the fp32 floor of the difference
+    # (1e-6 of the probabilities), not 1e-5 of the tiny gradient itself
+    t, s = synth.logits_bf16(tokens=16, vocab=vocab, teacher_std=std, seed=int(100 * T + std))
+    loss, rows, g = run_kl(dev, t, s, T, g_dt, "near one-hot")
+    ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
+    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
+    _check_rows(rows, ref_rows)
+    assert_kl_grad_close(g, ref_g, floor=prob_scale(host(t), host(s), T, 1.0 / 16))
 
 
 def test_kl_forward_only_matches(dev):

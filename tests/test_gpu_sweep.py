@@ -1,0 +1,139 @@
+"""Seeded random sweeps of the main entry points against the oracle: shapes,
+dtypes, scale modes, value ranges and temperatures drawn from a fixed
+generator, each case checked by the same rules as the focused tests (codes,
+scales, tensor scales and QDQ outputs bit for bit; KL within the 1e-5 rules).
+They look for edge cases the hand-picked shapes miss: ragged tails at every
+offset, vocabularies on both sides of segment boundaries, tensor scales from
+2^-100 to 2^100 (both division paths), sparse tensors, exact ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantization_aware_amd as q
+from nvfp4_quantization_aware_amd import synth
+from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_device()
+
+
+def random_tensor(rng, shape, dtype):
+    """float32 values of a randomly chosen character, then cast to dtype"""
+    kind = rng.integers(0, 5)
+    scale = float(2.0 ** rng.uniform(-100, 100))
+    if kind == 0:
+        x = rng.standard_normal(shape) * scale
+    elif kind == 1:
+        x = rng.standard_t(3, size=shape) * scale
+    elif kind == 2:   # sparse: mostly exact zeros (and some -0)
+        x = rng.standard_normal(shape) * scale * (rng.random(shape) < 0.05)
+        x[rng.random(shape) < 0.01] = -0.0
+    elif kind == 3:   # E2M1 grid points and midpoints times one scale
+        grid = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6])
+        x = rng.choice(grid, size=shape) * np.where(rng.random(shape) < 0.5, -1, 1) * scale
+    else:             # heavy outliers
+        x = rng.standard_normal(shape) * scale
+        x[rng.random(shape) < 0.002] *= 1e3
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_nvfp4_quantize_sweep(dev, orc, case):
+    rng = np.random.default_rng(1000 + case)
+    dtype = ["bf16", "fp32"][case % 2]
+    B, R, C = int(rng.integers(1, 5)), int(rng.integers(1, 300)), 16 * int(rng.integers(1, 300))
+    x = random_tensor(rng, (B, R, C), dtype)
+    frozen = case % 3 == 2
+    announce("nvfp4 sweep case %d %s B=%d R=%d C=%d frozen=%s" % (case, dtype, B, R, C, frozen))
+    xh = host(x)
+    if frozen:
+        sc = rng.integers(0, 127, (B, R, C // 16)).astype(np.uint8)
+        ts = (2.0 ** rng.uniform(-90, 60, B)).astype(np.float32)
+        codes, scales, tsd, y = q.nvfp4_quantize(x.to(dev), torch.from_numpy(sc).to(dev), torch.from_numpy(ts).to(dev))
+    else:
+        codes, scales, tsd, y = q.nvfp4_quantize(x.to(dev))
+    torch.cuda.synchronize()
+    cg, sg, tg, yg = host(codes), host(scales), host(tsd), host(y)
+    for b in range(B):
+        if frozen:
+            rc, rs, rt, ry = orc.nvfp4_quantize(xh[b], sc[b], float(ts[b]))
+        else:
+            rc, rs, rt, ry = orc.nvfp4_quantize(xh[b])
+        assert tg[b].view(np.uint32) == np.float32(rt).view(np.uint32), (case, b)
+        assert np.array_equal(sg[b].reshape(rs.shape), rs), (case, b, "scales")
+        assert np.array_equal(cg[b].reshape(rc.shape), rc), (case, b, "codes")
+        assert np.array_equal(yg[b].reshape(ry.shape), ry), (case, b, "y")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fp8_quantize_sweep(dev, orc, case):
+    rng = np.random.default_rng(2000 + case)
+    dtype = ["bf16", "fp32"][case % 2]
+    B, R, C = int(rng.integers(1, 4)), int(rng.integers(1, 200)), 8 * int(rng.integers(1, 400))
+    x = random_tensor(rng, (B, R, C), dtype)
+    frozen = case % 4 == 3
+    ts = (2.0 ** rng.uniform(-90, 60, B)).astype(np.float32) if frozen else None
+    announce("fp8 sweep case %d %s B=%d R=%d C=%d frozen=%s" % (case, dtype, B, R, C, frozen))
+    codes, tsd, y = q.fp8_quantize(x.to(dev), None if ts is None else torch.from_numpy(ts).to(dev))
+    torch.cuda.synchronize()
+    xh, cg, tg, yg = host(x), host(codes), host(tsd), host(y)
+    for b in range(B):
+        rc, rt, ry = orc.fp8_quantize(xh[b], None if ts is None else float(ts[b]))
+        assert tg[b].view(np.uint32) == np.float32(rt).view(np.uint32), (case, b)
+        assert np.array_equal(cg[b], rc), (case, b, "codes")
+        assert np.array_equal(yg[b], ry), (case, b, "y")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_kl_sweep(dev, orc, case):
+    rng = np.random.default_rng(3000 + case)
+    tokens = int(rng.integers(1, 24))
+    if case % 3 == 0:     # on and around a segment boundary (16384 logits)
+        vocab = 16384 * int(rng.integers(1, 9)) + 8 * int(rng.integers(-1, 2))
+    else:
+        vocab = 8 * int(rng.integers(1, 20000))
+    vocab = max(vocab, 8)
+    T = float(rng.choice([0.5, 1.0, 2.0]))
+    in_dt = [torch.bfloat16, torch.float32][case % 2]
+    g_dt = [torch.bfloat16, torch.float32][(case // 2) % 2]
+    std = float(rng.uniform(0.5, 8.0))
+    t, s = synth.logits_bf16(tokens=tokens, vocab=vocab, teacher_std=std, seed=3000 + case)
+    t, s = t.to(in_dt), s.to(in_dt)
+    announce("kl sweep case %d tokens=%d vocab=%d T=%g in=%s grad=%s" % (case, tokens, vocab, T, in_dt, g_dt))
+    loss, rows, g = q.qad_kl_fwd_bwd(t.to(dev), s.to(dev), temperature=T, grad_dtype=g_dt, row_loss=True)
+    torch.cuda.synchronize()
+    ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
+    assert abs(float(host(loss)[0]) - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-7, case
+    rr = host(rows).astype(np.float64)
+    assert np.all(np.abs(rr - ref_rows) <= 1e-5 * np.abs(ref_rows) + 1e-6), case
+    # near one-hot rows (low T, wide logits) make the gradient a small
+    # difference of O(1) probabilities: the fp32 floor applies there
+    assert_kl_grad_close(host(g), ref_g, floor=prob_scale(host(t), host(s), T, 1.0 / tokens))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_clipped_ste_sweep(dev, orc, case):
+    rng = np.random.default_rng(4000 + case)
+    xt, gt = ["bf16", "fp32"][case % 2], ["bf16", "fp32"][(case // 2) % 2]
+    B, R, C = int(rng.integers(1, 4)), int(rng.integers(1, 200)), 16 * int(rng.integers(1, 300))
+    x = random_tensor(rng, (B, R, C), xt)
+    gy = random_tensor(rng, (B, R, C), gt)
+    xh = host(x)
+    sc = np.empty((B, R, C // 16), np.uint8)
+    ts = np.empty(B, np.float32)
+    for b in range(B):   # the oracle's own dynamic forward scales
+        _, s_b, t_b, _ = orc.nvfp4_quantize(xh[b])
+        sc[b], ts[b] = s_b.reshape(R, C // 16), t_b
+    announce("clipped STE sweep case %d x=%s g=%s B=%d R=%d C=%d" % (case, xt, gt, B, R, C))
+    gx = q.nvfp4_qdq_bwd_clipped(gy.to(dev), x.to(dev), torch.from_numpy(sc).to(dev), torch.from_numpy(ts).to(dev))
+    torch.cuda.synchronize()
+    gh, gyh = host(gx), host(gy)
+    for b in range(B):
+        ref, _ = orc.nvfp4_qdq_bwd_clipped(gyh[b].ravel(), xh[b].ravel(), sc[b].ravel(), float(ts[b]))
+        assert np.array_equal(gh[b].ravel(), ref), (case, b)
