@@ -40,13 +40,17 @@ def bf16_ulp(a: np.ndarray) -> np.ndarray:
     return np.maximum(2.0 ** (e - 7), 2.0**-133)
 
 
-def prob_scale(t_bits: np.ndarray, s_bits: np.ndarray, T: float, grad_scale: float):
+def prob_scale(t_bits: np.ndarray, s_bits: np.ndarray, T: float, grad_scale: float, kept=None):
     """Per row, the size of the probabilities whose difference the gradient
     is: max_v and L2 over v of (p_v + q_v) grad_scale / T, in binary64 from the
-    inputs (bf16 bits or float32)."""
+    inputs (bf16 bits or float32).  `kept` (bool, the shape of the inputs):
+    the probabilities renormalized over the kept entries of each row, as the
+    top-k and top-p losses take them."""
     f = lambda a: ((a.astype(np.uint32) << 16).view(np.float32) if a.dtype == np.uint16 else a).astype(np.float64)
     def softmax(x):
         x = x / T
+        if kept is not None:
+            x = np.where(kept, x, -np.inf)
         e = np.exp(x - x.max(axis=-1, keepdims=True))
         return e / e.sum(axis=-1, keepdims=True)
     ps = (softmax(f(t_bits)) + softmax(f(s_bits))) * grad_scale / T

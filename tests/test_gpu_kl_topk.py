@@ -6,8 +6,10 @@ is exactly 0 elsewhere.  Tolerances as for the full-vocabulary KL: mean loss
 1e-5 relative, per-row loss 1e-5 relative + 1e-6 absolute, gradient per row
 within 1e-5 of the row's largest reference magnitude (plus half a bf16 ulp
 for a bf16 gradient; where a row's reference gradient is 0 everywhere, as
-with a single kept entry, grad_scale / T stands in for that magnitude).  The
-kept set itself is compared exactly: the gradient must be 0 at every entry
+with a single kept entry, grad_scale / T stands in for that magnitude; where
+the kept set is near one-hot the tolerance is floored at 1e-6 of the largest
+renormalised (p + q) grad_scale / T, the binary32 limit of q - p).  The kept
+set itself is compared exactly: the gradient must be 0 at every entry
 outside it.
 """
 import numpy as np
@@ -16,7 +18,7 @@ import torch
 
 import nvfp4_quantization_aware_amd as q
 from nvfp4_quantization_aware_amd import synth
-from gpu_util import announce, assert_kl_grad_close, gpu_device, host
+from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +56,8 @@ def run_and_check(dev, orc, t, s, k, T, g_dt, label, grad_scale=None):
         assert np.array_equal(kept.sum(axis=1), cnt)
         assert np.all(gh[~kept] == 0), "gradient outside the kept set"
         gs = grad_scale if grad_scale is not None else 1.0 / t.shape[0]
-        assert_kl_grad_close(gh, ref_g, zero_row_scale=gs / T)
+        # near one-hot kept sets: the fp32 floor of a difference of probabilities
+        assert_kl_grad_close(gh, ref_g, zero_row_scale=gs / T, floor=prob_scale(th, sh, T, gs, kept))
     return loss
 
 
@@ -94,6 +97,23 @@ def test_topk_count_overflow_rows(dev, orc, k):
     t[2, rng.choice(131072, 100000, replace=False)] = -1.25
     s = (t.double() + torch.from_numpy(rng.normal(0, 0.5, (3, 131072)))).to(torch.bfloat16)
     run_and_check(dev, orc, t, s, k, 1.0, torch.float32, "count overflow")
+
+
+@pytest.mark.parametrize("k", [1, 100, 700])
+def test_topk_rows_of_changing_scale(dev, orc, k):
+    # one workgroup takes every (CU count)-th row and counts only the keys at
+    # or above a bound taken from its previous row; blocks of rows with other
+    # offsets and spreads put the k-th key below that bound (the row is
+    # redone by the radix rounds), far above it, or between k and 4k keys
+    # past it
+    rng = np.random.default_rng(40 + k)
+    rows, vocab = 1100, 2048
+    shift = rng.choice([-60.0, -2.0, 0.0, 3.0, 60.0], size=(rows + 63) // 64).repeat(64)[:rows]
+    std = rng.choice([0.25, 1.0, 3.0, 8.0], size=(rows + 31) // 32).repeat(32)[:rows]
+    tf = rng.normal(0, 1, (rows, vocab)) * std[:, None] + shift[:, None]
+    t = torch.from_numpy(tf).to(torch.bfloat16)
+    s = (t.double() + torch.from_numpy(rng.normal(0, 0.5, (rows, vocab)))).to(torch.bfloat16)
+    run_and_check(dev, orc, t, s, k, 1.0, torch.bfloat16, "changing row scale")
 
 
 def test_topk_signed_zero_ties(dev, orc):
