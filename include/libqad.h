@@ -59,8 +59,15 @@
  *    qad_check_finite()); the other outputs are then unspecified.
  *  - Alignment: tensor pointers 16-byte aligned, packed codes 4-byte aligned;
  *    scale and scalar pointers have no requirement beyond their type.
- *  - Results are deterministic: the same inputs give bitwise-equal outputs.
- *  - Thread-safe: no global mutable state.
+ *  - Results are deterministic: the same inputs give bitwise-equal outputs
+ *    (the W4A4 linear: within a process, once its GEMM plan for the shape
+ *    is chosen; see qad_w4a4_linear_fwd).
+ *  - Thread-safe.  The only state kept across calls is per-device and
+ *    written once: the compute-unit count and the quantizer's occupancy
+ *    (atomics), and for the W4A4 linear a hipBLASLt handle and its GEMM
+ *    plans (under a mutex).  Calls only enqueue kernels on `stream` (no
+ *    memset, no allocation, no host synchronisation; qad_check_finite
+ *    excepted), so a sequence of calls can be captured into a HIP graph.
  */
 #ifndef LIBQAD_H
 #define LIBQAD_H
@@ -229,7 +236,13 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  *             overlap another or an input
  *   workspace : qad_workspace_bytes(QAD_OP_W4A4_LINEAR, M, N, K) bytes
  * The library keeps one hipBLASLt handle per device, created on first use;
- * hipBLASLt's scratch comes from the workspace. */
+ * hipBLASLt's scratch comes from the workspace.  The first call of a shape
+ * on a device times up to 16 of hipBLASLt's candidate algorithms on the
+ * call's own operands (one synchronisation of `stream`) and keeps the
+ * fastest for every later call of that shape; under graph capture it takes
+ * the heuristic's first candidate untimed.  Another process may choose
+ * another algorithm: results then differ within the fp32 accumulation
+ * bound, not bit for bit. */
 qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, int64_t M, int64_t N, int64_t K,
                                  const uint8_t* w_scales_in, const float* w_tscale_in, void* y, void* xq, void* wq,
                                  void* workspace, size_t ws_bytes, qad_stream_t stream);
