@@ -93,14 +93,56 @@ def _stream(dev: torch.device):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _brc(x: torch.Tensor):
-    if not x.is_contiguous():
-        raise ValueError("tensor must be contiguous")
+def _gpu(t, name: str, dev: torch.device | None = None, dtype=None, numel: int | None = None) -> torch.Tensor:
+    """Check a tensor argument before its pointer goes to the library: a
+    contiguous tensor on the GPU (on `dev` when given), of `dtype` (one dtype
+    or a tuple) and `numel` elements when given.  Raises ValueError or
+    TypeError; the library itself cannot tell a host pointer or a short
+    buffer from a good one."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got device %s" % (name, t.device))
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s must hold %d elements, got %d" % (name, numel, t.numel()))
+    return t
+
+
+def _opt(t, name: str, dev: torch.device, dtype=None, numel: int | None = None):
+    return None if t is None else _gpu(t, name, dev, dtype, numel)
+
+
+_FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _ws(ws, dev: torch.device):
+    """The caller's workspace: a uint8 GPU tensor (its size is checked by the library)."""
+    return _opt(ws, "ws", dev, torch.uint8)
+
+
+def _brc(x: torch.Tensor, name: str = "x"):
+    _gpu(x, name, dtype=_FLOAT)
     if x.dim() == 2:
         return 1, x.shape[0], x.shape[1]
     if x.dim() == 3:
         return x.shape[0], x.shape[1], x.shape[2]
     raise ValueError("expected [R, C] or [B, R, C], got shape %s" % (tuple(x.shape),))
+
+
+def _logits(teacher: torch.Tensor, student: torch.Tensor):
+    """(tokens, vocab, device) of a teacher / student pair of one dtype and shape"""
+    _gpu(teacher, "teacher", dtype=_FLOAT)
+    _gpu(student, "student", teacher.device, teacher.dtype)
+    if teacher.shape != student.shape or teacher.dim() != 2:
+        raise ValueError("teacher and student must both be [tokens, vocab]")
+    tokens, vocab = teacher.shape
+    return tokens, vocab, teacher.device
 
 
 def qad_workspace_bytes(op: int, B: int, R: int, C_: int) -> int:
@@ -115,6 +157,8 @@ def workspace(op: int, B: int, R: int, C_: int, device) -> torch.Tensor | None:
 def nvfp4_amax(x: torch.Tensor, amax_out: torch.Tensor | None = None,
                ws: torch.Tensor | None = None) -> torch.Tensor:
     B, R, Cc = _brc(x)
+    amax_out = _opt(amax_out, "amax_out", x.device, torch.float32, B)
+    ws = _ws(ws, x.device)
     if amax_out is None:
         amax_out = torch.empty(B, dtype=torch.float32, device=x.device)
     if ws is None:
@@ -133,16 +177,22 @@ def nvfp4_quantize(x: torch.Tensor, scales_in=None, tscale_in=None, codes=True, 
     """
     B, R, Cc = _brc(x)
     dev = x.device
+    n = B * R * Cc
+    scales_in = _opt(scales_in, "scales_in", dev, torch.uint8, n // 16)
+    tscale_in = _opt(tscale_in, "tscale_in", dev, torch.float32, B)
+    ws = _ws(ws, dev)
 
-    def out(arg, shape, dtype):
+    def out(arg, name, shape, dtype):
         if arg is True:
             return torch.empty(shape, dtype=dtype, device=dev)
-        return arg if isinstance(arg, torch.Tensor) else None
+        if arg is None or arg is False:
+            return None
+        return _gpu(arg, name, dev, dtype, shape[0] * shape[1] * shape[2] if len(shape) == 3 else shape[0])
 
-    codes = out(codes, (B, R, Cc // 2), torch.uint8)
-    scales_out = out(scales_out, (B, R, Cc // 16), torch.uint8)
-    tscale_out = out(tscale_out, (B,), torch.float32)
-    y = out(y, (B, R, Cc), torch.bfloat16)
+    codes = out(codes, "codes", (B, R, Cc // 2), torch.uint8)
+    scales_out = out(scales_out, "scales_out", (B, R, Cc // 16), torch.uint8)
+    tscale_out = out(tscale_out, "tscale_out", (B,), torch.float32)
+    y = out(y, "y", (B, R, Cc), torch.bfloat16)
     if ws is None and scales_in is None:
         ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, dev)
     _check(lib().nvfp4_quantize(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
@@ -154,6 +204,11 @@ def nvfp4_quantize(x: torch.Tensor, scales_in=None, tscale_in=None, codes=True, 
 def nvfp4_qdq_fwd(x: torch.Tensor, scales_in=None, tscale_in=None, y: torch.Tensor | None = None,
                   ws: torch.Tensor | None = None) -> torch.Tensor:
     B, R, Cc = _brc(x)
+    n = B * R * Cc
+    scales_in = _opt(scales_in, "scales_in", x.device, torch.uint8, n // 16)
+    tscale_in = _opt(tscale_in, "tscale_in", x.device, torch.float32, B)
+    y = _opt(y, "y", x.device, torch.bfloat16, n)
+    ws = _ws(ws, x.device)
     if y is None:
         y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     if ws is None and scales_in is None:
@@ -164,8 +219,8 @@ def nvfp4_qdq_fwd(x: torch.Tensor, scales_in=None, tscale_in=None, y: torch.Tens
 
 
 def nvfp4_qdq_bwd(grad_y: torch.Tensor, grad_x: torch.Tensor | None = None) -> torch.Tensor:
-    if not grad_y.is_contiguous():
-        raise ValueError("tensor must be contiguous")
+    _gpu(grad_y, "grad_y", dtype=_FLOAT)
+    grad_x = _opt(grad_x, "grad_x", grad_y.device, grad_y.dtype, grad_y.numel())
     if grad_x is None:
         grad_x = torch.empty_like(grad_y)
     _check(lib().nvfp4_qdq_bwd(_p(grad_y), _p(grad_x), _dt(grad_y), grad_y.numel(),
@@ -179,15 +234,12 @@ def nvfp4_qdq_bwd_clipped(grad_y: torch.Tensor, x: torch.Tensor, scales: torch.T
     where |x| <= 6 * s_eff, +0 elsewhere.  grad_y and x share the shape
     [R, C] or [B, R, C]; scales [.., C/16] u8, tscale [B] float32."""
     B, R, Cc = _brc(x)
+    _gpu(grad_y, "grad_y", x.device, _FLOAT)
     if tuple(grad_y.shape) != tuple(x.shape):
         raise ValueError("grad_y and x shapes differ")
-    for t in (grad_y, scales, tscale):
-        if not t.is_contiguous():
-            raise ValueError("tensor must be contiguous")
-    if scales.dtype != torch.uint8 or scales.numel() != B * R * (Cc // 16):
-        raise ValueError("scales must be uint8 with one code per 16 elements")
-    if tscale.dtype != torch.float32 or tscale.numel() != B:
-        raise ValueError("tscale must be float32 with one scale per tensor")
+    _gpu(scales, "scales (uint8, one code per 16 elements)", x.device, torch.uint8, B * R * (Cc // 16))
+    _gpu(tscale, "tscale (float32, one scale per tensor)", x.device, torch.float32, B)
+    grad_x = _opt(grad_x, "grad_x", x.device, grad_y.dtype, grad_y.numel())
     if grad_x is None:
         grad_x = torch.empty_like(grad_y)
     _check(lib().nvfp4_qdq_bwd_clipped(_p(grad_y), _dt(grad_y), _p(x), _dt(x), B, R, Cc, _p(scales), _p(tscale),
@@ -198,8 +250,11 @@ def nvfp4_qdq_bwd_clipped(grad_y: torch.Tensor, x: torch.Tensor, scales: torch.T
 def nvfp4_mse_calibrate(w: torch.Tensor, n_candidates: int = 64, k_min: float = 0.5, k_max: float = 1.0,
                         scales_out: torch.Tensor | None = None, tscale_out: torch.Tensor | None = None,
                         ws: torch.Tensor | None = None):
-    B, R, Cc = _brc(w)
+    B, R, Cc = _brc(w, "w")
     dev = w.device
+    scales_out = _opt(scales_out, "scales_out", dev, torch.uint8, B * R * (Cc // 16))
+    tscale_out = _opt(tscale_out, "tscale_out", dev, torch.float32, B)
+    ws = _ws(ws, dev)
     if scales_out is None:
         scales_out = torch.empty((B, R, Cc // 16), dtype=torch.uint8, device=dev)
     if tscale_out is None:
@@ -217,16 +272,16 @@ def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: fl
                    loss_out: torch.Tensor | None = None, grad: torch.Tensor | None = None,
                    ws: torch.Tensor | None = None):
     """Returns (loss f32[1], row_loss f32[tokens] or None, grad or None)."""
-    if teacher.shape != student.shape or teacher.dim() != 2:
-        raise ValueError("teacher and student must both be [tokens, vocab]")
-    tokens, vocab = teacher.shape
-    dev = teacher.device
+    tokens, vocab, dev = _logits(teacher, student)
+    loss_out = _opt(loss_out, "loss_out", dev, torch.float32, 1)
+    grad = _opt(grad, "grad", dev, _FLOAT, tokens * vocab)
+    ws = _ws(ws, dev)
     if grad_scale is None:
         grad_scale = 1.0 / tokens if tokens else 0.0
     if loss_out is None:
         loss_out = torch.empty(1, dtype=torch.float32, device=dev)
     rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
-        row_loss if isinstance(row_loss, torch.Tensor) else None)
+        _gpu(row_loss, "row_loss", dev, torch.float32, tokens) if isinstance(row_loss, torch.Tensor) else None)
     if grad is None and grad_dtype is not None:
         grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
     gt = _dt(grad) if grad is not None else QAD_BF16
@@ -245,10 +300,14 @@ def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=T
     or None, tscale f32[B], y bf16 like x or None)."""
     B, R, Cc = _brc(x)
     dev = x.device
+    n = B * R * Cc
+    tscale_in = _opt(tscale_in, "tscale_in", dev, torch.float32, B)
+    tscale_out = _opt(tscale_out, "tscale_out", dev, torch.float32, B)
+    ws = _ws(ws, dev)
     cd = torch.empty(x.shape, dtype=torch.uint8, device=dev) if codes is True else (
-        codes if isinstance(codes, torch.Tensor) else None)
+        _gpu(codes, "codes", dev, torch.uint8, n) if isinstance(codes, torch.Tensor) else None)
     yy = torch.empty(x.shape, dtype=torch.bfloat16, device=dev) if y is True else (
-        y if isinstance(y, torch.Tensor) else None)
+        _gpu(y, "y", dev, torch.bfloat16, n) if isinstance(y, torch.Tensor) else None)
     if tscale_out is None:
         tscale_out = torch.empty(B, dtype=torch.float32, device=dev)
     if ws is None and tscale_in is None:
@@ -263,13 +322,20 @@ def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=No
     """y = QDQ(x) QDQ(w)^T (bf16) for x [M, K], w [N, K]; w's scales are
     dynamic, or the frozen w_scales_in (u8 [N, K/16]) / w_tscale_in (f32 [1]).
     Returns (y, xq, wq)."""
-    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1] or x.dtype != w.dtype:
+    _gpu(x, "x", dtype=_FLOAT)
+    _gpu(w, "w", x.device, x.dtype)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError("x [M, K] and w [N, K] of one dtype")
     (M, K), N = x.shape, w.shape[0]
     dev = x.device
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
-    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if xq is None else xq
-    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if wq is None else wq
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else _gpu(y, "y", dev, torch.bfloat16, M * N)
+    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if xq is None else _gpu(xq, "xq", dev, torch.bfloat16,
+                                                                                        M * K)
+    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if wq is None else _gpu(wq, "wq", dev, torch.bfloat16,
+                                                                                        N * K)
+    ws = _ws(ws, dev)
+    w_scales_in = _opt(w_scales_in, "w_scales_in", dev)
+    w_tscale_in = _opt(w_tscale_in, "w_tscale_in", dev)
     if ws is None:
         ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
     if (w_scales_in is None) != (w_tscale_in is None):
@@ -285,13 +351,21 @@ def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=No
 def qad_w4a4_linear_bwd(grad_y: torch.Tensor, xq: torch.Tensor, wq: torch.Tensor, grad_x=True, grad_w=True,
                         ws: torch.Tensor | None = None):
     """Straight-through backward: returns (grad_x [M, K] or None, grad_w [N, K] or None)."""
+    _gpu(grad_y, "grad_y", dtype=torch.bfloat16)
+    dev = grad_y.device
+    _gpu(xq, "xq", dev, torch.bfloat16)
+    _gpu(wq, "wq", dev, torch.bfloat16)
+    if grad_y.dim() != 2 or xq.dim() != 2 or wq.dim() != 2:
+        raise ValueError("grad_y [M, N], xq [M, K] and wq [N, K]")
     M, N = grad_y.shape
     K = xq.shape[1]
-    dev = grad_y.device
+    if xq.shape[0] != M or tuple(wq.shape) != (N, K):
+        raise ValueError("grad_y [M, N], xq [M, K] and wq [N, K]")
     gx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if grad_x is True else (
-        grad_x if isinstance(grad_x, torch.Tensor) else None)
+        _gpu(grad_x, "grad_x", dev, torch.bfloat16, M * K) if isinstance(grad_x, torch.Tensor) else None)
     gw = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if grad_w is True else (
-        grad_w if isinstance(grad_w, torch.Tensor) else None)
+        _gpu(grad_w, "grad_w", dev, torch.bfloat16, N * K) if isinstance(grad_w, torch.Tensor) else None)
+    ws = _ws(ws, dev)
     if ws is None:
         ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
     _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), _p(ws), ws.numel(),
@@ -306,16 +380,16 @@ def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, te
     """KL over the teacher's top-k entries of each row (ties with the k-th
     largest kept, both softmaxes renormalised over them).  Returns (loss
     f32[1], row_loss f32[tokens] or None, grad or None)."""
-    if teacher.shape != student.shape or teacher.dim() != 2:
-        raise ValueError("teacher and student must both be [tokens, vocab]")
-    tokens, vocab = teacher.shape
-    dev = teacher.device
+    tokens, vocab, dev = _logits(teacher, student)
+    loss_out = _opt(loss_out, "loss_out", dev, torch.float32, 1)
+    grad = _opt(grad, "grad", dev, _FLOAT, tokens * vocab)
+    ws = _ws(ws, dev)
     if grad_scale is None:
         grad_scale = 1.0 / tokens if tokens else 0.0
     if loss_out is None:
         loss_out = torch.empty(1, dtype=torch.float32, device=dev)
     rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
-        row_loss if isinstance(row_loss, torch.Tensor) else None)
+        _gpu(row_loss, "row_loss", dev, torch.float32, tokens) if isinstance(row_loss, torch.Tensor) else None)
     if grad is None and grad_dtype is not None:
         grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
     gt = _dt(grad) if grad is not None else QAD_BF16
@@ -335,18 +409,18 @@ def qad_kl_topp_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, top_p: flo
     largest teacher value at which the teacher mass reaches top_p (ties
     kept), both softmaxes renormalised over them.  Returns (loss f32[1],
     row_loss f32[tokens] or None, grad or None, tau f32[tokens] or None)."""
-    if teacher.shape != student.shape or teacher.dim() != 2:
-        raise ValueError("teacher and student must both be [tokens, vocab]")
-    tokens, vocab = teacher.shape
-    dev = teacher.device
+    tokens, vocab, dev = _logits(teacher, student)
+    loss_out = _opt(loss_out, "loss_out", dev, torch.float32, 1)
+    grad = _opt(grad, "grad", dev, _FLOAT, tokens * vocab)
+    ws = _ws(ws, dev)
     if grad_scale is None:
         grad_scale = 1.0 / tokens if tokens else 0.0
     if loss_out is None:
         loss_out = torch.empty(1, dtype=torch.float32, device=dev)
     rows = torch.empty(tokens, dtype=torch.float32, device=dev) if row_loss is True else (
-        row_loss if isinstance(row_loss, torch.Tensor) else None)
+        _gpu(row_loss, "row_loss", dev, torch.float32, tokens) if isinstance(row_loss, torch.Tensor) else None)
     taus = torch.empty(tokens, dtype=torch.float32, device=dev) if tau is True else (
-        tau if isinstance(tau, torch.Tensor) else None)
+        _gpu(tau, "tau", dev, torch.float32, tokens) if isinstance(tau, torch.Tensor) else None)
     if grad is None and grad_dtype is not None:
         grad = torch.empty((tokens, vocab), dtype=grad_dtype, device=dev)
     gt = _dt(grad) if grad is not None else QAD_BF16
@@ -360,6 +434,7 @@ def qad_kl_topp_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, top_p: flo
 
 def qad_check_finite(values: torch.Tensor) -> bool:
     """True if every value is finite (synchronises the current stream)."""
+    _gpu(values, "values", dtype=torch.float32)
     st = lib().qad_check_finite(_p(values), values.numel(), _stream(values.device))
     if st == 6:
         return False

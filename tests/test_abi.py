@@ -326,3 +326,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_binding_rejects_host_tensors():
+    # host tensors never reach the library: their pointers would be read by
+    # the kernels as device addresses
+    import numpy as np
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    t = torch.zeros(2, 64, dtype=torch.bfloat16)
+    calls = [
+        lambda: q.nvfp4_amax(x),
+        lambda: q.nvfp4_quantize(x),
+        lambda: q.nvfp4_qdq_fwd(x),
+        lambda: q.nvfp4_qdq_bwd(x),
+        lambda: q.nvfp4_qdq_bwd_clipped(x, x, torch.zeros(8, dtype=torch.uint8), torch.ones(1)),
+        lambda: q.nvfp4_mse_calibrate(x),
+        lambda: q.fp8_quantize(x),
+        lambda: q.qad_kl_fwd_bwd(t, t),
+        lambda: q.qad_kl_topk_fwd_bwd(t, t, 4),
+        lambda: q.qad_kl_topp_fwd_bwd(t, t, 0.9),
+        lambda: q.qad_w4a4_linear_fwd(x, x),
+        lambda: q.qad_w4a4_linear_bwd(x[:, :4].contiguous(), x, x),
+        lambda: q.qad_check_finite(torch.zeros(3)),
+    ]
+    for i, f in enumerate(calls):
+        with pytest.raises(ValueError, match="must be on the GPU"):
+            f()
+    with pytest.raises(TypeError):
+        q.nvfp4_quantize(np.zeros((4, 32), np.float32))
