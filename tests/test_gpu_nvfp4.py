@@ -247,6 +247,25 @@ def test_mse_calibrate(dev, orc, dtype, shape, n, kmin, kmax):
     check_quantize(orc, w3.to(dev), "frozen-after-mse", frozen=(host(sc), host(ts)))
 
 
+@pytest.mark.parametrize("dtype,shape", [("bf16", (32, 256, 2048)), ("fp32", (64, 256, 1024))])
+def test_mse_calibrate_large_batch(dev, orc, dtype, shape):
+    # a batch of many tensors in one grid (workgroups of several tensors
+    # resident together, each reading its own tensor scale); every scale of
+    # every tensor is compared
+    g = torch.Generator().manual_seed(shape[0])
+    w = torch.randn(shape, generator=g) * 0.02
+    w[..., ::29] *= 12.0
+    w = w.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    announce("nvfp4_mse_calibrate batch %s %s" % (dtype, shape))
+    sc, ts = q.nvfp4_mse_calibrate(w.to(dev))
+    torch.cuda.synchronize()
+    wc, sch, tsh = host(w), host(sc), host(ts)
+    for b in range(shape[0]):
+        rs, rt = orc.mse_calibrate(wc[b])
+        assert tsh[b] == np.float32(rt), b
+        assert np.array_equal(sch[b].reshape(rs.shape), rs), b
+
+
 def test_deterministic(dev):
     w, _ = synth.moe_weights_bf16(experts=4, rows=256, cols=512, seed=2, with_grad=False)
     w = w.to(dev)
