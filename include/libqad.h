@@ -54,6 +54,11 @@
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check returns its status and launches nothing.  A failed launch returns
  *    QAD_ERR_HIP.  Calls that share a workspace must not overlap in time.
+ *  - Empty inputs are valid, and a pointer to an empty buffer may be NULL.
+ *    For tensors with R*C == 0 nothing is coded;
+ *    tscale_out (when given) receives 1.0f per tensor, the scale of the
+ *    zero tensor, or with frozen scales the given tscale_in, and
+ *    nvfp4_amax writes 0.  The KL losses with tokens == 0 write loss 0.
  *  - Inputs must be finite.  A NaN or infinity makes the tensor amax and the
  *    tensor scale non-finite (visible in amax_out / tscale_out, or through
  *    qad_check_finite()); the other outputs are then unspecified.
@@ -235,6 +240,8 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  *             receive QDQ(x), QDQ(w) (kept for the backward); no output may
  *             overlap another or an input
  *   workspace : qad_workspace_bytes(QAD_OP_W4A4_LINEAR, M, N, K) bytes
+ * M == 0 or N == 0: y is empty and the other operand's QDQ output (xq or wq)
+ * is still written; pointers of empty buffers may be NULL.
  * The library keeps one hipBLASLt handle per device, created on first use;
  * hipBLASLt's scratch comes from the workspace.  The first call of a shape
  * on a device times up to 16 of hipBLASLt's candidate algorithms on the

@@ -25,7 +25,7 @@ inline hipStream_t hs(qad_stream_t s) { return reinterpret_cast<hipStream_t>(s);
 // B, R, C non-negative and B*R*C bounded; returns the element count or -1
 int64_t tensor_elems(int64_t B, int64_t R, int64_t C)
 {
-    if (B < 0 || R < 0 || C < 0) return -1;
+    if (B < 0 || R < 0 || C < 0 || B > kMaxElems || R > kMaxElems || C > kMaxElems) return -1;
     if (B == 0 || R == 0 || C == 0) return 0;
     if (R > kMaxElems / C) return -1;
     const int64_t rc = R * C;
@@ -57,7 +57,7 @@ size_t record_bytes(int64_t B, int64_t rc)
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return x < y + nb && y < x + na;
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
 }
 
 // fp8: per-tensor E4M3 (no block scales; frozen iff tscale_in is given;
@@ -70,9 +70,22 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
     if (n < 0 || C % (fp8 ? 8 : 16) != 0 || !batch_grid_ok(B, R * C)) return QAD_ERR_SHAPE;
+    // frozen iff the tensor scales are given (the block scales of an empty
+    // tensor may be NULL like every other empty buffer)
+    if (!fp8 && scales_in && !tscale_in) return QAD_ERR_INVALID_ARG;
+    const bool frozen = tscale_in != nullptr;
+    if (n == 0) {
+        // empty tensors: nothing to code; a tensor scale is still reported,
+        // the frozen one as given and the dynamic one as for the zero tensor
+        if (B == 0 || !tscale_out) return QAD_OK;
+        if (!aligned(tscale_out, 4) || (tscale_in && !aligned(tscale_in, 4))) return QAD_ERR_ALIGNMENT;
+        uint32_t* ts = reinterpret_cast<uint32_t*>(tscale_out);
+        if (frozen)
+            return hip_status(qad::launch_copy_u32(reinterpret_cast<const uint32_t*>(tscale_in), ts, B, hs(stream)));
+        return hip_status(qad::launch_fill_u32(ts, B, 0x3F800000u, hs(stream)));   // 1.0f
+    }
     if (!codes && !scales_out && !tscale_out && !y) return QAD_ERR_INVALID_ARG;
-    if (!fp8 && (scales_in == nullptr) != (tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
-    if (n == 0) return QAD_OK;
+    if (!fp8 && frozen && !scales_in) return QAD_ERR_INVALID_ARG;
     if (!x) return QAD_ERR_INVALID_ARG;
     if (!aligned(x, 16) || (y && !aligned(y, 16)) || (codes && !aligned(codes, fp8 ? 8 : 4)) ||
         (tscale_in && !aligned(tscale_in, 4)) || (tscale_out && !aligned(tscale_out, 4)))
@@ -82,7 +95,6 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
         (codes && ranges_overlap(x, xbytes, codes, fp8 ? (size_t)n : (size_t)n / 2)) ||
         (scales_out && ranges_overlap(x, xbytes, scales_out, (size_t)n / 16)))
         return QAD_ERR_INVALID_ARG;
-    const bool frozen = fp8 ? tscale_in != nullptr : scales_in != nullptr;
     if (!frozen) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C)) return QAD_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
@@ -179,7 +191,6 @@ qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
                            const uint8_t* scales_in, const float* tscale_in, void* y, void* workspace,
                            size_t ws_bytes, qad_stream_t stream)
 {
-    if (!y) return QAD_ERR_INVALID_ARG;
     return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, nullptr, nullptr, nullptr, y, workspace, ws_bytes,
                          stream);
 }
@@ -247,7 +258,12 @@ qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64
     // step at most 1/16, below the narrowest E4M3 rounding interval, 1/15)
     if (n_candidates > 1 && ((double)k_max - (double)k_min) / (double)(n_candidates - 1) > (double)k_min / 16.0)
         return QAD_ERR_INVALID_ARG;
-    if (n == 0) return QAD_OK;
+    if (n == 0) {
+        // empty tensors: no block scales; the tensor scale of the zero tensor
+        if (B == 0 || !tscale_out) return QAD_OK;
+        if (!aligned(tscale_out, 4)) return QAD_ERR_ALIGNMENT;
+        return hip_status(qad::launch_fill_u32(reinterpret_cast<uint32_t*>(tscale_out), B, 0x3F800000u, hs(stream)));
+    }
     if (!w || !scales_out || !tscale_out) return QAD_ERR_INVALID_ARG;
     if (!aligned(w, 16) || !aligned(tscale_out, 4)) return QAD_ERR_ALIGNMENT;
     if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_MSE_CALIBRATE, B, R, C)) return QAD_ERR_WORKSPACE;

@@ -179,7 +179,7 @@ bool dims_ok(int64_t M, int64_t N, int64_t K)
 bool overlap(const void* a, size_t na, const void* b, size_t nb)
 {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return x < y + nb && y < x + na;
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
 }
 
 } // namespace
@@ -201,10 +201,15 @@ qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, i
 {
     if (dt != QAD_BF16 && dt != QAD_F32) return QAD_ERR_DTYPE;
     if (!dims_ok(M, N, K) || K <= 0 || K % 16 != 0) return QAD_ERR_SHAPE;
-    if (!y || !xq || !wq || (w_scales_in == nullptr) != (w_tscale_in == nullptr)) return QAD_ERR_INVALID_ARG;
-    if (M == 0 || N == 0) return QAD_OK;
-    if (!x || !w) return QAD_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(xq) || !aligned16(wq)) return QAD_ERR_ALIGNMENT;
+    // empty outputs (M == 0 or N == 0) may be NULL; the other QDQ output is
+    // still written
+    if ((M > 0 && (!x || !xq)) || (N > 0 && (!w || !wq)) || (M > 0 && N > 0 && !y) ||
+        (w_scales_in == nullptr) != (w_tscale_in == nullptr))
+        return QAD_ERR_INVALID_ARG;
+    if (M == 0 && N == 0) return QAD_OK;
+    if ((M > 0 && (!aligned16(x) || !aligned16(xq))) || (N > 0 && (!aligned16(w) || !aligned16(wq))) ||
+        (M > 0 && N > 0 && !aligned16(y)))
+        return QAD_ERR_ALIGNMENT;
     const size_t es = dt == QAD_BF16 ? 2 : 4;
     if (overlap(y, (size_t)M * N * 2, xq, (size_t)M * K * 2) || overlap(y, (size_t)M * N * 2, wq, (size_t)N * K * 2) ||
         overlap(xq, (size_t)M * K * 2, wq, (size_t)N * K * 2) || overlap(x, (size_t)M * K * es, y, (size_t)M * N * 2) ||
@@ -213,10 +218,15 @@ qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, i
     if (!workspace || ws_bytes < qad::linear_workspace_bytes(M, N, K)) return QAD_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return QAD_ERR_ALIGNMENT;
     const size_t rec = qad::linear_workspace_bytes(M, N, K) - kGemmWorkspace;
-    qad_status_t st = nvfp4_qdq_fwd(x, dt, 1, M, K, nullptr, nullptr, xq, workspace, rec, stream);
-    if (st != QAD_OK) return st;
-    st = nvfp4_qdq_fwd(w, dt, 1, N, K, w_scales_in, w_tscale_in, wq, workspace, rec, stream);
-    if (st != QAD_OK) return st;
+    if (M > 0) {
+        const qad_status_t st = nvfp4_qdq_fwd(x, dt, 1, M, K, nullptr, nullptr, xq, workspace, rec, stream);
+        if (st != QAD_OK) return st;
+    }
+    if (N > 0) {
+        const qad_status_t st = nvfp4_qdq_fwd(w, dt, 1, N, K, w_scales_in, w_tscale_in, wq, workspace, rec, stream);
+        if (st != QAD_OK) return st;
+    }
+    if (M == 0 || N == 0) return QAD_OK;
     // row-major y[M][N] = xq[M][K] wq[N][K]^T is the column-major N x M
     // product wq^T (K x N stored, transposed) times xq (K x M stored)
     return gemm_bf16(true, false, N, M, K, wq, K, xq, K, y, N, static_cast<char*>(workspace) + rec,
@@ -227,7 +237,7 @@ qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void*
                                  void* grad_x, void* grad_w, void* workspace, size_t ws_bytes, qad_stream_t stream)
 {
     if (!dims_ok(M, N, K) || K <= 0 || K % 16 != 0) return QAD_ERR_SHAPE;
-    if (!grad_x && !grad_w) return QAD_ERR_INVALID_ARG;
+    if (!grad_x && !grad_w && (M > 0 || N > 0)) return QAD_ERR_INVALID_ARG;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (M == 0 || N == 0) {
         // an empty sum: the other gradient is all zeros (K is even)

@@ -462,6 +462,12 @@ __global__ void fill_u32_kernel(uint32_t* out, int64_t n, uint32_t v)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] = v;
 }
 
+__global__ void copy_u32_kernel(const uint32_t* src, uint32_t* dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------------------
 // Straight-through backward: chunked 16-byte non-temporal copy (16 KiB per
 // workgroup) plus a tail of up to seven 16-bit halves.
@@ -710,6 +716,15 @@ hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t v, hipStream_t str
     int64_t grid = (n + kQThreads - 1) / kQThreads;
     if (grid > 4096) grid = 4096;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream, out, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_u32(const uint32_t* src, uint32_t* dst, int64_t n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    int64_t grid = (n + kQThreads - 1) / kQThreads;
+    if (grid > 4096) grid = 4096;
+    hipLaunchKernelGGL(copy_u32_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream, src, dst, n);
     return hipGetLastError();
 }
 

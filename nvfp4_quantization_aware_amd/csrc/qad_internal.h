@@ -11,6 +11,8 @@ namespace qad {
 
 // out[i] = v for i < n (graph-safe replacement for a memset)
 hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t v, hipStream_t stream);
+// n words from src to dst (4-byte aligned, no overlap)
+hipError_t launch_copy_u32(const uint32_t* src, uint32_t* dst, int64_t n, hipStream_t stream);
 
 // Words of one tensor's record in the workspace for a tensor cut into P
 // chunks (amax publication, sub-group counters, broadcast slots).

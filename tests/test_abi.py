@@ -116,6 +116,20 @@ def test_quantize_rejects(L):
     assert f(P, 1, 0, 4, 32, None, None, None, None, None, P * 2, P * 3, ws, None) == OK
 
 
+def test_empty_tensors_accepted_without_launch(L):
+    # R * C == 0: every buffer is empty and may be NULL; without a tensor
+    # scale output nothing is launched, so these return on the host
+    f = L.nvfp4_quantize
+    assert f(None, 1, 3, 0, 64, None, None, None, None, None, None, None, 0, None) == OK
+    assert f(None, 1, 3, 0, 64, None, P, None, None, None, None, None, 0, None) == OK      # frozen, no block scales
+    assert f(None, 1, 3, 0, 64, P, None, None, None, None, None, None, 0, None) == INVALID  # block scales alone
+    assert L.nvfp4_qdq_fwd(None, 1, 2, 0, 32, None, None, None, None, 0, None) == OK
+    assert L.fp8_quantize(None, 0, 2, 5, 0, None, None, None, None, None, 0, None) == OK
+    assert L.nvfp4_mse_calibrate(None, 1, 2, 0, 32, 64, 0.5, 1.0, None, None, None, 0, None) == OK
+    # the batch count stays bounded even when every tensor is empty
+    assert f(None, 1, 1 << 40, 0, 64, None, None, None, None, None, None, None, 0, None) == SHAPE
+
+
 def test_batches_beyond_one_grid_rejected(L):
     # 2^31 tensors of 16 elements: 2^35 elements (allowed) but one workgroup
     # per tensor already exceeds a grid's 2^31 - 1 workgroups
@@ -154,11 +168,14 @@ def test_w4a4_linear_rejects(L):
     assert fw(*a(wsb=ws - 256)) == WS and fw(*a(ws=None)) == WS
     assert fw(*a(ws=P * 6 + 128)) == ALIGN
     assert fw(*a(y=P * 4)) == INVALID                 # y overlaps xq
-    assert fw(*a(M=0)) == OK                          # nothing to do
+    assert fw(*a(M=0, N=0)) == OK                     # nothing to do
+    assert fw(*a(M=0, N=0, x=None, w=None, y=None, xq=None, wq=None)) == OK   # empty buffers may be NULL
+    assert fw(*a(M=0, wq=None)) == INVALID            # wq is still written when only M is 0
     b = lambda **kw: [kw.get("gy", P), kw.get("xq", P * 2), kw.get("wq", P * 3), kw.get("M", 64), kw.get("N", 32),
                       kw.get("K", 128), kw.get("gx", P * 4), kw.get("gw", P * 5), kw.get("ws", P * 6),
                       kw.get("wsb", ws), None]
     assert bw(*b(gx=None, gw=None)) == INVALID
+    assert bw(*b(M=0, N=0, gx=None, gw=None)) == OK
     assert bw(*b(K=8)) == SHAPE
     assert bw(*b(wq=None)) == INVALID                 # grad_x needs wq
     assert bw(*b(gx=P)) == INVALID                    # grad_x overlaps grad_y
