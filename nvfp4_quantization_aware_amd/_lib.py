@@ -91,6 +91,10 @@ def _p(t):
 
 def _stream(dev: torch.device):
     return torch.cuda.current_stream(dev).cuda_stream
+# Every library call runs with the tensors' device current (torch.cuda.device):
+# the library launches on the stream it is given, but keys its per-device
+# state (CU count, occupancy, the linear's hipBLASLt handle) by HIP's current
+# device, and the two must agree.
 
 
 def _gpu(t, name: str, dev: torch.device | None = None, dtype=None, numel: int | None = None) -> torch.Tensor:
@@ -163,8 +167,9 @@ def nvfp4_amax(x: torch.Tensor, amax_out: torch.Tensor | None = None,
         amax_out = torch.empty(B, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = workspace(QAD_OP_AMAX, B, R, Cc, x.device)
-    _check(lib().nvfp4_amax(_p(x), _dt(x), B, R, Cc, _p(amax_out), _p(ws), 0 if ws is None else ws.numel(),
-                            _stream(x.device)), "nvfp4_amax")
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_amax(_p(x), _dt(x), B, R, Cc, _p(amax_out), _p(ws), 0 if ws is None else ws.numel(),
+                                _stream(x.device)), "nvfp4_amax")
     return amax_out
 
 
@@ -195,9 +200,10 @@ def nvfp4_quantize(x: torch.Tensor, scales_in=None, tscale_in=None, codes=True, 
     y = out(y, "y", (B, R, Cc), torch.bfloat16)
     if ws is None and scales_in is None:
         ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, dev)
-    _check(lib().nvfp4_quantize(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
-                                _p(scales_out), _p(tscale_out), _p(y), _p(ws),
-                                0 if ws is None else ws.numel(), _stream(dev)), "nvfp4_quantize")
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_quantize(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
+                                    _p(scales_out), _p(tscale_out), _p(y), _p(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)), "nvfp4_quantize")
     return codes, scales_out, tscale_out, y
 
 
@@ -213,8 +219,9 @@ def nvfp4_qdq_fwd(x: torch.Tensor, scales_in=None, tscale_in=None, y: torch.Tens
         y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     if ws is None and scales_in is None:
         ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, x.device)
-    _check(lib().nvfp4_qdq_fwd(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(y), _p(ws),
-                               0 if ws is None else ws.numel(), _stream(x.device)), "nvfp4_qdq_fwd")
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_qdq_fwd(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(y), _p(ws),
+                                   0 if ws is None else ws.numel(), _stream(x.device)), "nvfp4_qdq_fwd")
     return y
 
 
@@ -223,8 +230,9 @@ def nvfp4_qdq_bwd(grad_y: torch.Tensor, grad_x: torch.Tensor | None = None) -> t
     grad_x = _opt(grad_x, "grad_x", grad_y.device, grad_y.dtype, grad_y.numel())
     if grad_x is None:
         grad_x = torch.empty_like(grad_y)
-    _check(lib().nvfp4_qdq_bwd(_p(grad_y), _p(grad_x), _dt(grad_y), grad_y.numel(),
-                               _stream(grad_y.device)), "nvfp4_qdq_bwd")
+    with torch.cuda.device(grad_y.device):
+        _check(lib().nvfp4_qdq_bwd(_p(grad_y), _p(grad_x), _dt(grad_y), grad_y.numel(),
+                                   _stream(grad_y.device)), "nvfp4_qdq_bwd")
     return grad_x
 
 
@@ -242,8 +250,9 @@ def nvfp4_qdq_bwd_clipped(grad_y: torch.Tensor, x: torch.Tensor, scales: torch.T
     grad_x = _opt(grad_x, "grad_x", x.device, grad_y.dtype, grad_y.numel())
     if grad_x is None:
         grad_x = torch.empty_like(grad_y)
-    _check(lib().nvfp4_qdq_bwd_clipped(_p(grad_y), _dt(grad_y), _p(x), _dt(x), B, R, Cc, _p(scales), _p(tscale),
-                                       _p(grad_x), _stream(x.device)), "nvfp4_qdq_bwd_clipped")
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_qdq_bwd_clipped(_p(grad_y), _dt(grad_y), _p(x), _dt(x), B, R, Cc, _p(scales), _p(tscale),
+                                           _p(grad_x), _stream(x.device)), "nvfp4_qdq_bwd_clipped")
     return grad_x
 
 
@@ -261,9 +270,10 @@ def nvfp4_mse_calibrate(w: torch.Tensor, n_candidates: int = 64, k_min: float = 
         tscale_out = torch.empty(B, dtype=torch.float32, device=dev)
     if ws is None:
         ws = workspace(QAD_OP_MSE_CALIBRATE, B, R, Cc, dev)
-    _check(lib().nvfp4_mse_calibrate(_p(w), _dt(w), B, R, Cc, n_candidates, k_min, k_max, _p(scales_out),
-                                     _p(tscale_out), _p(ws), 0 if ws is None else ws.numel(),
-                                     _stream(dev)), "nvfp4_mse_calibrate")
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_mse_calibrate(_p(w), _dt(w), B, R, Cc, n_candidates, k_min, k_max, _p(scales_out),
+                                         _p(tscale_out), _p(ws), 0 if ws is None else ws.numel(),
+                                         _stream(dev)), "nvfp4_mse_calibrate")
     return scales_out, tscale_out
 
 
@@ -287,9 +297,10 @@ def qad_kl_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, temperature: fl
     gt = _dt(grad) if grad is not None else QAD_BF16
     if ws is None:
         ws = workspace(QAD_OP_KL, 1, tokens, vocab, dev)
-    _check(lib().qad_kl_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, temperature,
-                                grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
-                                0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_fwd_bwd")
+    with torch.cuda.device(dev):
+        _check(lib().qad_kl_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, temperature,
+                                    grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_fwd_bwd")
     return loss_out, rows, grad
 
 
@@ -312,8 +323,9 @@ def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=T
         tscale_out = torch.empty(B, dtype=torch.float32, device=dev)
     if ws is None and tscale_in is None:
         ws = workspace(QAD_OP_QUANTIZE, B, R, Cc, dev)
-    _check(lib().fp8_quantize(_p(x), _dt(x), B, R, Cc, _p(tscale_in), _p(cd), _p(tscale_out), _p(yy), _p(ws),
-                              0 if ws is None else ws.numel(), _stream(dev)), "fp8_quantize")
+    with torch.cuda.device(dev):
+        _check(lib().fp8_quantize(_p(x), _dt(x), B, R, Cc, _p(tscale_in), _p(cd), _p(tscale_out), _p(yy), _p(ws),
+                                  0 if ws is None else ws.numel(), _stream(dev)), "fp8_quantize")
     return cd, tscale_out, yy
 
 
@@ -343,8 +355,9 @@ def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=No
     if w_scales_in is not None and (w_scales_in.dtype != torch.uint8 or w_scales_in.numel() != N * (K // 16)
                                     or w_tscale_in.dtype != torch.float32 or w_tscale_in.numel() != 1):
         raise ValueError("w_scales_in must be uint8 [N, K/16] and w_tscale_in float32 [1]")
-    _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(w_scales_in), _p(w_tscale_in), _p(y), _p(xq),
-                                     _p(wq), _p(ws), ws.numel(), _stream(dev)), "qad_w4a4_linear_fwd")
+    with torch.cuda.device(dev):
+        _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(w_scales_in), _p(w_tscale_in), _p(y), _p(xq),
+                                         _p(wq), _p(ws), ws.numel(), _stream(dev)), "qad_w4a4_linear_fwd")
     return y, xq, wq
 
 
@@ -368,8 +381,9 @@ def qad_w4a4_linear_bwd(grad_y: torch.Tensor, xq: torch.Tensor, wq: torch.Tensor
     ws = _ws(ws, dev)
     if ws is None:
         ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
-    _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), _p(ws), ws.numel(),
-                                     _stream(dev)), "qad_w4a4_linear_bwd")
+    with torch.cuda.device(dev):
+        _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), _p(ws), ws.numel(),
+                                         _stream(dev)), "qad_w4a4_linear_bwd")
     return gx, gw
 
 
@@ -395,9 +409,10 @@ def qad_kl_topk_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, k: int, te
     gt = _dt(grad) if grad is not None else QAD_BF16
     if ws is None:
         ws = workspace(QAD_OP_KL_TOPK, 1, tokens, vocab, dev)
-    _check(lib().qad_kl_topk_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, int(k), temperature,
-                                     grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
-                                     0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topk_fwd_bwd")
+    with torch.cuda.device(dev):
+        _check(lib().qad_kl_topk_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, int(k), temperature,
+                                         grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(ws),
+                                         0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topk_fwd_bwd")
     return loss_out, rows, grad
 
 
@@ -426,16 +441,18 @@ def qad_kl_topp_fwd_bwd(teacher: torch.Tensor, student: torch.Tensor, top_p: flo
     gt = _dt(grad) if grad is not None else QAD_BF16
     if ws is None:
         ws = workspace(QAD_OP_KL_TOPP, 1, tokens, vocab, dev)
-    _check(lib().qad_kl_topp_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, float(top_p),
-                                     temperature, grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(taus),
-                                     _p(ws), 0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topp_fwd_bwd")
+    with torch.cuda.device(dev):
+        _check(lib().qad_kl_topp_fwd_bwd(_p(teacher), _p(student), _dt(teacher), tokens, vocab, float(top_p),
+                                         temperature, grad_scale, _p(loss_out), _p(rows), _p(grad), gt, _p(taus),
+                                         _p(ws), 0 if ws is None else ws.numel(), _stream(dev)), "qad_kl_topp_fwd_bwd")
     return loss_out, rows, grad, taus
 
 
 def qad_check_finite(values: torch.Tensor) -> bool:
     """True if every value is finite (synchronises the current stream)."""
     _gpu(values, "values", dtype=torch.float32)
-    st = lib().qad_check_finite(_p(values), values.numel(), _stream(values.device))
+    with torch.cuda.device(values.device):
+        st = lib().qad_check_finite(_p(values), values.numel(), _stream(values.device))
     if st == 6:
         return False
     _check(st, "qad_check_finite")
