@@ -995,9 +995,11 @@ constexpr int kSelKeysPerLane = 65536 / kTopThreads;
 struct alignas(16) SelShared {
     struct {
         uint32_t hist[kSelWords];
+        unsigned long long mass[kTopThreads];   // top-p: the teacher mass of each lane's keys
         unsigned long long wave_tot64[kTopThreads / 64];
         uint32_t wave_tot[kTopThreads / 64];
         uint32_t wave_key[kTopThreads / 64];
+        uint32_t wave_grp[kTopThreads / 64];      // top-p: which 32-lane groups hold counts
         unsigned long long total64, target, rem64;
         uint32_t total, key, lane, rem;
     } c;
@@ -1065,34 +1067,62 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
         __syncthreads();
         return sh.c.key;
     } else {
-        // the largest (smallest for top_p >= 1) key present
+        // the largest (smallest for top_p >= 1) key present.  Bit b of nz is
+        // word whi - ((b + tid) & 31); rotated by tid, bit o is word whi - o,
+        // so the lane's highest (lowest) counted word is one count of zeros
+        // away, and one read of it picks the key inside.
         const bool want_min = top_p >= 1.0f;
+        const uint32_t rot = __builtin_rotateleft32(nz, (uint32_t)tid & (kWordsPerLane - 1));
         uint32_t e = want_min ? 0xFFFFFFFFu : 0u;
-        for (uint32_t m = nz; m; m &= m - 1u) {   // only the lane's nonzero words
-            const uint32_t wi = word_at(__builtin_ctz(m)), w = sh.c.hist[wi];
-            if (w & 0xFFFFu) e = want_min ? min(e, 2u * wi) : umax(e, 2u * wi);
-            if (w >> 16) e = want_min ? min(e, 2u * wi + 1u) : umax(e, 2u * wi + 1u);
+        if (rot) {
+            const uint32_t o = want_min ? 31u - (uint32_t)__builtin_clz(rot) : (uint32_t)__builtin_ctz(rot);
+            const uint32_t wi = whi - o, w = sh.c.hist[wi];
+            e = want_min ? ((w & 0xFFFFu) ? 2u * wi : 2u * wi + 1u) : ((w >> 16) ? 2u * wi + 1u : 2u * wi);
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             const uint32_t n = __shfl_xor(e, o, 64);
             e = want_min ? min(e, n) : umax(e, n);
         }
-        if ((tid & 63) == 0) sh.c.wave_key[tid >> 6] = e;
+        // 32-lane groups (lanes 32 g .. 32 g + 31) whose words hold counts
+        const unsigned long long act = __ballot(nz != 0u);
+        if ((tid & 63) == 0) {
+            const uint32_t wv = (uint32_t)tid >> 6;
+            sh.c.wave_key[wv] = e;
+            sh.c.wave_grp[wv] = ((uint32_t)act ? 1u : 0u) << (2 * wv) | ((uint32_t)(act >> 32) ? 1u : 0u) << (2 * wv + 1);
+        }
         __syncthreads();
         e = sh.c.wave_key[0];
-        for (int i = 1; i < kTopThreads / 64; ++i) e = want_min ? min(e, sh.c.wave_key[i]) : umax(e, sh.c.wave_key[i]);
+        uint32_t groups = sh.c.wave_grp[0];
+        for (int i = 1; i < kTopThreads / 64; ++i) {
+            e = want_min ? min(e, sh.c.wave_key[i]) : umax(e, sh.c.wave_key[i]);
+            groups |= sh.c.wave_grp[i];
+        }
         if (want_min) return e;
         const float m = value_of_key<true>(e) * c;
         // fixed-point mass of each key: count x floor(2^(c v - m) 2^40)
         auto key_mass = [&](uint32_t key, uint32_t n) {
             return fix40(exp2_hw(__builtin_fmaf(value_of_key<true>(key), c, -m))) * n;
         };
-        unsigned long long lm = 0;
-        for (uint32_t mk = nz; mk; mk &= mk - 1u) {   // only the lane's nonzero words
-            const uint32_t wi = word_at(__builtin_ctz(mk)), w = sh.c.hist[wi];
-            lm += key_mass(2u * wi, w & 0xFFFFu) + key_mass(2u * wi + 1u, w >> 16);
+        // The mass of each lane's 32 words.  The distinct values of a row
+        // crowd into a few thousand neighbouring keys, the words of a few
+        // dozen lanes, so the work is spread instead: the 1024 words of group
+        // g (lanes 32 g .. 32 g + 31 own them) are read one per lane, word
+        // 1024 (31 - g) + t by lane t, and each 32-lane half of a wave, which
+        // then holds the 32 words of one owner, sums them.  Only groups with
+        // counts are visited (a handful per row); integer sums, so the totals
+        // do not depend on the order.
+        static_assert(kSelWords == kWordsPerLane * kTopThreads && kWordsPerLane == 32, "one group per round");
+        for (uint32_t gm = groups; gm; gm &= gm - 1u) {
+            const uint32_t j = 31u - (uint32_t)__builtin_ctz(gm);
+            const uint32_t wi = j * (uint32_t)kTopThreads + (uint32_t)tid, w = sh.c.hist[wi];
+            unsigned long long v = w ? key_mass(2u * wi, w & 0xFFFFu) + key_mass(2u * wi + 1u, w >> 16) : 0ull;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+            if ((tid & 31) == 0) sh.c.mass[(uint32_t)(kTopThreads - 1) - (wi >> 5)] = v;
         }
+        __syncthreads();
+        const unsigned long long lm = (groups >> ((uint32_t)tid >> 5)) & 1u ? sh.c.mass[tid] : 0ull;
         const unsigned long long incl64 = block_incl_scan64(lm, sh.c.wave_tot64);
         if (tid == kTopThreads - 1) {
             unsigned long long t = (unsigned long long)ceil((double)top_p * (double)incl64);
