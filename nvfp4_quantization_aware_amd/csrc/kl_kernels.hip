@@ -180,17 +180,25 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         if (!valid) continue;
         float tv[8], sv[8], pt[8], ps[8];
         u.values(tv, sv);
-        bool kept[8];
-        float tk[8], sk[8];
+        // TOPK: dropped entries become -inf, whose weights 2^(-inf) are
+        // exactly 0 once a kept entry has set the maxima; a unit of this lane
+        // with no kept entry changes nothing and is skipped (which also
+        // keeps -inf - (-inf) out of the exponent)
+        float d[8];
+        if constexpr (TOPK) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kept[i] = !TOPK || tv[i] >= tau;
-            tk[i] = kept[i] ? tv[i] : -__builtin_inff();
-            sk[i] = kept[i] ? sv[i] : -__builtin_inff();
+            for (int i = 0; i < 8; ++i) {
+                d[i] = tv[i] - sv[i];
+                const bool kept = tv[i] >= tau;
+                tv[i] = kept ? tv[i] : -__builtin_inff();
+                sv[i] = kept ? sv[i] : -__builtin_inff();
+            }
         }
+        const float tmax = max8(tv);
+        if (TOPK && tmax == -__builtin_inff()) continue;
         // c > 0: the max of the scaled logits is the scaled max
-        const float nmt = maxnan(mt, max8(tk) * c);
-        const float nms = maxnan(ms, max8(sk) * c);
+        const float nmt = maxnan(mt, tmax * c);
+        const float nms = maxnan(ms, max8(sv) * c);
         // equal maxima (also both -inf) need no rescaling
         const float ft = nmt == mt ? 1.0f : exp2_hw(mt - nmt);
         const float fs = nms == ms ? 1.0f : exp2_hw(ms - nms);
@@ -201,8 +209,7 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         for (int i = 0; i < 8; ++i) {
             pt[i] = exp2_hw(__builtin_fmaf(tv[i], c, -mt));
             ps[i] = exp2_hw(__builtin_fmaf(sv[i], c, -ms));
-            if (TOPK) { pt[i] = kept[i] ? pt[i] : 0.0f; ps[i] = kept[i] ? ps[i] : 0.0f; }
-            pa = __builtin_fmaf(pt[i], tv[i] - sv[i], pa);
+            pa = __builtin_fmaf(pt[i], TOPK ? d[i] : tv[i] - sv[i], pa);
         }
         zt = zt * ft + sum8(pt);
         at = at * ft + pa;
