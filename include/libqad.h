@@ -115,6 +115,19 @@ const char* qad_status_string(qad_status_t status);
 /* Version of this ABI (incremented on any incompatible change). */
 int qad_abi_version(void);
 
+/* Bound on the device-side waits of the one-pass kernels, in microseconds of
+ * wall clock (default 20000).  The dynamic quantizers (nvfp4_quantize,
+ * nvfp4_qdq_fwd, fp8_quantize and the W4A4 linear when a tensor fits on chip)
+ * and the KL segment kernels (rows of more than 16384 logits) exchange
+ * partial results between workgroups that are resident together; a workgroup
+ * whose wait reaches the bound computes what it waited for from the inputs
+ * itself, with the same arithmetic, so results never depend on the bound --
+ * only the time does, when other work keeps workgroups from being resident.
+ * 0 makes every wait give up at once (which exercises those paths).  Applies
+ * to calls made after it, process-wide; us < 0 only queries.  Returns the
+ * previous bound.  Host-only, never fails. */
+int64_t qad_set_wait_limit_us(int64_t us);
+
 /* Bytes of workspace entry point `op` needs for B tensors of R x C elements
  * of either dtype (for QAD_OP_KL: R token rows of C vocabulary logits).
  * Always a multiple of 256.  Returns 0 for invalid sizes (the entry point

@@ -9,4 +9,4 @@ from ._lib import (QAD_BF16, QAD_F32, QAD_OP_AMAX, QAD_OP_KL, QAD_OP_KL_TOPK, QA
                    QAD_OP_MSE_CALIBRATE, QAD_OP_QUANTIZE, QadError, fp8_quantize, lib, nvfp4_amax, nvfp4_mse_calibrate,
                    nvfp4_qdq_bwd, nvfp4_qdq_bwd_clipped, nvfp4_qdq_fwd, nvfp4_quantize, qad_check_finite,
                    qad_kl_fwd_bwd, qad_kl_topk_fwd_bwd, qad_kl_topp_fwd_bwd, qad_w4a4_linear_bwd, qad_w4a4_linear_fwd,
-                   qad_workspace_bytes, workspace)
+                   qad_workspace_bytes, set_wait_limit_us, workspace)

@@ -27,6 +27,7 @@ _vp, _i64, _f32, _i32, _sz, _int = C.c_void_p, C.c_int64, C.c_float, C.c_int32, 
 SIGNATURES = {
     "qad_status_string": (C.c_char_p, [_int]),
     "qad_abi_version": (_int, []),
+    "qad_set_wait_limit_us": (_i64, [_i64]),
     "qad_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -147,6 +148,13 @@ def _logits(teacher: torch.Tensor, student: torch.Tensor):
         raise ValueError("teacher and student must both be [tokens, vocab]")
     tokens, vocab = teacher.shape
     return tokens, vocab, teacher.device
+
+
+def set_wait_limit_us(us: int) -> int:
+    """Bound of the one-pass kernels' device-side waits in microseconds
+    (default 20000; 0: every wait gives up at once and the workgroup computes
+    what it waited for itself; negative: query).  Returns the previous bound."""
+    return int(lib().qad_set_wait_limit_us(int(us)))
 
 
 def qad_workspace_bytes(op: int, B: int, R: int, C_: int) -> int:

@@ -39,7 +39,6 @@ constexpr int kSegThreads = QAD_KL_THREADS; // lanes per segment workgroup
 constexpr int kSegUnits = QAD_KL_UNITS;     // 8-element units per lane, row and tensor
 constexpr int64_t kSegSpan = (int64_t)kSegThreads * kSegUnits; // units per segment
 constexpr int kMaxSegments = 64;           // longer rows take the two-pass kernel
-constexpr uint64_t kWaitTicks = 2000000;   // bounded wait (20 ms at 100 MHz)
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
@@ -247,7 +246,7 @@ __device__ __forceinline__ void publish(uint64_t* rec64, int seg, const Stats& s
 
 // Wave 0 waits (bounded) for all W segment states of a row and copies them to
 // `seg`; returns, to every lane of the workgroup, whether they all arrived.
-__device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg, uint32_t* flag)
+__device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg, uint32_t* flag, uint64_t wait_ticks)
 {
     const int tid = threadIdx.x;
     if (tid < 64) {
@@ -269,7 +268,7 @@ __device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg
             done = __all(mine_done);
             if (done) break;
             __builtin_amdgcn_s_sleep(2);
-            if (wall_clock64() - t0 > kWaitTicks) break;
+            if (wall_clock64() - t0 > wait_ticks) break;
         }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -341,7 +340,7 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
     Stats row_st = my_seg;
     if (W > 1) {
         const uint64_t* rec64 = reinterpret_cast<const uint64_t*>(rec_base + row * rec_words(W));
-        if (!collect(rec64, W, sh.seg_stats, &sh.flag)) {
+        if (!collect(rec64, W, sh.seg_stats, &sh.flag, a.wait_ticks)) {
             // timed out: compute every segment's state here, with the same
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {

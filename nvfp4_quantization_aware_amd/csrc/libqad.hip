@@ -5,9 +5,22 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "qad_internal.h"
 
 using qad::QuantizeArgs;
+
+namespace {
+
+// bound of the kernels' device-side waits, in microseconds (default 20 ms)
+std::atomic<int64_t> g_wait_us{20000};
+
+} // namespace
+
+namespace qad {
+uint64_t wait_ticks() { return (uint64_t)g_wait_us.load(std::memory_order_relaxed) * 100u; }
+} // namespace qad
 
 namespace {
 
@@ -112,6 +125,7 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
     a.tscale_out = tscale_out;
     a.y = static_cast<uint16_t*>(y);
     a.fp8 = fp8;
+    a.wait_ticks = qad::wait_ticks();
     if (frozen) return hip_status(qad::launch_quantize(a, qad::QUANT_FROZEN, nullptr, s));
     // dynamic scales: one pass when every chunk of a tensor can be resident at
     // once, otherwise an amax pass first
@@ -142,6 +156,13 @@ const char* qad_status_string(qad_status_t status)
 }
 
 int qad_abi_version(void) { return 1; }
+
+int64_t qad_set_wait_limit_us(int64_t us)
+{
+    if (us < 0) return g_wait_us.load(std::memory_order_relaxed);
+    if (us > (int64_t)1 << 40) us = (int64_t)1 << 40;   // keeps the tick count far from overflow
+    return g_wait_us.exchange(us, std::memory_order_relaxed);
+}
 
 size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
 {
@@ -318,6 +339,7 @@ qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_
     a.loss_out = loss_out;
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
+    a.wait_ticks = qad::wait_ticks();
     return hip_status(qad::launch_kl(a, workspace, hs(stream)));
 }
 
@@ -358,6 +380,7 @@ qad_status_t qad_kl_topk_fwd_bwd(const void* teacher, const void* student, qad_d
     a.loss_out = loss_out;
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
+    a.wait_ticks = qad::wait_ticks();
     return hip_status(qad::launch_kl_topk(a, k, workspace, hs(stream)));
 }
 
@@ -404,6 +427,7 @@ qad_status_t qad_kl_topp_fwd_bwd(const void* teacher, const void* student, qad_d
     a.loss_out = loss_out;
     a.grad = grad_student;
     a.grad_bf16 = gt == QAD_BF16;
+    a.wait_ticks = qad::wait_ticks();
     return hip_status(qad::launch_kl_topp(a, top_p, tau_out, workspace, hs(stream)));
 }
 

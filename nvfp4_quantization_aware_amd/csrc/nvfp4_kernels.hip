@@ -26,9 +26,9 @@ constexpr float kRcp6 = 0x1.555556p-3f;
 // range); smaller ones take IEEE division everywhere.
 constexpr float kFastMinScale = 0x1p-80f;
 constexpr int kQThreads = 256;
-// A bounded wait: after this many wall-clock ticks (20 ms at the 100 MHz
-// counter) a workgroup stops waiting and computes what it waited for itself.
-constexpr uint64_t kWaitTicks = 2000000;
+// The one-pass wait is bounded: after QuantizeArgs::wait_ticks ticks of the
+// 100 MHz wall clock (20 ms by default) a workgroup stops waiting and
+// computes what it waited for itself.
 
 __device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
 __device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
             uint32_t w;
             while (!((w = a_load(rec.slot(j))) & 0x80000000u)) {
                 __builtin_amdgcn_s_sleep(8);
-                if (wall_clock64() - t0 > kWaitTicks) break;
+                if (wall_clock64() - t0 > a.wait_ticks) break;
             }
             sh_amax = w;
         }

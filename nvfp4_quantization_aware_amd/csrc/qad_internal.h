@@ -45,6 +45,7 @@ struct QuantizeArgs {
     float* tscale_out;
     uint16_t* y;
     bool fp8 = false;          // FP8 (E4M3) per-tensor QDQ: no block scales, codes one byte per element
+    uint64_t wait_ticks = 0;   // bound of the one-pass amax wait (100 MHz ticks), from wait_ticks()
 };
 enum { QUANT_FROZEN = 0, QUANT_AMAX_GIVEN = 1, QUANT_ONE_PASS = 2 };
 // whether every chunk of one tensor can be resident at once with room to spare
@@ -93,7 +94,11 @@ struct KlArgs {
     void* grad;                // null: forward only
     bool grad_bf16;
     const float* tau = nullptr;  // teacher-top-k thresholds per row (null: full vocabulary)
+    uint64_t wait_ticks = 0;     // bound of the segment kernels' row exchange wait (100 MHz ticks)
 };
+// the process-wide bound of the kernels' device-side waits, in ticks of the
+// 100 MHz wall clock (qad_set_wait_limit_us)
+uint64_t wait_ticks();
 // scratch of launch_kl: per-row losses, then per-row exchange records
 size_t kl_workspace_bytes(int64_t tokens, int64_t vocab);
 hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream);

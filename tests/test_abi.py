@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -372,3 +372,17 @@ def test_binding_rejects_host_tensors():
             f()
     with pytest.raises(TypeError):
         q.nvfp4_quantize(np.zeros((4, 32), np.float32))
+
+
+def test_wait_limit_setting(L):
+    # host-only: the bound of the one-pass kernels' device waits
+    prev = L.qad_set_wait_limit_us(-1)
+    assert prev == 20000                       # default 20 ms
+    try:
+        assert L.qad_set_wait_limit_us(0) == 20000
+        assert L.qad_set_wait_limit_us(-5) == 0  # query only
+        assert q.set_wait_limit_us(1 << 50) == 0
+        assert q.set_wait_limit_us(-1) == 1 << 40  # clamped
+    finally:
+        L.qad_set_wait_limit_us(prev)
+    assert q.set_wait_limit_us(-1) == 20000
