@@ -386,3 +386,26 @@ def test_wait_limit_setting(L):
     finally:
         L.qad_set_wait_limit_us(prev)
     assert q.set_wait_limit_us(-1) == 20000
+
+
+def test_plain_c_client(L, tmp_path):
+    # the header is plain C (C99, no HIP include) and the library links into
+    # a C program; host-only calls need no GPU
+    import subprocess
+    src = tmp_path / "client.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <string.h>\n#include "libqad.h"\n'
+        "int main(void) {\n"
+        "  if (qad_abi_version() != 1) return 1;\n"
+        '  if (strncmp(qad_status_string(QAD_ERR_SHAPE), "QAD_ERR_SHAPE", 13) != 0) return 2;\n'
+        "  if (qad_workspace_bytes(QAD_OP_QUANTIZE, 1, 64, 64) % 256 != 0) return 3;\n"
+        "  if (qad_set_wait_limit_us(-1) != 20000) return 4;\n"
+        "  if (nvfp4_quantize(NULL, QAD_BF16, 1, 4, 24, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL)\n"
+        "      != QAD_ERR_SHAPE) return 5;\n"
+        '  printf("ok\\n");\n  return 0;\n}\n')
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lqad", "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr)
