@@ -992,8 +992,10 @@ __global__ __launch_bounds__(kTopThreads) void kl_topp_tau_kernel(const void* te
 // counts live in LDS as 16-bit halves of 32768 words (128 KiB; ds_add without
 // return).  A half that passes 65535 carries into its neighbour or out of
 // the word, which can only lower the sum of all halves, so a sum different
-// from the row length (more than 65535 equal logits in the row) sends the
-// workgroup to the streaming radix rounds instead.
+// from the row length (more than 65535 equal logits in the row) leaves the
+// row's threshold NaN, and the radix kernel launched next redoes exactly
+// those rows.  The per-row scan of the counts is spread over the whole
+// workgroup (a row's distinct values crowd into the keys of a few lanes).
 // ---------------------------------------------------------------------------
 constexpr int kSelWords = 32768;        // two 16-bit counters per word
 constexpr int kSelKeysPerLane = 65536 / kTopThreads;
@@ -1016,9 +1018,7 @@ __device__ __forceinline__ uint32_t sel_count(const uint32_t* hist, uint32_t key
     return (hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
 }
 
-// TOPP: nucleus of mass top_p (top_p >= 1: the smallest key); else the k-th
-// largest.  Returns the threshold key of the row.
-// count the 16 teacher keys of two units into the histogram
+// count the 8 teacher keys of one unit (16 bytes of bf16) into the histogram
 __device__ __forceinline__ void sel_count_unit(uint32_t* hist, const v4u& v)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
