@@ -119,17 +119,29 @@ class Workload:
         rec(7)
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the KL kernels' sources as code: comments removed and
+    whitespace collapsed, so that only a change to the code itself counts."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "nvfp4_quantization_aware_amd", "csrc")
+    parts = []
+    for n in ("kl_kernels.hip", "qad_device.h", "qad_internal.h"):
+        t = open(os.path.join(csrc, n)).read()
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        parts.append(" ".join(t.split()).encode())
+    return hashlib.sha256(b"".join(parts)).hexdigest()
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel's sources changed since it was taken."""
-    import hashlib
+    summary, or None when the kernel's code changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "kl_seg_bf16_kernel_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    csrc = os.path.join(ROOT, "nvfp4_quantization_aware_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, n), "rb").read() for n in ("kl_kernels.hip", "qad_device.h", "qad_internal.h"))
-    if rec.get("kernel") != kernel or rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("kernel") != kernel or rec.get("code_sha256") != kernel_source_digest():
         return None
     return rec["traffic_bytes"]
 
