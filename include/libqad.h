@@ -67,10 +67,11 @@
  *  - Results are deterministic: the same inputs give bitwise-equal outputs
  *    (the W4A4 linear: within a process, once its GEMM plan for the shape
  *    is chosen; see qad_w4a4_linear_fwd).
- *  - Thread-safe.  The only state kept across calls is per-device and
- *    written once: the compute-unit count and the quantizer's occupancy
- *    (atomics), and for the W4A4 linear a hipBLASLt handle and its GEMM
- *    plans (under a mutex).  Calls only enqueue kernels on `stream` (no
+ *  - Thread-safe.  The state kept across calls: per device and written
+ *    once, the compute-unit count and the quantizer's occupancy (atomics)
+ *    and for the W4A4 linear a hipBLASLt handle and its GEMM plans (under a
+ *    mutex); process-wide, the wait bound of qad_set_wait_limit_us (an
+ *    atomic).  Calls only enqueue kernels on `stream` (no
  *    memset, no allocation, no host synchronisation; qad_check_finite
  *    excepted), so a sequence of calls can be captured into a HIP graph.
  */

@@ -1,6 +1,7 @@
 // C-ABI entry points of libqad: argument validation, workspace layout and
 // launch sequencing.  Declarations, ownership and error rules:
-// include/libqad.h.  Nothing here allocates device memory or keeps state.
+// include/libqad.h.  Nothing here allocates device memory; the one setting
+// kept is the bound of the kernels' device-side waits (an atomic).
 #include "libqad.h"
 
 #include <math.h>
