@@ -2,8 +2,8 @@
 
 The kept set of a row is every entry whose teacher logit is at least the k-th
 largest (ties kept); both softmaxes are renormalised over it and the gradient
-is exactly 0 elsewhere.  Tolerances as for the full-vocabulary KL: mean loss
-1e-5 relative, per-row loss 1e-5 relative + 1e-6 absolute, gradient per row
+is exactly 0 elsewhere.  Tolerances as for the full-vocabulary KL: mean and
+per-row loss 1e-5 relative + 1e-6 nats absolute, gradient per row
 within 1e-5 of the row's largest reference magnitude (plus half a bf16 ulp
 for a bf16 gradient; where a row's reference gradient is 0 everywhere, as
 with a single kept entry, grad_scale / T stands in for that magnitude; where
@@ -47,7 +47,7 @@ def run_and_check(dev, orc, t, s, k, T, g_dt, label, grad_scale=None):
     th, sh = host(t), host(s)
     ref_loss, ref_rows, ref_g, cnt = orc.kl_topk_fwd_bwd(th, sh, k, T=T, grad_scale=grad_scale)
     loss = float(host(loss)[0])
-    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-7, (loss, ref_loss)
+    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-6, (loss, ref_loss)
     rr = host(rows).astype(np.float64)
     assert np.all(np.abs(rr - ref_rows) <= 1e-5 * np.abs(ref_rows) + 1e-6)
     if g is not None:

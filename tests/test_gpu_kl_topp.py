@@ -10,7 +10,7 @@ require the identical threshold wherever the oracle's decision margin
 exceeds 1e-5; elsewhere the library's threshold must be a valid nucleus
 boundary within 1e-5 (checked with the oracle's binary64 masses).  On the
 set the library chose, loss and gradient follow the rules of the top-k KL:
-mean loss 1e-5 relative, per-row loss 1e-5 relative + 1e-6 absolute,
+mean and per-row loss 1e-5 relative + 1e-6 nats absolute,
 gradient within 1e-5 of the row's largest reference magnitude (plus half a
 bf16 ulp for a bf16 gradient; grad_scale / T stands in for a row whose
 reference gradient is 0 everywhere; floored at 1e-6 of the largest
@@ -75,7 +75,7 @@ def run_and_check(dev, orc, t, s, top_p, T, g_dt, label, grad_scale=None):
         ref_rows[r], ref_g[r] = rr[0], gr[0]
     ref_loss = float(ref_rows.mean())
     loss = float(host(loss)[0])
-    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-7, (loss, ref_loss)
+    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-6, (loss, ref_loss)
     rr = host(rows).astype(np.float64)
     assert np.all(np.abs(rr - ref_rows) <= 1e-5 * np.abs(ref_rows) + 1e-6)
     kept = tv >= tg[:, None]

@@ -109,7 +109,7 @@ def test_kl_sweep(dev, orc, case):
     loss, rows, g = q.qad_kl_fwd_bwd(t.to(dev), s.to(dev), temperature=T, grad_dtype=g_dt, row_loss=True)
     torch.cuda.synchronize()
     ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
-    assert abs(float(host(loss)[0]) - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-7, case
+    assert abs(float(host(loss)[0]) - ref_loss) <= 1e-5 * abs(ref_loss) + 1e-6, case
     rr = host(rows).astype(np.float64)
     assert np.all(np.abs(rr - ref_rows) <= 1e-5 * np.abs(ref_rows) + 1e-6), case
     # near one-hot rows (low T, wide logits) make the gradient a small
