@@ -4,7 +4,10 @@ generator, each case checked by the same rules as the focused tests (codes,
 scales, tensor scales and QDQ outputs bit for bit; KL within the 1e-5 rules).
 They look for edge cases the hand-picked shapes miss: ragged tails at every
 offset, vocabularies on both sides of segment boundaries, tensor scales from
-2^-100 to 2^100 (both division paths), sparse tensors, exact ties.
+2^-100 to 2^100 (both division paths), sparse tensors, exact ties.  The
+top-k / top-p cases go through those tests' own checkers (random k, top_p,
+temperature, dtypes, tie-heavy teachers; case 16 is a single row whose KL is
+near 0).
 """
 import numpy as np
 import pytest
@@ -13,6 +16,8 @@ import torch
 import nvfp4_quantization_aware_amd as q
 from nvfp4_quantization_aware_amd import synth
 from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
+import test_gpu_kl_topk
+import test_gpu_kl_topp
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +142,27 @@ def test_clipped_ste_sweep(dev, orc, case):
     for b in range(B):
         ref, _ = orc.nvfp4_qdq_bwd_clipped(gyh[b].ravel(), xh[b].ravel(), sc[b].ravel(), float(ts[b]))
         assert np.array_equal(gh[b].ravel(), ref), (case, b)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_topk_topp_sweep(dev, orc, case):
+    rng = np.random.default_rng(9000 + case)
+    tokens = int(rng.integers(1, 40))
+    if case % 3 == 0:
+        vocab = 16384 * int(rng.integers(1, 4)) + 8 * int(rng.integers(-2, 3))
+    else:
+        vocab = 8 * int(rng.integers(1, 6000))
+    vocab = max(vocab, 8)
+    T = float(rng.choice([0.5, 1.0, 2.0]))
+    in_dt = [torch.bfloat16, torch.float32][case % 2]
+    g_dt = [torch.bfloat16, torch.float32][(case // 2) % 2]
+    t, s = synth.logits_bf16(tokens=tokens, vocab=vocab, teacher_std=float(rng.uniform(0.5, 6)), seed=9000 + case)
+    if case % 5 == 4:   # tie-heavy teacher on a coarse grid
+        t = (torch.round(t.float() * 2) / 2).to(torch.bfloat16)
+    t, s = t.to(in_dt), s.to(in_dt)
+    if case % 2 == 0:
+        k = int(rng.integers(1, vocab + 3))
+        test_gpu_kl_topk.run_and_check(dev, orc, t, s, k, T, g_dt, "sweep %d" % case)
+    else:
+        p = float(rng.choice([1e-4, 0.1, 0.5, 0.9, 0.99, 1.0])) if case % 7 else float(rng.uniform(0.01, 1.0))
+        test_gpu_kl_topp.run_and_check(dev, orc, t, s, p, T, g_dt, "sweep %d" % case)
