@@ -18,6 +18,7 @@ from nvfp4_quantization_aware_amd import synth
 from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
 import test_gpu_kl_topk
 import test_gpu_kl_topp
+import test_gpu_linear
 
 pytestmark = pytest.mark.gpu
 
@@ -166,3 +167,39 @@ def test_topk_topp_sweep(dev, orc, case):
     else:
         p = float(rng.choice([1e-4, 0.1, 0.5, 0.9, 0.99, 1.0])) if case % 7 else float(rng.uniform(0.01, 1.0))
         test_gpu_kl_topp.run_and_check(dev, orc, t, s, p, T, g_dt, "sweep %d" % case)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_mse_calibrate_sweep(dev, orc, case):
+    # random shapes, dtypes, candidate counts and k ranges (the grid kept no
+    # coarser than k_min/16 per step, as the library requires), magnitudes
+    # from 2^-40 to 2^40 with outlier columns; every scale compared
+    rng = np.random.default_rng(7000 + case)
+    B, R, C = int(rng.integers(1, 4)), int(rng.integers(1, 120)), 16 * int(rng.integers(1, 200))
+    dt = [torch.bfloat16, torch.float32][case % 2]
+    n = int(rng.choice([1, 2, 16, 64, 128]))
+    kmin = float(rng.choice([0.25, 0.5, 0.75, 0.9]))
+    kmax = 1.0 if n > 1 else kmin
+    if n > 1 and (kmax - kmin) / (n - 1) > kmin / 16:
+        n = int(np.ceil((kmax - kmin) * 16 / kmin)) + 1
+    x = torch.from_numpy(rng.standard_normal((B, R, C)).astype(np.float32) * float(2.0 ** rng.uniform(-40, 40)))
+    x[..., ::int(rng.integers(3, 50))] *= float(rng.uniform(1, 40))
+    x = x.to(dt)
+    announce("mse sweep case %d B=%d R=%d C=%d %s n=%d k=[%g,%g]" % (case, B, R, C, dt, n, kmin, kmax))
+    sc, ts = q.nvfp4_mse_calibrate(x.to(dev), n, kmin, kmax)
+    torch.cuda.synchronize()
+    xh = host(x)
+    for b in range(B):
+        rs, rt = orc.mse_calibrate(xh[b], n, kmin, kmax)
+        assert host(ts)[b] == np.float32(rt), (case, b)
+        assert np.array_equal(host(sc)[b].reshape(rs.shape), rs), (case, b)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_linear_sweep(dev, orc, case):
+    # random M, N, K through the W4A4 linear's own checker; every fourth with
+    # the oracle's MSE-calibrated weight scales frozen
+    rng = np.random.default_rng(8000 + case)
+    M, N, K = int(rng.integers(1, 700)), int(rng.integers(1, 700)), 16 * int(rng.integers(1, 80))
+    dt = [torch.bfloat16, torch.float32][case % 2]
+    test_gpu_linear.run_case(dev, orc, M, N, K, dt, seed=8000 + case, frozen=case % 4 == 3)
