@@ -1037,19 +1037,26 @@ template <bool TOPP>
 __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, SelShared& sh)
 {
     const int tid = threadIdx.x;
-    // lane l owns the kSelKeysPerLane keys below 65536 - kSelKeysPerLane l
-    // (32 words); order-free passes over them start at a lane-dependent word
-    // so that the lanes of a wave read different LDS banks
+    // lane l owns the kSelKeysPerLane keys below 65536 - kSelKeysPerLane l:
+    // 32 words, contiguous and 128-byte aligned, read as eight 16-byte
+    // vectors starting at a lane-dependent one so that the lanes of a wave
+    // spread over the LDS banks
     constexpr int kWordsPerLane = kSelKeysPerLane / 2;
+    static_assert(kWordsPerLane == 32, "eight 16-byte reads per lane");
     const uint32_t hi = 65535u - (uint32_t)tid * kSelKeysPerLane;
     const uint32_t whi = hi >> 1;
-    auto word_at = [&](int b) { return whi - (uint32_t)((b + tid) & (kWordsPerLane - 1)); };
-    uint32_t local = 0, nz = 0;   // nz: the lane's words holding any count
-#pragma unroll 8
-    for (int b = 0; b < kWordsPerLane; ++b) {
-        const uint32_t w = sh.c.hist[word_at(b)];
-        local += (w & 0xFFFFu) + (w >> 16);
-        nz |= (w != 0u ? 1u : 0u) << b;
+    const v4u* lane_words = reinterpret_cast<const v4u*>(sh.c.hist) + (whi - 31u) / 4u;
+    uint32_t local = 0, nz = 0;   // nz bit o: word whi - o holds a count
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t cc = (uint32_t)(c + tid) & 7u;
+        const v4u v = lane_words[cc];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            local += (w[i] & 0xFFFFu) + (w[i] >> 16);
+            nz |= (w[i] != 0u ? 1u : 0u) << (31u - (4u * cc + (uint32_t)i));
+        }
     }
     const uint32_t incl = block_incl_scan(local, sh.c.wave_tot);
     if (tid == kTopThreads - 1) sh.c.total = incl;
@@ -1073,15 +1080,13 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
         __syncthreads();
         return sh.c.key;
     } else {
-        // the largest (smallest for top_p >= 1) key present.  Bit b of nz is
-        // word whi - ((b + tid) & 31); rotated by tid, bit o is word whi - o,
-        // so the lane's highest (lowest) counted word is one count of zeros
-        // away, and one read of it picks the key inside.
+        // the largest (smallest for top_p >= 1) key present.  Bit o of nz is
+        // word whi - o, so the lane's highest (lowest) counted word is one
+        // count of zeros away, and one read of it picks the key inside.
         const bool want_min = top_p >= 1.0f;
-        const uint32_t rot = __builtin_rotateleft32(nz, (uint32_t)tid & (kWordsPerLane - 1));
         uint32_t e = want_min ? 0xFFFFFFFFu : 0u;
-        if (rot) {
-            const uint32_t o = want_min ? 31u - (uint32_t)__builtin_clz(rot) : (uint32_t)__builtin_ctz(rot);
+        if (nz) {
+            const uint32_t o = want_min ? 31u - (uint32_t)__builtin_clz(nz) : (uint32_t)__builtin_ctz(nz);
             const uint32_t wi = whi - o, w = sh.c.hist[wi];
             e = want_min ? ((w & 0xFFFFu) ? 2u * wi : 2u * wi + 1u) : ((w >> 16) ? 2u * wi + 1u : 2u * wi);
         }
