@@ -1193,17 +1193,12 @@ __global__ __launch_bounds__(kTopThreads) void kl_sel16_kernel(const void* teach
             if (bi + 1 < nbatch) load_batch(row, bi + 1, nxt);
             else load_batch(row + gridDim.x, 0, nxt);
             // unrolled, the batch's units are read straight from registers
-            // (a rolled loop indexes them dynamically); top-p's scan leaves
-            // no registers for that, so it keeps the rolled loop
-            if constexpr (!TOPP) {
+            // (a rolled loop indexes them dynamically, one move per word);
+            // for top-p this adds spills in the per-row scan, which cost
+            // less than the indexing in the counting loop did
 #pragma unroll
-                for (int q = 0; q < kSelBatch; ++q)
-                    if ((int64_t)bi * per_batch + (int64_t)q * kTopThreads + tid < units) sel_count_unit(sh.c.hist, cur[q]);
-            } else {
-#pragma unroll 1
-                for (int q = 0; q < kSelBatch; ++q)
-                    if ((int64_t)bi * per_batch + (int64_t)q * kTopThreads + tid < units) sel_count_unit(sh.c.hist, cur[q]);
-            }
+            for (int q = 0; q < kSelBatch; ++q)
+                if ((int64_t)bi * per_batch + (int64_t)q * kTopThreads + tid < units) sel_count_unit(sh.c.hist, cur[q]);
 #pragma unroll
             for (int q = 0; q < kSelBatch; ++q) cur[q] = nxt[q];
         }
