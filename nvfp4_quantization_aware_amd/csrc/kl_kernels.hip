@@ -1013,6 +1013,28 @@ struct alignas(16) SelShared {
     } c;
 };
 
+// This kernel's keys: 0x8000 plus the bf16's sign-magnitude bits read as a
+// two's-complement integer (order-preserving; -0 and +0 both give 0x8000;
+// finite values give 1 .. 0xFFFF), a few integer operations without compares.
+// Only threshold values leave the kernel, so its keys need not match the
+// radix kernels' ones.
+__device__ __forceinline__ uint32_t sel_key_lo(uint32_t w)   // the bf16 in bits 0..15
+{
+    const int32_t mag = (int32_t)(w & 0x7FFFu), s = (int32_t)(w << 16) >> 31;
+    return (uint32_t)(((mag ^ s) - s) + 0x8000);
+}
+__device__ __forceinline__ uint32_t sel_key_hi(uint32_t w)   // the bf16 in bits 16..31
+{
+    const int32_t mag = (int32_t)((w >> 16) & 0x7FFFu), s = (int32_t)w >> 31;
+    return (uint32_t)(((mag ^ s) - s) + 0x8000);
+}
+__device__ __forceinline__ float sel_value(uint32_t key)
+{
+    const int32_t v = (int32_t)key - 0x8000;
+    const uint32_t h = v >= 0 ? (uint32_t)v : (0x8000u | (uint32_t)(-v));
+    return as_f(h << 16);
+}
+
 __device__ __forceinline__ uint32_t sel_count(const uint32_t* hist, uint32_t key)
 {
     return (hist[key >> 1] >> ((key & 1u) * 16u)) & 0xFFFFu;
@@ -1024,9 +1046,9 @@ __device__ __forceinline__ void sel_count_unit(uint32_t* hist, const v4u& v)
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t k0 = key16(w[i] & 0xFFFFu), k1 = key16(w[i] >> 16);
-        atomicAdd(&hist[k0 >> 1], 1u << ((k0 & 1u) * 16u));
-        atomicAdd(&hist[k1 >> 1], 1u << ((k1 & 1u) * 16u));
+        const uint32_t k0 = sel_key_lo(w[i]), k1 = sel_key_hi(w[i]);
+        atomicAdd(&hist[k0 >> 1], 1u + (k0 & 1u) * 0xFFFFu);   // 1 or 1 << 16
+        atomicAdd(&hist[k1 >> 1], 1u + (k1 & 1u) * 0xFFFFu);
     }
 }
 
@@ -1110,10 +1132,10 @@ __device__ uint32_t sel16_key(int64_t vocab, uint32_t k, float top_p, float c, S
             groups |= sh.c.wave_grp[i];
         }
         if (want_min) return e;
-        const float m = value_of_key<true>(e) * c;
+        const float m = sel_value(e) * c;
         // fixed-point mass of each key: count x floor(2^(c v - m) 2^40)
         auto key_mass = [&](uint32_t key, uint32_t n) {
-            return fix40(exp2_hw(__builtin_fmaf(value_of_key<true>(key), c, -m))) * n;
+            return fix40(exp2_hw(__builtin_fmaf(sel_value(key), c, -m))) * n;
         };
         // The mass of each lane's 32 words.  The distinct values of a row
         // crowd into a few thousand neighbouring keys, the words of a few
@@ -1206,7 +1228,7 @@ __global__ __launch_bounds__(kTopThreads) void kl_sel16_kernel(const void* teach
         const uint32_t key = sel16_key<TOPP>(vocab, k, top_p, c, sh);
         // a counter overflowed (more than 65535 equal logits): NaN marks the
         // row for the streaming radix kernels launched after this one
-        if (tid == 0) tau_out[row] = key == 0xFFFFFFFFu ? __builtin_nanf("") : value_of_key<true>(key);
+        if (tid == 0) tau_out[row] = key == 0xFFFFFFFFu ? __builtin_nanf("") : sel_value(key);
         __syncthreads();
         for (int i = tid; i < kSelWords / 4; i += kTopThreads)
             reinterpret_cast<v4u*>(sh.c.hist)[i] = v4u{0u, 0u, 0u, 0u};
