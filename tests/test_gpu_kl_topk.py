@@ -116,14 +116,30 @@ def test_topk_rows_of_changing_scale(dev, orc, k):
     run_and_check(dev, orc, t, s, k, 1.0, torch.bfloat16, "changing row scale")
 
 
-def test_topk_signed_zero_ties(dev, orc):
-    # -0 and +0 are equal teacher logits: both are kept when zero is the k-th value
+@pytest.mark.parametrize("in_dt", [torch.float32, torch.bfloat16])
+def test_topk_signed_zero_ties(dev, orc, in_dt):
+    # -0 and +0 are equal teacher logits: both are kept when zero is the k-th
+    # value (bf16 teachers take the key-count kernel, fp32 ones the radix rounds)
     t = torch.zeros(2, 64, dtype=torch.float32)
     t[:, :10] = torch.arange(1, 11, dtype=torch.float32)
     t[:, 20:30] = -0.0
     t[:, 40:] = -5.0
     s = torch.linspace(-1, 1, 128, dtype=torch.float32).reshape(2, 64)
-    run_and_check(dev, orc, t, s, 12, 1.0, torch.float32, "signed zeros")
+    run_and_check(dev, orc, t.to(in_dt), s.to(in_dt), 12, 1.0, torch.float32, "signed zeros")
+
+
+@pytest.mark.parametrize("k", [1, 65, 200, 448, 449, 512, 640, 1000])
+def test_topk_bf16_keys_around_zero(dev, orc, k):
+    # bf16 teachers made only of values around zero: +-denormals, +-0, +-tiny
+    # normals, each repeated 64 times, so k lands on every step of their
+    # order, across the sign and the denormal range (the key-count kernel's
+    # ordering and its -0 = +0 folding)
+    vals = np.array([3e-38, 1e-38, 2e-39, 5e-40, 1e-40, 0.0, -0.0, -1e-40, -5e-40, -2e-39, -1e-38, -3e-38,
+                     1e-3, -1e-3, 7.0, -7.0], np.float32)
+    rng = np.random.default_rng(k)
+    t = torch.from_numpy(np.stack([rng.permutation(np.repeat(vals, 64)) for _ in range(3)])).to(torch.bfloat16)
+    s = (t.float() + torch.from_numpy(rng.normal(0, 0.5, t.shape).astype(np.float32))).to(torch.bfloat16)
+    run_and_check(dev, orc, t, s, k, 1.0, torch.float32, "bf16 keys around zero")
 
 
 def test_topk_identical(dev):

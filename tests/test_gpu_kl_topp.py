@@ -136,13 +136,15 @@ def test_topp_count_overflow_rows(dev, orc, top_p):
     run_and_check(dev, orc, t, s, top_p, 1.0, torch.float32, "count overflow")
 
 
-def test_topp_signed_zero_group(dev, orc):
+@pytest.mark.parametrize("in_dt", [torch.float32, torch.bfloat16])
+def test_topp_signed_zero_group(dev, orc, in_dt):
     # -0 and +0 are one teacher value: kept together when zero is the boundary
+    # (bf16 teachers take the key-count kernel, fp32 ones the radix rounds)
     t = torch.full((2, 64), -30.0, dtype=torch.float32)
     t[:, 20:30] = -0.0
     t[:, 30:40] = 0.0
     s = torch.linspace(-1, 1, 128, dtype=torch.float32).reshape(2, 64)
-    tg, n = run_and_check(dev, orc, t, s, 0.5, 1.0, torch.float32, "signed zeros")
+    tg, n = run_and_check(dev, orc, t.to(in_dt), s.to(in_dt), 0.5, 1.0, torch.float32, "signed zeros")
     assert (tg == 0).all() and (n == 20).all()
 
 
