@@ -272,7 +272,8 @@ qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, i
  * both quantizers: grad_x[M][K] = grad_y[M][N] * wq[N][K] and
  * grad_w[N][K] = grad_y^T * xq[M][K] (bf16, fp32 accumulation).
  *   grad_y : device bf16 [M][N]; xq, wq: the forward's QDQ outputs
- *   grad_x, grad_w : device bf16 outputs, either may be NULL (not both)
+ *   grad_x, grad_w : device bf16 outputs, either may be NULL (not both,
+ *                    unless both are empty)
  *   workspace : as for the forward
  * M == 0 or N == 0 writes zeros to the other gradient. */
 qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void* wq, int64_t M, int64_t N, int64_t K,
