@@ -401,7 +401,15 @@ void orc_mse_calibrate(const void* x, int dtype, int64_t R, int64_t C,
  *   KL_row = sum_v p_v (log p_v - log q_v)   (forward KL, teacher first),
  *   loss   = mean over rows,
  *   dloss/ds_v scaled by grad_scale: (q_v - p_v) * grad_scale / T.
- * Straight definition in binary64 with the usual max subtraction.
+ * Binary64 with the usual max subtraction.  With d_v = log p_v - log q_v =
+ * (t_v - s_v)/T - (LSE_t - LSE_s) we have q_v = p_v e^-d_v, so
+ *   q_v - p_v = p_v expm1(-d_v),
+ *   KL_row    = sum_v p_v (expm1(-d_v) + d_v),
+ * the second because sum_v (q_v - p_v) = 0.  Every term of that sum is
+ * non-negative, so binary64 keeps its relative accuracy however small the
+ * divergence, and an error in the row constant LSE_t - LSE_s enters only to
+ * second order; the plain sum of p_v d_v loses ~1e-14 nats to the rounding
+ * of the log-normalisers, which is all of a divergence near 1e-10.
  * ---------------------------------------------------------------------- */
 static double load_d(const void* p, int dtype, int64_t i)
 {
@@ -427,15 +435,16 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
             zt += exp(load_d(teacher, dtype, o + v) / T - mt);
             zs += exp(load_d(student, dtype, o + v) / T - ms);
         }
-        const double lse_t = mt + log(zt), lse_s = ms + log(zs);
+        const double delta = (mt - ms) + log(zt / zs);   /* LSE_t - LSE_s */
         double kl = 0.0;
         for (int64_t v = 0; v < V; ++v) {
             double t = load_d(teacher, dtype, o + v) / T;
             double s = load_d(student, dtype, o + v) / T;
-            double logp = t - lse_t, logq = s - lse_s;
-            double p = exp(logp);
-            kl += p * (logp - logq);
-            if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
+            double d = (t - s) - delta;                     /* log p_v - log q_v */
+            double p = exp(t - mt) / zt;
+            double em = expm1(-d);                          /* q_v / p_v - 1 */
+            kl += p * (em + d);
+            if (grad) grad[o + v] = p * em * grad_scale / T;
         }
         if (row_kl) row_kl[r] = kl;
         total += kl;
@@ -453,7 +462,8 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
  *   p~, q~ = softmax(t/T), softmax(s/T) renormalised over S;
  *   row loss = sum_{v in S} p~_v (log p~_v - log q~_v);
  *   gradient = (q~_v - p~_v) * grad_scale / T on S, 0 elsewhere.
- * Binary64, straightforward: a sorted copy of the row gives tau.
+ * Binary64, evaluated as the full-vocabulary KL above (non-negative terms);
+ * a sorted copy of the row gives tau.
  * ---------------------------------------------------------------------- */
 static int cmp_desc(const void* a, const void* b)
 {
@@ -482,7 +492,7 @@ static double kl_kept_row(const void* teacher, const void* student, int dtype, i
         zt += exp(load_d(teacher, dtype, o + v) / T - mt);
         zs += exp(load_d(student, dtype, o + v) / T - ms);
     }
-    const double lse_t = mt + log(zt), lse_s = ms + log(zs);
+    const double delta = (mt - ms) + log(zt / zs);   /* LSE_t - LSE_s over S */
     double kl = 0.0;
     for (int64_t v = 0; v < V; ++v) {
         const double tv = load_d(teacher, dtype, o + v);
@@ -490,10 +500,12 @@ static double kl_kept_row(const void* teacher, const void* student, int dtype, i
             if (grad) grad[o + v] = 0.0;
             continue;
         }
-        const double logp = tv / T - lse_t, logq = load_d(student, dtype, o + v) / T - lse_s;
-        const double p = exp(logp);
-        kl += p * (logp - logq);
-        if (grad) grad[o + v] = (exp(logq) - p) * grad_scale / T;
+        const double t = tv / T, s = load_d(student, dtype, o + v) / T;
+        const double d = (t - s) - delta;
+        const double p = exp(t - mt) / zt;
+        const double em = expm1(-d);
+        kl += p * (em + d);
+        if (grad) grad[o + v] = p * em * grad_scale / T;
     }
     if (count_out) *count_out = count;
     return kl;

@@ -8,7 +8,9 @@ loss compares the two logit vectors element-wise over the vocabulary.
 
 Pins: torch's float64 kl_div + autograd (an independent library routine),
 closed forms (two-way vocabulary, uniform teacher), KL(p||p) = 0, KL >= 0,
-shift invariance, central finite differences, gradient rows summing to 0.
+shift invariance, central finite differences, gradient rows summing to 0,
+and for students a tiny perturbation away from the teacher the cumulant
+series of the divergence (relative accuracy where the divergence is ~1e-13).
 """
 import math
 
@@ -105,3 +107,37 @@ def test_config_like_magnitude(orc):
     t, s = synth.logits_bf16(tokens=4, vocab=131072, seed=5)
     loss, row, _ = orc.kl_fwd_bwd(synth.bf16_bits(t), synth.bf16_bits(s), want_grad=False)
     assert 0.08 < loss < 0.16
+
+
+@pytest.mark.parametrize("eps,T", [(1e-6, 1.0), (3e-5, 0.25), (1e-4, 2.0)])
+def test_small_divergence_cumulant_series(orc, eps, T):
+    # q = softmax((t + e)/T) with a tiny perturbation e: with
+    # delta_v = (t_v - s_v)/T and p = softmax(t/T), KL(p || q) is
+    # E_p[delta] + log E_p[exp(-delta)] = k2/2 - k3/6 + k4/24 - ..., the
+    # cumulants k_n of delta under p (computed here from central moments, a
+    # route that shares nothing with the oracle's sums).  With |delta| ~ eps
+    # the series to k4 is exact to ~eps^3 relative, and the divergence is so
+    # small (~1e-13 at eps = 1e-6) that summing p_v (log p_v - log q_v)
+    # directly loses most of its digits.
+    rng = np.random.default_rng(int(1e6 * eps))
+    t = rng.normal(0, 3, (4, 5000)).astype(np.float32)
+    s = (t.astype(np.float64) + eps * rng.normal(0, 1, t.shape)).astype(np.float32)
+    _, row, g = orc.kl_fwd_bwd(t, s, T=T, grad_scale=1.0)
+    td, sd = t.astype(np.float64) / T, s.astype(np.float64) / T
+    p = np.exp(td - td.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    delta = td - sd                    # exact: both are float32 values over a power of two
+    mu = (p * delta).sum(axis=1, keepdims=True)
+    c = delta - mu
+    m2, m3, m4 = ((p * c ** k).sum(axis=1) for k in (2, 3, 4))
+    series = m2 / 2 - m3 / 6 + (m4 - 3 * m2 ** 2) / 24
+    assert np.all(series > 0)
+    assert np.all(np.abs(row - series) <= 1e-7 * series), np.abs(row / series - 1).max()
+    # gradient: q_v - p_v = p_v (exp(-c_v) / E_p[exp(-c)] - 1), c = delta - mu,
+    # which is p_v (-c_v + (c_v^2 - m2)/2) to second order; checked to a
+    # bound of the third-order remainder plus binary64's own limit, 1e-14 p_v
+    # (the rounding of the row's normalisers shifts every log-ratio alike)
+    quad = p * (-c + (c ** 2 - m2[:, None]) / 2) / T
+    amax = np.abs(c).max(axis=1, keepdims=True)
+    rem = p * (np.abs(c) ** 3 + 3 * amax * m2[:, None] + 1e-14) / T
+    assert np.all(np.abs(g - quad) <= rem)
