@@ -44,14 +44,22 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ v4u ldnt(const void* p, int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i); }
 __device__ __forceinline__ void stnt(void* p, int64_t i, v4u v) { __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p) + i); }
 
+// A lane's (or a merged) online state: the running maxima m_t, m_s of c t
+// and c s, the sums of 2^(c t - m_t) and 2^(c s - m_s), the teacher-weighted
+// sum of t - s, and the largest s - t seen (which bounds the row's
+// log-ratios log2(q/p) for pass 2).
 struct Stats {
-    float mt, zt, at, ms, zs;
+    float mt, zt, at, ms, zs, dx;
 };
 
-__device__ __forceinline__ Stats empty_stats() { return Stats{-__builtin_inff(), 0.0f, 0.0f, -__builtin_inff(), 0.0f}; }
+__device__ __forceinline__ Stats empty_stats()
+{
+    return Stats{-__builtin_inff(), 0.0f, 0.0f, -__builtin_inff(), 0.0f, -__builtin_inff()};
+}
 
 // merge two partial (max, sum) states; equal maxima (also both -inf) need no
-// rescaling, which keeps empty partials from producing 0 * inf
+// rescaling, which keeps empty partials from producing 0 * inf.  Symmetric in
+// its operands, bit for bit.
 __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b)
 {
     Stats r;
@@ -64,13 +72,14 @@ __device__ __forceinline__ Stats merge(const Stats& a, const Stats& b)
     const float ga = a.ms == r.ms ? 1.0f : exp2_hw(a.ms - r.ms);
     const float gb = b.ms == r.ms ? 1.0f : exp2_hw(b.ms - r.ms);
     r.zs = a.zs * ga + b.zs * gb;
+    r.dx = maxnan(a.dx, b.dx);
     return r;
 }
 
 __device__ __forceinline__ Stats shfl_xor_stats(const Stats& s, int o)
 {
     return Stats{__shfl_xor(s.mt, o, 64), __shfl_xor(s.zt, o, 64), __shfl_xor(s.at, o, 64),
-                 __shfl_xor(s.ms, o, 64), __shfl_xor(s.zs, o, 64)};
+                 __shfl_xor(s.ms, o, 64), __shfl_xor(s.zs, o, 64), __shfl_xor(s.dx, o, 64)};
 }
 
 // workgroup reduction in a fixed order (xor tree in each wave, then waves in
@@ -83,6 +92,38 @@ __device__ Stats group_merge(Stats st, Stats* part)
     __syncthreads();
     Stats r = part[0];
     for (int w = 1; w < NT / 64; ++w) r = merge(r, part[w]);
+    __syncthreads();
+    return r;
+}
+
+// per-lane sums of the term-wise KL (see termwise_kl)
+struct LossAcc {
+    float l, y, p;
+};
+
+// sums of the lanes' term-wise sums over the workgroup in binary64, fixed
+// order; the result is returned to every lane
+struct LossSum {
+    double l, y, p;
+};
+
+template <int NT>
+__device__ LossSum group_sum(const LossAcc& a, LossSum* part)
+{
+    LossSum v{(double)a.l, (double)a.y, (double)a.p};
+    for (int o = 32; o > 0; o >>= 1) {
+        v.l += __shfl_xor(v.l, o, 64);
+        v.y += __shfl_xor(v.y, o, 64);
+        v.p += __shfl_xor(v.p, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    LossSum r = part[0];
+    for (int w = 1; w < NT / 64; ++w) {
+        r.l += part[w].l;
+        r.y += part[w].y;
+        r.p += part[w].p;
+    }
     __syncthreads();
     return r;
 }
@@ -118,6 +159,172 @@ __device__ __forceinline__ void unpack8(v4u w, float (&v)[8])
     v[4] = bf_lo(w.z); v[5] = bf_hi(w.z); v[6] = bf_lo(w.w); v[7] = bf_hi(w.w);
 }
 
+// ---------------------------------------------------------------------------
+// What a row's pass 2 needs, computed once per row (in binary64) from the
+// merged statistics, and the row's loss by the difference form
+//   KL = E_p[t - s]/T - (LSE_t - LSE_s),  LSE in log2 units m + log2 Z.
+// That form subtracts two terms that are large next to a small KL (a student
+// close to the teacher, or shifted from it by a constant): its binary32
+// exponentials leave ~1e-7 nats of error.  Where the KL is not large against
+// that (below 1/16 nat plus 1/16 of the two terms' magnitudes), the row's loss
+// is taken instead in pass 2, element by element, in the form
+//   KL = sum_v p_v psi(x_v),  x_v = log2(q_v / p_v),  psi(x) = 2^x - 1 - x ln 2,
+// whose terms are all non-negative (the sum of p_v (2^x_v - 1) is sum q - sum p
+// = 0), so it keeps its relative accuracy however small the KL, and whose
+// first-order sensitivity to an error in the row's LSE difference is zero.
+// ---------------------------------------------------------------------------
+constexpr double kLn2d = 0.69314718055994530942;
+constexpr double kRobustAbs = 1.0 / 16.0;   // nats
+constexpr double kRobustRel = 1.0 / 16.0;
+
+// Pass 2 takes one of three forms per row (the same in every workgroup of the
+// row, all of which hold bit-identical statistics):
+//   FORM_PLAIN  g = (P 2^x - P) 2^-40 with P = p grad_scale / T 2^40 and x =
+//               log2(q/p) from s - t: one exponential of the teacher's logit
+//               (the weight folded into its reference) and one of x; taken on
+//               rows whose largest x is at most 14, so that q <= 2^14 p and P
+//               stays a normal number wherever q is not negligible;
+//   FORM_SELECT g = +-big (1 - 2^-|x|) from the larger of p and q: any x;
+//   FORM_LOSS   FORM_SELECT, plus the row's KL term by term (rows whose KL
+//               is small next to the difference form's rounding).
+// The exponentials run above the row's references (2^kShift in the select
+// forms, 2^40 in the plain one) so that probabilities far below the largest
+// stay normal binary32 numbers (the hardware exponential flushes subnormal
+// results); the weights carry the compensating powers of two.  A shifted
+// reference may round: that scales every p (or q) of the row by the same
+// factor within 2^-20, a relative error of the gradient well inside its band,
+// and one the term-wise KL cancels (see termwise_kl).
+constexpr float kShift = 32.0f;
+constexpr double kPlainShift = 40.0;
+constexpr double kPlainMaxX = 14.0;      // FORM_PLAIN's bound on x (a margin below 16)
+enum { FORM_PLAIN = 0, FORM_SELECT = 1, FORM_LOSS = 2 };
+
+struct RowConst {
+    float mt, ms;      // select forms: row references of c t and c s, minus kShift
+    float dh;          // x = log2(q / p) = c (s - t) - dh
+    float wt, ws;      // grad_scale / T / Z_t and / Z_s, times 2^-kShift
+    float izt, izs;    // 1 / Z_t and 1 / Z_s, times 2^-kShift
+    float mtp;         // plain form: reference of c t giving p |grad_scale / T| 2^40
+    float psc;         // plain form: 2^-40 with the sign of grad_scale
+    float loss;        // the row's KL by the difference form
+    uint32_t form;
+};
+
+// log2 of a positive binary32 value as its exponent plus log2 of its
+// significand in [1, 2) (the hardware logarithm on a value near 1, so the
+// result's absolute error stays near 1e-7 whatever the magnitude)
+__device__ __forceinline__ double log2_split(float v)
+{
+    int e = 0;
+    const float m = __builtin_frexpf(v, &e);   // v = m 2^e, m in [0.5, 1)
+    return (double)(e - 1) + (double)__builtin_amdgcn_logf(2.0f * m);
+}
+
+// (one lane per workgroup; lgmul = log2 |grad_scale / T|)
+__device__ __forceinline__ RowConst row_const(const Stats& st, float c, float inv_t, float gmul, float lgmul,
+                                              bool want_grad)
+{
+    RowConst k;
+    const float izt = __builtin_amdgcn_rcpf(st.zt), izs = __builtin_amdgcn_rcpf(st.zs);
+    // log2 Z_t and log2 (Z_t / Z_s) (the quotient correctly rounded: equal sums give exactly 0)
+    const double lt = log2_split(st.zt), lr = log2_split(st.zt / st.zs);
+    const double t1 = (double)(st.at * izt) * (double)inv_t;
+    const double t2 = kLn2d * (((double)st.mt - (double)st.ms) + lr);
+    const double kl = t1 - t2;
+    const double dh = ((double)st.ms - (double)st.mt) - lr;
+    constexpr float kUnshift = 0x1p-32f;   // 2^-kShift
+    k.mt = st.mt - kShift;
+    k.ms = st.ms - kShift;
+    k.dh = (float)dh;
+    k.wt = gmul * izt * kUnshift;
+    k.ws = gmul * izs * kUnshift;
+    k.izt = izt * kUnshift;
+    k.izs = izs * kUnshift;
+    k.mtp = (float)((double)st.mt - kPlainShift - ((double)lgmul - lt));
+    k.psc = gmul < 0.0f ? -0x1p-40f : 0x1p-40f;
+    k.loss = (float)kl;
+    const bool robust = !(kl >= kRobustAbs + kRobustRel * (__builtin_fabs(t1) + __builtin_fabs(t2)));
+    // largest log2(q/p) of the row: c max(s - t) - dh
+    const bool bounded = (double)c * (double)st.dx - dh <= kPlainMaxX;
+    k.form = robust ? FORM_LOSS : (bounded || !want_grad) ? FORM_PLAIN : FORM_SELECT;
+    return k;
+}
+
+// The term-wise KL of a row from three sums over its entries, with p' the
+// probabilities as computed and x' the log-ratios as computed:
+//   L = sum p' psi(x'),  Y = sum p' x' ln 2,  P = sum p'.
+// If p' = p (1 + e_p) and x' = x + e for row constants e_p, e (the rounding
+// of Z_t and of the row's offset dh), then D = L + Y = P (2^e - 1) and
+//   KL = (L - (D - P log1p(D / P))) / P
+// exactly: the constant errors cancel to every order (alone, L would carry
+// e^2 ln^2(2) / 2, ~1e-14 nats, which is all of a KL near 1e-10).
+__host__ __device__ inline double termwise_kl(double L, double Y, double P)
+{
+    const double D = L + Y;
+    return (L - (D - P * log1p(D / P))) / P;
+}
+
+// Taylor coefficients of (e^y - 1 - y) / y^2 = 1/2! + y/3! + ... + y^6/8!
+// (binary32; for |y| <= 1/2 the truncation is below 6e-8 of the sum)
+constexpr float kPsi0 = 0.5f, kPsi1 = 1.0f / 6.0f, kPsi2 = 1.0f / 24.0f, kPsi3 = 1.0f / 120.0f,
+                kPsi4 = 1.0f / 720.0f, kPsi5 = 1.0f / 5040.0f, kPsi6 = 1.0f / 40320.0f;
+
+// Gradient of one logit pair, (q - p) grad_scale / T, from the larger of p and
+// q and the ratio r = 2^-|x| of the smaller to it:
+//   x >= 0 (q >= p):  q (1 - r) grad_scale / T,   q = 2^(c s - m_s) / Z_s
+//   x <  0 (p >  q): -p (1 - r) grad_scale / T,   p = 2^(c t - m_t) / Z_t.
+// Unlike the difference of the two separately rounded probabilities, this
+// keeps its relative accuracy where q and p nearly agree (x is computed from
+// s - t, not from two large exponents), and its rounding errors scale with
+// |q - p|.  FORM_LOSS: also adds p psi(x) to acc (the term-wise KL, nats).
+template <int FORM>
+__device__ __forceinline__ float grad_elem(float t, float s, float c, const RowConst& k, LossAcc& acc)
+{
+    if constexpr (FORM == FORM_PLAIN) {
+        const float E = exp2_hw(__builtin_fmaf(s - t, c, -k.dh));   // q / p
+        const float P = exp2_hw(__builtin_fmaf(t, c, -k.mtp));      // p |grad_scale / T| 2^40
+        return __builtin_fmaf(P, E, -P) * k.psc;
+    }
+    constexpr bool LOSS = FORM == FORM_LOSS;
+    const float x = __builtin_fmaf(s - t, c, -k.dh);
+    const bool pos = x >= 0.0f;
+    const float v = pos ? s : t, m = pos ? k.ms : k.mt;
+    const float a = __builtin_fmaf(v, c, -m);
+    float big = exp2_hw(a);
+    if constexpr (LOSS) {
+        // the exponent c v - m is exact in binary64; its remainder after the
+        // binary32 rounding a corrects 2^a to first order, so that p and q
+        // hold their relative accuracy however far below the row's maximum
+        // they are
+        const double ad = (double)v * (double)c - (double)m;
+        const float lo = (float)(ad - (double)a);
+        big = __builtin_fmaf(big, lo * kLn2, big);
+    }
+    const float r = exp2_hw(-__builtin_fabsf(x));
+    const float h = __builtin_fmaf(-big, r, big);
+    const float g = h * (pos ? k.ws : -k.wt);
+    if constexpr (LOSS) {
+        // p psi(x): as q ((1 - r) - r y) or p ((r - 1) - y) with y = x ln 2,
+        // and for |y| <= 1/2, where those cancel, as p y^2 P(y)
+        const float y = x * kLn2;
+        const float pm = big * (pos ? k.izs : k.izt);   // max(p, q)
+        const float pp = pos ? pm * r : pm;             // p
+        const float om = 1.0f - r;
+        const float dir = pos ? __builtin_fmaf(-r, y, om) : -om - y;
+        float P = __builtin_fmaf(kPsi6, y, kPsi5);
+        P = __builtin_fmaf(P, y, kPsi4);
+        P = __builtin_fmaf(P, y, kPsi3);
+        P = __builtin_fmaf(P, y, kPsi2);
+        P = __builtin_fmaf(P, y, kPsi1);
+        P = __builtin_fmaf(P, y, kPsi0);
+        const float sm = (y * y) * P * (pos ? r : 1.0f);
+        acc.l = __builtin_fmaf(pm, __builtin_fabsf(y) <= 0.5f ? sm : dir, acc.l);
+        acc.y = __builtin_fmaf(pp, y, acc.y);
+        acc.p += pp;
+    }
+    return g;
+}
+
 // One unit of 8 teacher and 8 student logits, as held in registers: one
 // 16-byte vector per tensor for bf16, two for fp32.
 template <bool BF16>
@@ -147,6 +354,37 @@ struct Unit {
     }
 };
 
+// Gradients of one unit (masked by the teacher threshold when TOPK) written
+// to `unit` of the gradient; LOSS adds the unit's term-wise KL to acc.
+template <int GRAD, bool TOPK, int FORM>
+__device__ __forceinline__ void unit_grad(const float (&tv)[8], const float (&sv)[8], float c, float tau,
+                                          const RowConst& k, const KlArgs& a, int64_t unit, LossAcc& acc)
+{
+    float g[8];
+    LossAcc ua{0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        LossAcc e{0.0f, 0.0f, 0.0f};
+        g[i] = grad_elem<FORM>(tv[i], sv[i], c, k, e);
+        if (TOPK && !(tv[i] >= tau)) { g[i] = 0.0f; e = LossAcc{0.0f, 0.0f, 0.0f}; }
+        ua.l += e.l;
+        ua.y += e.y;
+        ua.p += e.p;
+    }
+    if (FORM == FORM_LOSS) {
+        acc.l += ua.l;
+        acc.y += ua.y;
+        acc.p += ua.p;
+    }
+    if constexpr (GRAD == 1) {
+        stnt(a.grad, unit, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                               pack_bf16x2(g[6], g[7])});
+    } else if constexpr (GRAD == 2) {
+        stnt(a.grad, 2 * unit, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
+        stnt(a.grad, 2 * unit + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
+    }
+}
+
 // Opaque to the optimiser: values derived from v before this point cannot be
 // reused after it.  Used so that widened logits are recomputed from the packed
 // registers where needed instead of being kept alive (64 extra registers).
@@ -170,7 +408,7 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
 {
     constexpr int kUnroll = UNROLL ? kSegUnits : 1;
     float mt = -__builtin_inff(), ms = -__builtin_inff();
-    float zt = 0.0f, zs = 0.0f, at = 0.0f;
+    float zt = 0.0f, zs = 0.0f, at = 0.0f, dx = -__builtin_inff();
 #pragma unroll kUnroll
     for (int k = 0; k < kSegUnits; ++k) {
         const bool valid = FULL || lane_unit(seg_u0, k) < units;
@@ -184,14 +422,19 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         // with no kept entry changes nothing and is skipped (which also
         // keeps -inf - (-inf) out of the exponent)
         float d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = tv[i] - sv[i];
         if constexpr (TOPK) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                d[i] = tv[i] - sv[i];
                 const bool kept = tv[i] >= tau;
                 tv[i] = kept ? tv[i] : -__builtin_inff();
                 sv[i] = kept ? sv[i] : -__builtin_inff();
+                dx = maxnan(dx, kept ? -d[i] : -__builtin_inff());
             }
+        } else {
+            dx = maxnan(maxnan(maxnan(dx, -d[0]), maxnan(-d[1], -d[2])), maxnan(maxnan(-d[3], -d[4]), -d[5]));
+            dx = maxnan(dx, maxnan(-d[6], -d[7]));
         }
         const float tmax = max8(tv);
         if (TOPK && tmax == -__builtin_inff()) continue;
@@ -208,15 +451,15 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         for (int i = 0; i < 8; ++i) {
             pt[i] = exp2_hw(__builtin_fmaf(tv[i], c, -mt));
             ps[i] = exp2_hw(__builtin_fmaf(sv[i], c, -ms));
-            pa = __builtin_fmaf(pt[i], TOPK ? d[i] : tv[i] - sv[i], pa);
+            pa = __builtin_fmaf(pt[i], d[i], pa);
         }
         zt = zt * ft + sum8(pt);
         at = at * ft + pa;
         zs = zs * fs + sum8(ps);
         // unit by unit: later units' work is not hoisted above this point
-        if (UNROLL) asm volatile("" : "+v"(zt), "+v"(zs), "+v"(at), "+v"(mt), "+v"(ms));
+        if (UNROLL) asm volatile("" : "+v"(zt), "+v"(zs), "+v"(at), "+v"(mt), "+v"(ms), "+v"(dx));
     }
-    return Stats{mt, zt, at, ms, zs};
+    return Stats{mt, zt, at, ms, zs, dx};
 }
 
 // every lane's state over a segment held in registers
@@ -226,54 +469,75 @@ __device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_
     return lane_state<BF16, true, FULL, TOPK>(seg_u0, units, c, tau, [&](int k, Unit<BF16>& u) { u = m[k]; });
 }
 
-// per-row exchange record for W segments, in words (whole 128-byte lines)
-__host__ __device__ inline int64_t rec_words(int W) { return (10 * (int64_t)W + 31) & ~(int64_t)31; }
+// ---------------------------------------------------------------------------
+// Per-row record of the segment kernels (rec_words(W) words, whole 128-byte
+// lines, zeroed before each launch):
+//   [0, 12 W)     segment s publishes its 6 state words (Stats) at 6 s .. 6 s + 5,
+//                 each as a 64-bit {value, tag = 1} pair written by one
+//                 single-copy-atomic store (no round trip for the writer); a
+//                 reader waits until all 6 W tags are set;
+//   [12 W, 18 W)  segment s's shares of the term-wise KL's three sums
+//                 (binary64 L, Y, P), written after pass 2 on rows that take
+//                 that form;
+//   [18 W]        1 when the row takes the term-wise form (the mean kernel
+//                 then adds the shares up and forms the row's loss).
+// ---------------------------------------------------------------------------
+constexpr int kStateWords = 6;
+__host__ __device__ inline int64_t rec_words(int W) { return (18 * (int64_t)W + 1 + 31) & ~(int64_t)31; }
+__host__ __device__ inline int64_t share_word(int W, int seg) { return 12 * (int64_t)W + 6 * seg; }
+__host__ __device__ inline int64_t flag_word(int W) { return 18 * (int64_t)W; }
 
-// Per-row exchange record (rec_words(W) words, own cache lines): segment s
-// publishes its 5 state words as 64-bit {value, tag = 1} pairs at 5 s .. 5 s
-// + 4 with single-copy-atomic stores (no round trip for the writer); a
-// reader waits until all 5W tags are set.  Records are zeroed before each
-// launch.
+__device__ __forceinline__ float state_word(const Stats& st, int j)
+{
+    return j == 0 ? st.mt : j == 1 ? st.zt : j == 2 ? st.at : j == 3 ? st.ms : j == 4 ? st.zs : st.dx;
+}
+
+__device__ __forceinline__ Stats state_of_words(const uint32_t* w)
+{
+    return Stats{as_f(w[0]), as_f(w[1]), as_f(w[2]), as_f(w[3]), as_f(w[4]), as_f(w[5])};
+}
+
 __device__ __forceinline__ void publish(uint64_t* rec64, int seg, const Stats& st)
 {
     const int tid = threadIdx.x;
-    if (tid < 5) {
-        const float v = tid == 0 ? st.mt : tid == 1 ? st.zt : tid == 2 ? st.at : tid == 3 ? st.ms : st.zs;
-        __hip_atomic_store(rec64 + 5 * seg + tid, ((uint64_t)1 << 32) | as_u(v), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid < kStateWords)
+        __hip_atomic_store(rec64 + kStateWords * seg + tid, ((uint64_t)1 << 32) | as_u(state_word(st, tid)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0 waits (bounded) for all W segment states of a row and copies them to
-// `seg`; returns, to every lane of the workgroup, whether they all arrived.
-__device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg, uint32_t* flag, uint64_t wait_ticks)
+// Wave 0 waits (bounded) for all W segment states of a row and copies their
+// words to `words` as they arrive; returns, to every lane of the workgroup,
+// whether they all arrived.
+__device__ __forceinline__ bool collect(const uint64_t* rec64, int W, uint32_t* words, uint32_t* flag,
+                                        uint64_t wait_ticks)
 {
     const int tid = threadIdx.x;
     if (tid < 64) {
-        // lane l watches words l, l + 64, ... (5W <= 5 kMaxSegments)
-        constexpr int kPer = (5 * kMaxSegments + 63) / 64;
-        uint64_t w[kPer];
+        // lane l watches words l, l + 64, ... (6 W <= 6 kMaxSegments)
+        constexpr int kPer = (kStateWords * kMaxSegments + 63) / 64;
+        const int n = kStateWords * W;
+        uint32_t got = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) w[j] = 0;
+        for (int j = 0; j < kPer; ++j) got |= (tid + 64 * j >= n ? 1u : 0u) << j;
+        const uint32_t all = (1u << kPer) - 1u;
         const uint64_t t0 = wall_clock64();
         bool done = false;
         while (true) {
-            bool mine_done = true;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int i = tid + 64 * j;
-                if (i < 5 * W && !(w[j] >> 32)) w[j] = __hip_atomic_load(rec64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                mine_done = mine_done && (i >= 5 * W || (w[j] >> 32) != 0);
+                if (!(got >> j & 1u)) {
+                    const uint64_t w = __hip_atomic_load(rec64 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (w >> 32) {
+                        words[i] = (uint32_t)w;
+                        got |= 1u << j;
+                    }
+                }
             }
-            done = __all(mine_done);
+            done = __all(got == all);
             if (done) break;
             __builtin_amdgcn_s_sleep(2);
             if (wall_clock64() - t0 > wait_ticks) break;
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = tid + 64 * j;
-            if (i < 5 * W) (&seg[i / 5].mt)[i % 5] = as_f((uint32_t)w[j]);
         }
         if (tid == 0) *flag = done ? 1u : 0u;
     }
@@ -284,13 +548,13 @@ __device__ __forceinline__ bool collect(const uint64_t* rec64, int W, Stats* seg
 // Merge the W segment states of a row in a fixed tree (lane l of every wave
 // starts from segment l; xor partners, merge is symmetric in its operands),
 // so every workgroup of the row obtains bit-identical row statistics.
-__device__ __forceinline__ Stats merge_segments(const Stats* seg, int W)
+__device__ __forceinline__ Stats merge_segments(const uint32_t* words, int W)
 {
     const int l = threadIdx.x & 63;
-    Stats st = l < W ? seg[l] : empty_stats();
+    Stats st = l < W ? state_of_words(words + kStateWords * l) : empty_stats();
     for (int o = 1; o < W; o <<= 1) st = merge(st, shfl_xor_stats(st, o));
     return Stats{__shfl(st.mt, 0, 64), __shfl(st.zt, 0, 64), __shfl(st.at, 0, 64), __shfl(st.ms, 0, 64),
-                 __shfl(st.zs, 0, 64)};
+                 __shfl(st.zs, 0, 64), __shfl(st.dx, 0, 64)};
 }
 
 template <bool BF16_IN>
@@ -322,25 +586,43 @@ __device__ __forceinline__ Stats seg_pass1(SegRegs<BF16_IN>& m, int64_t seg_u0, 
 
 struct SegShared {
     Stats part[kSegThreads / 64];
-    Stats seg_stats[kMaxSegments];
+    LossSum lpart[kSegThreads / 64];
+    uint32_t seg_words[kStateWords * kMaxSegments];
+    RowConst rk;
     uint32_t flag;
 };
 
-// the row's statistics (exchange + merge), its loss (segment 0) and pass 2:
-// p = 2^(c t - m_row) / Z_row and q alike, times grad_scale / T, written as
-// the gradient from the logits still held in registers
+// pass 2 over the units held in registers: the gradient, and in FORM_LOSS the
+// lane's share of the term-wise KL
+template <bool BF16_IN, int GRAD, bool FULL, bool TOPK, int FORM>
+__device__ __forceinline__ LossAcc seg_pass2(SegRegs<BF16_IN>& m, const KlArgs& a, int64_t row_unit0, int64_t seg_u0,
+                                             int64_t units, float c, float tau, const RowConst& k)
+{
+    LossAcc acc{0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kSegUnits; ++j) {
+        if (!FULL && lane_unit(seg_u0, j) >= units) continue;
+        float tv[8], sv[8];
+        m[j].values(tv, sv);
+        unit_grad<GRAD, TOPK, FORM>(tv, sv, c, tau, k, a, row_unit0 + lane_unit(seg_u0, j), acc);
+    }
+    return acc;
+}
+
+// the row's statistics (exchange + merge), its loss and pass 2 from the
+// logits still held in registers
 template <bool BF16_IN, int GRAD, bool FULL, bool TOPK>
 __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a, int W, int64_t row, int seg,
-                                           const Stats& my_seg, float c, float tau, float inv_t, float gmul,
+                                           const Stats& my_seg, float c, float tau, float gmul,
                                            uint32_t* rec_base, SegShared& sh)
 {
     const int64_t units = a.vocab >> 3;
     const int64_t row_unit0 = row * units;
     const int64_t seg_u0 = seg * kSegSpan;
+    uint32_t* rec = rec_base + row * rec_words(W);
     Stats row_st = my_seg;
     if (W > 1) {
-        const uint64_t* rec64 = reinterpret_cast<const uint64_t*>(rec_base + row * rec_words(W));
-        if (!collect(rec64, W, sh.seg_stats, &sh.flag, a.wait_ticks)) {
+        if (!collect(reinterpret_cast<const uint64_t*>(rec), W, sh.seg_words, &sh.flag, a.wait_ticks)) {
             // timed out: compute every segment's state here, with the same
             // lane mapping and arithmetic as its own workgroup
             for (int s = 0; s < W; ++s) {
@@ -349,40 +631,36 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
                     u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
                 });
                 const Stats os = group_merge<kSegThreads>(ol, sh.part);
-                if (threadIdx.x == 0) sh.seg_stats[s] = os;
+                if (threadIdx.x < kStateWords) sh.seg_words[kStateWords * s + threadIdx.x] = as_u(state_word(os, threadIdx.x));
             }
             __syncthreads();
         }
-        row_st = merge_segments(sh.seg_stats, W);
-        __syncthreads();  // seg_stats and flag are reused by the next row
+        row_st = merge_segments(sh.seg_words, W);
     }
-
-    if (seg == 0 && threadIdx.x == 0) {
-        // KL = E_p[t - s]/T - (LSE_t - LSE_s), LSE in log2 units m + log2 Z
-        a.row_loss[row] = (row_st.at / row_st.zt) * inv_t -
-                          kLn2 * ((row_st.mt - row_st.ms) + log2f(row_st.zt / row_st.zs));
+    if (threadIdx.x == 0) sh.rk = row_const(row_st, c, a.inv_t, gmul, a.lgmul, GRAD != 0);
+    __syncthreads();
+    const RowConst k = sh.rk;
+    if (k.form != FORM_LOSS) {
+        if (seg == 0 && threadIdx.x == 0) a.row_loss[row] = k.loss;
+        if constexpr (GRAD != 0) {
+            if (k.form == FORM_PLAIN) seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_PLAIN>(m, a, row_unit0, seg_u0, units, c, tau, k);
+            else seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_SELECT>(m, a, row_unit0, seg_u0, units, c, tau, k);
+        }
+        return;
     }
-    if constexpr (GRAD != 0) {
-        const float wt = gmul / row_st.zt, ws = gmul / row_st.zs;
-#pragma unroll
-        for (int k = 0; k < kSegUnits; ++k) {
-            if (!FULL && lane_unit(seg_u0, k) >= units) continue;
-            float tv[8], sv[8], g[8];
-            m[k].values(tv, sv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
-                const float eq = exp2_hw(__builtin_fmaf(sv[i], c, -row_st.ms));
-                g[i] = __builtin_fmaf(eq, ws, -(ep * wt));
-                if (TOPK) g[i] = tv[i] >= tau ? g[i] : 0.0f;
-            }
-            const int64_t u = row_unit0 + lane_unit(seg_u0, k);
-            if constexpr (GRAD == 1) {
-                stnt(a.grad, u, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                                    pack_bf16x2(g[6], g[7])});
-            } else {
-                stnt(a.grad, 2 * u, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
-                stnt(a.grad, 2 * u + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
+    const LossAcc acc = seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_LOSS>(m, a, row_unit0, seg_u0, units, c, tau, k);
+    const LossSum part = group_sum<kSegThreads>(acc, sh.lpart);
+    if (threadIdx.x == 0) {
+        if (W == 1) {
+            a.row_loss[row] = (float)termwise_kl(part.l, part.y, part.p);
+        } else {
+            double* share = reinterpret_cast<double*>(rec + share_word(W, seg));
+            share[0] = part.l;
+            share[1] = part.y;
+            share[2] = part.p;
+            if (seg == 0) {
+                a.row_loss[row] = k.loss;
+                rec[flag_word(W)] = 1u;
             }
         }
     }
@@ -394,7 +672,7 @@ __device__ __forceinline__ uint64_t* rec_of(uint32_t* rec_base, int64_t row, int
 }
 
 template <bool BF16_IN, int GRAD, bool FULL, bool TOPK>
-__device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, int seg, float c, float inv_t, float gmul,
+__device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, int seg, float c, float gmul,
                                          uint32_t* rec_base, SegShared& sh)
 {
     const int64_t units = a.vocab >> 3;
@@ -404,7 +682,7 @@ __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, in
     seg_load<BF16_IN, FULL>(m, a, row * units, seg_u0, units);
     const Stats st = seg_pass1<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau, sh.part);
     if (W > 1) publish(rec_of(rec_base, row, W), seg, st);
-    seg_finish<BF16_IN, GRAD, FULL, TOPK>(m, a, W, row, seg, st, c, tau, inv_t, gmul, rec_base, sh);
+    seg_finish<BF16_IN, GRAD, FULL, TOPK>(m, a, W, row, seg, st, c, tau, gmul, rec_base, sh);
 }
 
 // One workgroup per segment: load, pass 1, publish, wait, pass 2.  Segments
@@ -413,35 +691,36 @@ __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, in
 // TOPK: only the entries whose teacher logit is at least the row's threshold
 // a.tau[row] count (the kept set of the teacher-top-k KL); gradient 0 elsewhere
 template <bool BF16_IN, int GRAD, bool TOPK> // GRAD: 0 none, 1 bf16, 2 fp32
-__device__ __forceinline__ void seg_entry(const KlArgs& a, int W, float c, float inv_t, float gmul, uint32_t* rec_base)
+__device__ __forceinline__ void seg_entry(const KlArgs& a, int W, float c, float gmul, uint32_t* rec_base)
 {
     __shared__ SegShared sh;
     const int64_t row = blockIdx.x / W;
     const int seg = (int)(blockIdx.x - row * W);
     if ((seg + 1) * kSegSpan <= (a.vocab >> 3))
-        seg_body<BF16_IN, GRAD, true, TOPK>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+        seg_body<BF16_IN, GRAD, true, TOPK>(a, W, row, seg, c, gmul, rec_base, sh);
     else
-        seg_body<BF16_IN, GRAD, false, TOPK>(a, W, row, seg, c, inv_t, gmul, rec_base, sh);
+        seg_body<BF16_IN, GRAD, false, TOPK>(a, W, row, seg, c, gmul, rec_base, sh);
 }
 
 // bf16 logits: held to 128 VGPRs, four workgroups per CU
 template <int GRAD, bool TOPK>
-__global__ __launch_bounds__(kSegThreads, 4) void kl_seg_bf16_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+__global__ __launch_bounds__(kSegThreads, 4) void kl_seg_bf16_kernel(KlArgs a, int W, float c, float gmul,
                                                                      uint32_t* rec_base)
 {
-    seg_entry<true, GRAD, TOPK>(a, W, c, inv_t, gmul, rec_base);
+    seg_entry<true, GRAD, TOPK>(a, W, c, gmul, rec_base);
 }
 
 template <int GRAD, bool TOPK>
-__global__ __launch_bounds__(kSegThreads) void kl_seg_f32_kernel(KlArgs a, int W, float c, float inv_t, float gmul,
+__global__ __launch_bounds__(kSegThreads) void kl_seg_f32_kernel(KlArgs a, int W, float c, float gmul,
                                                                  uint32_t* rec_base)
 {
-    seg_entry<false, GRAD, TOPK>(a, W, c, inv_t, gmul, rec_base);
+    seg_entry<false, GRAD, TOPK>(a, W, c, gmul, rec_base);
 }
 
 // ---------------------------------------------------------------------------
 // Two-pass kernel for rows longer than kMaxSegments segments: one workgroup
-// per row streams the row twice (online state, then the gradient).
+// per row streams the row twice (online state, then the gradient and, on rows
+// that take it, the term-wise KL).
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 1024;
 
@@ -461,16 +740,23 @@ __device__ __forceinline__ void accumulate(Stats& st, const float (&t)[8], const
         et[i] = exp2_hw(__builtin_fmaf(t[i], c, -nmt));
         es[i] = exp2_hw(__builtin_fmaf(s[i], c, -nms));
         pa = __builtin_fmaf(et[i], t[i] - s[i], pa);
+        st.dx = maxnan(st.dx, s[i] - t[i]);
     }
     st.zt = st.zt * ft + sum8(et);
     st.at = st.at * ft + pa;
     st.zs = st.zs * fs + sum8(es);
 }
 
+struct RowShared {
+    Stats part[kRowThreads / 64];
+    LossSum lpart[kRowThreads / 64];
+    RowConst rk;
+};
+
 template <bool BF16_IN, int GRAD>
-__global__ __launch_bounds__(kRowThreads) void kl_row_kernel(KlArgs a, float c, float inv_t, float gmul)
+__global__ __launch_bounds__(kRowThreads) void kl_row_kernel(KlArgs a, float c, float gmul)
 {
-    __shared__ Stats part[kRowThreads / 64];
+    __shared__ RowShared sh;
     const int64_t row = blockIdx.x;
     const int64_t units = a.vocab >> 3;
     const int64_t ubase = row * units;
@@ -482,38 +768,58 @@ __global__ __launch_bounds__(kRowThreads) void kl_row_kernel(KlArgs a, float c, 
         load8<BF16_IN>(a.student, ubase + u, true, s);
         accumulate(st, t, s, c);
     }
-    const Stats w = group_merge<kRowThreads>(st, part);
-    if (tid == 0)
-        a.row_loss[row] = (w.at / w.zt) * inv_t - kLn2 * ((w.mt - w.ms) + log2f(w.zt / w.zs));
-    if constexpr (GRAD == 0) return;
-    const float wt = gmul / w.zt, ws = gmul / w.zs;
+    const Stats w = group_merge<kRowThreads>(st, sh.part);
+    if (tid == 0) sh.rk = row_const(w, c, a.inv_t, gmul, a.lgmul, GRAD != 0);
+    __syncthreads();
+    const RowConst k = sh.rk;
+    if (GRAD == 0 && k.form != FORM_LOSS) {
+        if (tid == 0) a.row_loss[row] = k.loss;
+        return;
+    }
+    LossAcc acc{0.0f, 0.0f, 0.0f};
     for (int64_t u = tid; u < units; u += kRowThreads) {
-        float t[8], s[8], g[8];
+        float t[8], s[8];
         load8<BF16_IN>(a.teacher, ubase + u, true, t);
         load8<BF16_IN>(a.student, ubase + u, true, s);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float eq = exp2_hw(__builtin_fmaf(s[i], c, -w.ms));
-            const float ep = exp2_hw(__builtin_fmaf(t[i], c, -w.mt));
-            g[i] = __builtin_fmaf(eq, ws, -(ep * wt));
-        }
-        if constexpr (GRAD == 1) {
-            stnt(a.grad, ubase + u,
-                 v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])});
-        } else {
-            stnt(a.grad, 2 * (ubase + u), v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
-            stnt(a.grad, 2 * (ubase + u) + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
-        }
+        if (k.form == FORM_LOSS) unit_grad<GRAD, false, FORM_LOSS>(t, s, c, 0.0f, k, a, ubase + u, acc);
+        else if (k.form == FORM_PLAIN) unit_grad<GRAD, false, FORM_PLAIN>(t, s, c, 0.0f, k, a, ubase + u, acc);
+        else unit_grad<GRAD, false, FORM_SELECT>(t, s, c, 0.0f, k, a, ubase + u, acc);
     }
+    if (k.form != FORM_LOSS) {
+        if (tid == 0) a.row_loss[row] = k.loss;
+        return;
+    }
+    const LossSum part = group_sum<kRowThreads>(acc, sh.lpart);
+    if (tid == 0) a.row_loss[row] = (float)termwise_kl(part.l, part.y, part.p);
 }
 
-// mean of the per-row losses: fixed assignment of rows to lanes, binary64
-// accumulation, fixed reduction tree
-__global__ __launch_bounds__(1024) void kl_mean_kernel(const float* row_loss, int64_t rows, float* loss_out)
+// Mean of the per-row losses: fixed assignment of rows to lanes, binary64
+// accumulation, fixed reduction tree.  Rows the segment kernels marked for
+// the term-wise KL (rec non-null, W > 1) first get their loss from their
+// segments' shares, added in segment order (also written to row_loss).
+__global__ __launch_bounds__(1024) void kl_mean_kernel(float* row_loss, int64_t rows, float* loss_out,
+                                                       const uint32_t* rec, int W)
 {
     __shared__ double part[1024];
     double acc = 0.0;
-    for (int64_t r = threadIdx.x; r < rows; r += 1024) acc += (double)row_loss[r];
+    for (int64_t r = threadIdx.x; r < rows; r += 1024) {
+        float v = row_loss[r];
+        if (rec) {
+            const uint32_t* rr = rec + r * rec_words(W);
+            if (rr[flag_word(W)]) {
+                double l = 0.0, y = 0.0, p = 0.0;
+                for (int seg = 0; seg < W; ++seg) {
+                    const double* share = reinterpret_cast<const double*>(rr + share_word(W, seg));
+                    l += share[0];
+                    y += share[1];
+                    p += share[2];
+                }
+                v = (float)termwise_kl(l, y, p);
+                row_loss[r] = v;
+            }
+        }
+        acc += (double)v;
+    }
     part[threadIdx.x] = acc;
     __syncthreads();
     for (int w = 512; w > 0; w >>= 1) {
@@ -579,6 +885,8 @@ struct TopShared {
     uint32_t wave_tot[kTopThreads / 64];
     uint32_t digit, above;
     Stats part[kTopThreads / 64];
+    LossSum lpart[kTopThreads / 64];
+    RowConst rk;
 };
 
 // inclusive prefix sum over the workgroup's lanes in lane order
@@ -656,8 +964,20 @@ __device__ __forceinline__ uint32_t key_of_value(float v)
     return BF16 ? key16(as_u(v) >> 16) : key32(as_u(v));
 }
 
+// the value whose key is `key` (inverse of key16 / key32)
+template <bool BF16>
+__device__ __forceinline__ float value_of_key(uint32_t key)
+{
+    if constexpr (BF16) {
+        const uint32_t h = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xFFFFu);
+        return as_f(h << 16);
+    } else {
+        return as_f((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+    }
+}
+
 template <bool BF16_IN, int GRAD>
-__global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t k, float c, float inv_t, float gmul)
+__global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t k, float c, float gmul)
 {
     __shared__ TopShared sh;
     const int64_t row = blockIdx.x;
@@ -691,7 +1011,7 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t
     };
 
     // kept-set softmax state, online as in the full-vocabulary kernel
-    float mt = -__builtin_inff(), ms = -__builtin_inff(), zt = 0.0f, zs = 0.0f, at = 0.0f;
+    float mt = -__builtin_inff(), ms = -__builtin_inff(), zt = 0.0f, zs = 0.0f, at = 0.0f, dx = -__builtin_inff();
     for_ts([&](const Unit<BF16_IN>& both, bool valid, int64_t) {
         if (!valid) return;
         uint32_t key[8];
@@ -715,51 +1035,39 @@ __global__ __launch_bounds__(kTopThreads) void kl_topk_kernel(KlArgs a, uint32_t
             pt[i] = kept ? exp2_hw(__builtin_fmaf(tv[i], c, -mt)) : 0.0f;
             ps[i] = kept ? exp2_hw(__builtin_fmaf(sv[i], c, -ms)) : 0.0f;
             pa = kept ? __builtin_fmaf(pt[i], tv[i] - sv[i], pa) : pa;
+            dx = kept ? maxnan(dx, sv[i] - tv[i]) : dx;
         }
         zt = zt * ft + sum8(pt);
         at = at * ft + pa;
         zs = zs * fs + sum8(ps);
     });
-    const Stats row_st = group_merge<kTopThreads>(Stats{mt, zt, at, ms, zs}, sh.part);
-    if (tid == 0)
-        a.row_loss[row] = (row_st.at / row_st.zt) * inv_t -
-                          kLn2 * ((row_st.mt - row_st.ms) + log2f(row_st.zt / row_st.zs));
-    if constexpr (GRAD != 0) {
-        const float wt = gmul / row_st.zt, ws = gmul / row_st.zs;
-        for_ts([&](const Unit<BF16_IN>& both, bool valid, int64_t u) {
-            if (!valid) return;
-            uint32_t key[8];
-            teacher_keys<BF16_IN>(both, key);
-            float tv[8], sv[8], g[8];
-            both.values(tv, sv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float ep = exp2_hw(__builtin_fmaf(tv[i], c, -row_st.mt));
-                const float eq = exp2_hw(__builtin_fmaf(sv[i], c, -row_st.ms));
-                g[i] = key[i] >= tau ? __builtin_fmaf(eq, ws, -(ep * wt)) : 0.0f;
-            }
-            if constexpr (GRAD == 1) {
-                stnt(a.grad, u, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                                    pack_bf16x2(g[6], g[7])});
-            } else {
-                stnt(a.grad, 2 * u, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
-                stnt(a.grad, 2 * u + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
-            }
-        });
+    const Stats row_st = group_merge<kTopThreads>(Stats{mt, zt, at, ms, zs, dx}, sh.part);
+    if (tid == 0) sh.rk = row_const(row_st, c, a.inv_t, gmul, a.lgmul, GRAD != 0);
+    __syncthreads();
+    const RowConst rk = sh.rk;
+    if (GRAD == 0 && rk.form != FORM_LOSS) {
+        if (tid == 0) a.row_loss[row] = rk.loss;
+        return;
     }
+    // the kept set as a value test (keys fold -0 onto +0, as the comparison does)
+    const float tau_v = value_of_key<BF16_IN>(tau);
+    LossAcc acc{0.0f, 0.0f, 0.0f};
+    for_ts([&](const Unit<BF16_IN>& both, bool valid, int64_t u) {
+        if (!valid) return;
+        float tv[8], sv[8];
+        both.values(tv, sv);
+        if (rk.form == FORM_LOSS) unit_grad<GRAD, true, FORM_LOSS>(tv, sv, c, tau_v, rk, a, u, acc);
+        else if (rk.form == FORM_PLAIN) unit_grad<GRAD, true, FORM_PLAIN>(tv, sv, c, tau_v, rk, a, u, acc);
+        else unit_grad<GRAD, true, FORM_SELECT>(tv, sv, c, tau_v, rk, a, u, acc);
+    });
+    if (rk.form != FORM_LOSS) {
+        if (tid == 0) a.row_loss[row] = rk.loss;
+        return;
+    }
+    const LossSum part = group_sum<kTopThreads>(acc, sh.lpart);
+    if (tid == 0) a.row_loss[row] = (float)termwise_kl(part.l, part.y, part.p);
 }
 
-// the value whose key is `key` (inverse of key16 / key32)
-template <bool BF16>
-__device__ __forceinline__ float value_of_key(uint32_t key)
-{
-    if constexpr (BF16) {
-        const uint32_t h = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xFFFFu);
-        return as_f(h << 16);
-    } else {
-        return as_f((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
-    }
-}
 
 // Threshold of the teacher-top-k KL for the segment kernels: tau_out[row] =
 // the k-th largest teacher logit of the row (the radix select above), the
@@ -1243,6 +1551,15 @@ __global__ void zero_records_kernel(uint32_t* rec, int64_t words)
         rec[i] = 0u;
 }
 
+// the launch's scalars the row constants use: 1 / T and log2 |grad_scale / T|
+KlArgs with_row_scales(const KlArgs& a)
+{
+    KlArgs b = a;
+    b.inv_t = 1.0f / a.temperature;
+    b.lgmul = (float)log2(fabs((double)a.grad_scale / (double)a.temperature));
+    return b;
+}
+
 // segments of a row, kMaxSegments + 1 standing for "too many"
 int segments(int64_t vocab)
 {
@@ -1264,10 +1581,10 @@ namespace {
 
 // the one-pass segment kernels (rows of at most kMaxSegments record segments)
 // or the two-pass row kernel; TOPK: masked by a.tau
-hipError_t launch_rows(const KlArgs& a, void* workspace, bool topk, hipStream_t stream)
+hipError_t launch_rows(const KlArgs& a0, void* workspace, bool topk, hipStream_t stream)
 {
+    const KlArgs a = with_row_scales(a0);
     const float c = kLog2e / a.temperature;
-    const float inv_t = 1.0f / a.temperature;
     const float gmul = a.grad_scale / a.temperature;
     const int W = segments(a.vocab);
     const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
@@ -1293,7 +1610,7 @@ hipError_t launch_rows(const KlArgs& a, void* workspace, bool topk, hipStream_t 
         if (W <= kMaxSegments) {
             uint32_t* brec = rec + r0 * rec_words(W);
             const dim3 grid((unsigned)(b.tokens * W)), block(kSegThreads);
-#define KS(K, GM, TK) hipLaunchKernelGGL((K<GM, TK>), grid, block, 0, stream, b, W, c, inv_t, gmul, brec)
+#define KS(K, GM, TK) hipLaunchKernelGGL((K<GM, TK>), grid, block, 0, stream, b, W, c, gmul, brec)
 #define KS3(K, TK) { if (gmode == 0) KS(K, 0, TK); else if (gmode == 1) KS(K, 1, TK); else KS(K, 2, TK); }
             if (a.bf16_in) { if (topk) KS3(kl_seg_bf16_kernel, true) else KS3(kl_seg_bf16_kernel, false) }
             else { if (topk) KS3(kl_seg_f32_kernel, true) else KS3(kl_seg_f32_kernel, false) }
@@ -1301,7 +1618,7 @@ hipError_t launch_rows(const KlArgs& a, void* workspace, bool topk, hipStream_t 
 #undef KS
         } else {
             const dim3 grid((unsigned)b.tokens), block(kRowThreads);
-#define KR(BF, GM) hipLaunchKernelGGL((kl_row_kernel<BF, GM>), grid, block, 0, stream, b, c, inv_t, gmul)
+#define KR(BF, GM) hipLaunchKernelGGL((kl_row_kernel<BF, GM>), grid, block, 0, stream, b, c, gmul)
             if (a.bf16_in) { if (gmode == 0) KR(true, 0); else if (gmode == 1) KR(true, 1); else KR(true, 2); }
             else { if (gmode == 0) KR(false, 0); else if (gmode == 1) KR(false, 1); else KR(false, 2); }
 #undef KR
@@ -1310,6 +1627,20 @@ hipError_t launch_rows(const KlArgs& a, void* workspace, bool topk, hipStream_t 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// the mean kernel, after the row kernels; with the segment kernels' records
+// (W > 1) it first completes the rows that took the term-wise KL
+hipError_t launch_mean(const KlArgs& a, void* workspace, hipStream_t stream)
+{
+    const int W = a.tokens > 0 && a.vocab > 0 ? segments(a.vocab) : 0;
+    const uint32_t* rec =
+        W > 1 && W <= kMaxSegments
+            ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(workspace) +
+                                                (((size_t)a.tokens * 4 + 255) & ~(size_t)255))
+            : nullptr;
+    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out, rec, W);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -1322,8 +1653,7 @@ hipError_t launch_kl(const KlArgs& a, void* workspace, hipStream_t stream)
         hipError_t e = launch_rows(b, workspace, false, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
-    return hipGetLastError();
+    return launch_mean(a, workspace, stream);
 }
 
 size_t kl_topk_workspace_bytes(int64_t tokens, int64_t vocab)
@@ -1351,10 +1681,10 @@ dim3 sel_grid(int64_t rows)
 // rows longer than kMaxSegments record segments: one workgroup per row
 // streams it in every step (threshold from a.tau when given, else the k-th
 // largest teacher logit)
-hipError_t launch_topk_long_rows(const KlArgs& a, uint32_t kk, hipStream_t stream)
+hipError_t launch_topk_long_rows(const KlArgs& a0, uint32_t kk, hipStream_t stream)
 {
+    const KlArgs a = with_row_scales(a0);
     const float c = kLog2e / a.temperature;
-    const float inv_t = 1.0f / a.temperature;
     const float gmul = a.grad_scale / a.temperature;
     const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
     const size_t in_row = (size_t)a.vocab * (a.bf16_in ? 2 : 4);
@@ -1369,7 +1699,7 @@ hipError_t launch_topk_long_rows(const KlArgs& a, uint32_t kk, hipStream_t strea
         if (a.tau) b.tau = a.tau + r0;
         if (a.grad) b.grad = static_cast<char*>(a.grad) + r0 * g_row;
         const dim3 grid((unsigned)b.tokens), block(kTopThreads);
-#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, inv_t, gmul)
+#define KT(BF, GM) hipLaunchKernelGGL((kl_topk_kernel<BF, GM>), grid, block, 0, stream, b, kk, c, gmul)
         if (a.bf16_in) { if (gmode == 0) KT(true, 0); else if (gmode == 1) KT(true, 1); else KT(true, 2); }
         else { if (gmode == 0) KT(false, 0); else if (gmode == 1) KT(false, 1); else KT(false, 2); }
 #undef KT
@@ -1411,8 +1741,7 @@ hipError_t launch_kl_topk(const KlArgs& a, int64_t k, void* workspace, hipStream
             if (e != hipSuccess) return e;
         }
     }
-    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
-    return hipGetLastError();
+    return launch_mean(a, workspace, stream);
 }
 
 hipError_t launch_kl_topp(const KlArgs& a, float top_p, float* tau_out, void* workspace, hipStream_t stream)
@@ -1441,8 +1770,7 @@ hipError_t launch_kl_topp(const KlArgs& a, float top_p, float* tau_out, void* wo
                                                          : launch_topk_long_rows(b, 1u, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out);
-    return hipGetLastError();
+    return launch_mean(a, workspace, stream);
 }
 
 } // namespace qad

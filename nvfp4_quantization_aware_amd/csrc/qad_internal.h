@@ -95,6 +95,8 @@ struct KlArgs {
     bool grad_bf16;
     const float* tau = nullptr;  // teacher-top-k thresholds per row (null: full vocabulary)
     uint64_t wait_ticks = 0;     // bound of the segment kernels' row exchange wait (100 MHz ticks)
+    float inv_t = 1.0f;          // 1 / temperature (set by the launchers)
+    float lgmul = 0.0f;          // log2 |grad_scale / temperature| (set by the launchers)
 };
 // the process-wide bound of the kernels' device-side waits, in ticks of the
 // 100 MHz wall clock (qad_set_wait_limit_us)

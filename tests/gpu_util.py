@@ -40,52 +40,71 @@ def bf16_ulp(a: np.ndarray) -> np.ndarray:
     return np.maximum(2.0 ** (e - 7), 2.0**-133)
 
 
-def prob_scale(t_bits: np.ndarray, s_bits: np.ndarray, T: float, grad_scale: float, kept=None):
-    """Per row, the size of the probabilities whose difference the gradient
-    is: max_v and L2 over v of (p_v + q_v) grad_scale / T, in binary64 from the
-    inputs (bf16 bits or float32).  `kept` (bool, the shape of the inputs):
-    the probabilities renormalized over the kept entries of each row, as the
-    top-k and top-p losses take them."""
-    f = lambda a: ((a.astype(np.uint32) << 16).view(np.float32) if a.dtype == np.uint16 else a).astype(np.float64)
+def f32_ulp(a: np.ndarray) -> np.ndarray:
+    """Spacing of binary32 numbers at magnitude |a| (2^-149 below 2^-126)."""
+    a = np.maximum(np.abs(np.asarray(a, np.float64)), 2.0**-126)
+    return 2.0 ** (np.floor(np.log2(a)) - 23)
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    return ((a.astype(np.uint32) << 16).view(np.float32) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def kl_probs(t_bits: np.ndarray, s_bits: np.ndarray, T: float, kept=None):
+    """binary64 teacher and student probabilities p = softmax(t/T), q =
+    softmax(s/T) of each row (inputs as bf16 bits or float32); `kept` (bool,
+    the inputs' shape): renormalised over the kept entries, 0 elsewhere, as
+    the top-k and top-p losses take them."""
     def softmax(x):
         x = x / T
         if kept is not None:
             x = np.where(kept, x, -np.inf)
         e = np.exp(x - x.max(axis=-1, keepdims=True))
         return e / e.sum(axis=-1, keepdims=True)
-    ps = (softmax(f(t_bits)) + softmax(f(s_bits))) * grad_scale / T
-    return ps.max(axis=-1), np.linalg.norm(ps, axis=-1)
+    return softmax(_f64(t_bits)), softmax(_f64(s_bits))
 
 
-def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, rel=1e-5, zero_row_scale=0.0, floor=None):
-    """Gradient rule: per row, |g - g_ref| <= rel * max_row |g_ref| for a
-    float32 gradient; for bf16, the bf16 rounding of a value within that band
-    (so additionally half a bf16 ulp).  A row whose reference gradient is 0
-    everywhere (p and q equal, e.g. a single kept entry) has no relative
-    scale; there `zero_row_scale` (grad_scale / T, the bound of |q - p| times
-    the factor) stands in for max_row |g_ref|.  `floor` = prob_scale(...):
-    the fp32 floor of a difference of probabilities, 1e-6 of the row's
-    largest (p + q) grad_scale / T (and 1e-6 of its L2 for the L2 rule); it
-    only matters on rows whose gradient is far smaller than the
-    probabilities themselves (near one-hot rows where teacher and student
-    agree)."""
+def assert_kl_grad_close(g_dev: np.ndarray, g_ref: np.ndarray, probs, grad_scale: float, T: float, rel=1e-5):
+    """Gradient rule, element by element: with p, q = probs (kl_probs),
+        |g - g_ref| <= rel |g_ref| + 1e-6 (p + q) grad_scale / T
+    -- 1e-5 of the element itself, and 1e-6 of the two probabilities whose
+    difference it is (a binary32 probability carries a few units in its last
+    place) -- plus the output format's own rounding: one binary32 ulp of
+    g_ref (2^-149 below 2^-126) for an fp32 gradient, half a bf16 ulp of
+    |g_ref| + that band for a bf16 one.  Per row, for fp32: the L2 error
+    within rel ||g_ref|| + 1e-6 ||p + q|| grad_scale / T."""
     g_ref = np.asarray(g_ref, np.float64)
-    row_max = np.abs(g_ref).max(axis=-1, keepdims=True)
-    tol = rel * np.where(row_max > 0, row_max, zero_row_scale)
-    if floor is not None:
-        tol = np.maximum(tol, 1e-6 * np.asarray(floor[0])[:, None])
+    p, q = probs
+    pq = (p + q) * (grad_scale / T)
+    tol = rel * np.abs(g_ref) + 1e-6 * pq
     if g_dev.dtype == np.uint16:
-        g = (g_dev.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        g = _f64(g_dev)
         bound = tol + 0.5 * bf16_ulp(np.abs(g_ref) + tol)
     else:
         g = g_dev.astype(np.float64)
-        bound = tol
+        bound = tol + f32_ulp(g_ref)
         l2 = np.linalg.norm(g - g_ref, axis=-1)
-        l2_ref = np.linalg.norm(g_ref, axis=-1)
-        l2_tol = rel * np.where(l2_ref > 0, l2_ref, zero_row_scale * np.sqrt(g_ref.shape[-1]))
-        if floor is not None:
-            l2_tol = np.maximum(l2_tol, 1e-6 * np.asarray(floor[1]))
-        assert np.all(l2 <= l2_tol), l2.max()
+        l2_tol = rel * np.linalg.norm(g_ref, axis=-1) + 1e-6 * np.linalg.norm(pq, axis=-1)
+        assert np.all(l2 <= l2_tol), (l2 / l2_tol).max()
     err = np.abs(g - g_ref)
     bad = err > bound
-    assert not bad.any(), "worst excess %g at %s" % ((err - bound).max(), np.argwhere(bad)[:3])
+    assert not bad.any(), "worst err/bound %g at %s" % ((err / bound).max(), np.argwhere(bad)[:3])
+
+
+# A row whose exact KL is 0 (teacher and student distributions equal, e.g. a
+# single kept entry) has no relative scale; the library's term-wise sum then
+# holds only the second-order rounding of its log-ratios (|x| ~ 1e-7 gives
+# psi(x) ~ 1e-15).
+ZERO_KL_TOL = 1e-12
+
+
+def assert_kl_loss_close(val, ref, rel=1e-5):
+    """Loss rule (one mean or per-row losses): |val - ref| <= rel |ref|; where
+    ref is exactly 0, |val| <= ZERO_KL_TOL."""
+    val = np.asarray(val, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = np.where(ref == 0.0, ZERO_KL_TOL, rel * np.abs(ref))
+    err = np.abs(val - ref)
+    assert np.all(err <= bound), "worst err/bound %g at %s (val %s ref %s)" % (
+        (err / bound).max(), np.argmax(err / bound), val.ravel()[np.argmax(err / bound)],
+        ref.ravel()[np.argmax(err / bound)])

@@ -69,12 +69,13 @@ def test_workspace_sizes(L):
     for op in (q.QAD_OP_AMAX, q.QAD_OP_QUANTIZE, q.QAD_OP_MSE_CALIBRATE):
         for B, R, C_ in ((128, 2048, 4096), (1, 1, 16), (1, 8192, 8192), (3, 7, 48)):
             assert L.qad_workspace_bytes(op, B, R, C_) == _record_bytes(B, R * C_)
-    # KL: per-row losses, then one exchange record per row when a row spans
-    # 2..64 segments of 16384 logits (5 tagged 64-bit words per segment)
+    # KL: per-row losses, then one record per row when a row spans 2..64
+    # segments of 16384 logits (6 tagged 64-bit state words and three binary64
+    # loss shares per segment, one flag word)
     for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20), (3, (1 << 20) + 8),
                           (3, 1 << 22)):
         W = -(-vocab // 16384)
-        rec = ((10 * W + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
+        rec = ((18 * W + 1 + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
         expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
         assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
     # top-k KL: the KL workspace, then one float per row (thresholds)

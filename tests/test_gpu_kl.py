@@ -1,17 +1,13 @@
 """GPU parity of the fused KL(teacher || student) loss and gradient.
 
-Tolerances (the oracle is binary64; the kernels accumulate in fp32):
-  * mean loss: |L - L_ref| <= 1e-5 |L_ref|;
-  * per-row loss: |r - r_ref| <= 1e-5 |r_ref| + 1e-6 -- a row's KL is the
-    difference of O(1) terms (E_p[t-s]/T and the log-sum-exp gap), so fp32
-    leaves an absolute floor of a few 1e-7 nats on rows whose KL is near 0;
-  * fp32 gradient: per row, max and L2 error <= 1e-5 of the row's max / L2
-    norm of the reference;
-  * bf16 gradient: the bf16 rounding of a value inside that fp32 band;
-  * on near one-hot rows (low T, wide logits) the gradient q - p is far
-    below the probabilities it is the difference of; there the band is
-    1e-6 of max(p + q) (and of its L2), the fp32 floor of that difference.
-Full-size logits (8192 x 131072) are checked on sampled rows; the mean over
+Tolerances (the oracle is binary64; the kernels compute in fp32):
+  * mean loss and every per-row loss: |L - L_ref| <= 1e-5 |L_ref| (a row
+    whose exact KL is 0: |L| <= 1e-12, the second-order rounding);
+  * gradient, element by element: |g - g_ref| <= 1e-5 |g_ref| + 1e-6 (p + q)
+    grad_scale / T, plus one fp32 ulp (fp32 output) or half a bf16 ulp
+    (bf16 output); per row (fp32), the L2 error within 1e-5 of the
+    reference's L2 norm plus 1e-6 of that of (p + q) grad_scale / T.
+Full-size logits (8192 x 131072) are checked on 64 sampled rows; the mean over
 all rows is checked against the per-row losses the kernel wrote.
 """
 import numpy as np
@@ -20,7 +16,7 @@ import torch
 
 import nvfp4_quantization_aware_amd as q
 from nvfp4_quantization_aware_amd import synth
-from gpu_util import announce, assert_kl_grad_close, gpu_device, host, prob_scale
+from gpu_util import announce, assert_kl_grad_close, assert_kl_loss_close, gpu_device, host, kl_probs
 
 pytestmark = pytest.mark.gpu
 
@@ -28,12 +24,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def dev():
     return gpu_device()
-
-
-def _check_rows(rows_dev, rows_ref):
-    rows_dev = np.asarray(rows_dev, np.float64)
-    err = np.abs(rows_dev - rows_ref)
-    assert np.all(err <= 1e-5 * np.abs(rows_ref) + 1e-6), (err.max(), np.argmax(err))
 
 
 def run_kl(dev, t, s, T, grad_dtype, label):
@@ -59,9 +49,9 @@ def test_kl_small(dev, orc, tokens, vocab, T, in_dt, g_dt):
     t, s = t.to(in_dt), s.to(in_dt)
     loss, rows, g = run_kl(dev, t, s, T, g_dt, "small")
     ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
-    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
-    _check_rows(rows, ref_rows)
-    assert_kl_grad_close(g, ref_g)
+    assert_kl_loss_close(loss, ref_loss)
+    assert_kl_loss_close(rows, ref_rows)
+    assert_kl_grad_close(g, ref_g, kl_probs(host(t), host(s), T), 1.0 / tokens, T)
 
 
 @pytest.mark.parametrize("g_dt", [torch.bfloat16, None])
@@ -71,10 +61,10 @@ def test_kl_many_rounds(dev, orc, g_dt):
     t, s = synth.logits_bf16(tokens=1024, vocab=65544, seed=17)
     loss, rows, g = run_kl(dev, t, s, 1.0, g_dt, "many rounds")
     ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), grad_scale=1.0 / 1024)
-    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
-    _check_rows(rows, ref_rows)
+    assert_kl_loss_close(loss, ref_loss)
+    assert_kl_loss_close(rows, ref_rows)
     if g_dt is not None:
-        assert_kl_grad_close(g, ref_g)
+        assert_kl_grad_close(g, ref_g, kl_probs(host(t), host(s), 1.0), 1.0 / 1024, 1.0)
 
 
 @pytest.mark.parametrize("T,std,vocab", [(0.5, 8.0, 131072), (0.25, 8.0, 16384), (0.5, 5.0, 23744)])
@@ -82,14 +72,29 @@ def test_kl_many_rounds(dev, orc, g_dt):
 def test_kl_near_one_hot_rows(dev, orc, T, std, vocab, g_dt):
     # low temperature and wide logits: both distributions nearly one-hot at
     # the same entry, so the gradient q - p is many orders of magnitude below
-    # the probabilities; fp32 then reaches the fp32 floor of the difference
-    # (1e-6 of the probabilities), not 1e-5 of the tiny gradient itself
+    # the probabilities it is the difference of, and the KL of some rows is
+    # far below the two terms of its difference form
     t, s = synth.logits_bf16(tokens=16, vocab=vocab, teacher_std=std, seed=int(100 * T + std))
     loss, rows, g = run_kl(dev, t, s, T, g_dt, "near one-hot")
     ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
-    assert abs(loss - ref_loss) <= 1e-5 * abs(ref_loss)
-    _check_rows(rows, ref_rows)
-    assert_kl_grad_close(g, ref_g, floor=prob_scale(host(t), host(s), T, 1.0 / 16))
+    assert_kl_loss_close(loss, ref_loss)
+    assert_kl_loss_close(rows, ref_rows)
+    assert_kl_grad_close(g, ref_g, kl_probs(host(t), host(s), T), 1.0 / 16, T)
+
+
+@pytest.mark.parametrize("shift,noise,T", [(0.0, 0.02, 1.0), (-5.0, 0.2, 1.0), (12.0, 0.05, 0.5), (0.0, 0.0005, 2.0)])
+def test_kl_small_kl_rows(dev, orc, shift, noise, T):
+    # students very close to the teacher, or shifted from it by a constant:
+    # the per-row KL (down to ~1e-7 nats) is far below the terms of the
+    # difference form, so these rows take the term-wise form and must still
+    # be within 1e-5 of the oracle
+    t, s = synth.logits_bf16(tokens=12, vocab=40000, teacher_std=3.0, noise_std=noise, seed=int(1000 * noise) + 7)
+    s = (s.float() + shift).to(torch.bfloat16)
+    loss, rows, g = run_kl(dev, t, s, T, torch.float32, "small KL shift %g noise %g" % (shift, noise))
+    ref_loss, ref_rows, ref_g = orc.kl_fwd_bwd(host(t), host(s), T=T)
+    assert_kl_loss_close(loss, ref_loss)
+    assert_kl_loss_close(rows, ref_rows)
+    assert_kl_grad_close(g, ref_g, kl_probs(host(t), host(s), T), 1.0 / 12, T)
 
 
 def test_kl_forward_only_matches(dev):
@@ -105,8 +110,8 @@ def test_kl_identical_distributions(dev):
     t, _ = synth.logits_bf16(tokens=8, vocab=8192, seed=4)
     loss, rows, g = run_kl(dev, t, t.clone(), 1.0, torch.float32, "identical")
     assert loss == 0.0 and np.all(rows == 0.0)
-    # (q - p) is computed as one fused multiply-add: exact up to one rounding
-    assert np.abs(g).max() <= 1e-7 / 8
+    # equal logits give x = log2(q / p) = 0 exactly, hence a zero gradient
+    assert np.all(g == 0.0)
 
 
 def test_kl_deterministic(dev):
@@ -126,10 +131,12 @@ def test_kl_full_size_sampled(dev, orc):
     rows_h = host(rows).astype(np.float64)
     assert abs(loss - rows_h.mean()) <= 1e-6 * abs(loss)
     assert 0.08 < loss < 0.16
-    pick = [0, 1, 2047, 4096, 6000, 8191]
+    # 64 rows: both ends, and 62 spread over the rest with a seeded offset
+    rng = np.random.default_rng(64)
+    pick = sorted({0, 8191} | set(int(x) for x in np.arange(62) * 132 + rng.integers(1, 132, 62)))
     idx = torch.as_tensor(pick, device=dev)
     th, sh = host(t.index_select(0, idx)), host(s.index_select(0, idx))
     gh = host(g.index_select(0, idx))
     _, ref_rows, ref_g = orc.kl_fwd_bwd(th, sh, grad_scale=1.0 / 8192)
-    _check_rows(rows_h[pick], ref_rows)
-    assert_kl_grad_close(gh, ref_g)
+    assert_kl_loss_close(rows_h[pick], ref_rows)
+    assert_kl_grad_close(gh, ref_g, kl_probs(th, sh, 1.0), 1.0 / 8192, 1.0)
