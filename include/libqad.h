@@ -163,6 +163,25 @@ qad_status_t nvfp4_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R,
                             uint8_t* codes, uint8_t* scales_out, float* tscale_out, void* y,
                             void* workspace, size_t ws_bytes, qad_stream_t stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, outputs and errors without the workspace.  Dynamic
+ * scales keep their tensor records in a fixed 16 MiB scratch array inside
+ * the library (one per GPU, held until the process ends), so a call needs
+ * qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C) <= 16 MiB (the 128-expert
+ * 2048 x 4096 batch needs 9.5 MiB) and returns QAD_ERR_WORKSPACE beyond that;
+ * frozen scales need no scratch.  The call allocates nothing (no hipMalloc,
+ * no library allocation); it clears the records it uses on `stream` before
+ * its kernels read them.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give unspecified results -- order them on one stream, or use
+ * nvfp4_quantize with workspaces of their own.  QAD_ERR_HIP if the scratch's
+ * device address cannot be obtained. */
+qad_status_t nvfp4_quantize_noalloc(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                                    const uint8_t* scales_in, const float* tscale_in,
+                                    uint8_t* codes, uint8_t* scales_out, float* tscale_out, void* y,
+                                    qad_stream_t stream);
+
 /* Simulated quantization forward (quantize + dequantize, "QDQ") as run in
  * every student forward pass ([Lightning] "QAD的工作原理"): y = the
  * dequantized bf16 values of nvfp4_quantize, nothing else written. */

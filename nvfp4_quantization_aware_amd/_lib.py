@@ -31,6 +31,7 @@ SIGNATURES = {
     "qad_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_noalloc": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_qdq_fwd": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
     "nvfp4_qdq_bwd_clipped": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -212,6 +213,28 @@ def nvfp4_quantize(x: torch.Tensor, scales_in=None, tscale_in=None, codes=True, 
         _check(lib().nvfp4_quantize(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
                                     _p(scales_out), _p(tscale_out), _p(y), _p(ws),
                                     0 if ws is None else ws.numel(), _stream(dev)), "nvfp4_quantize")
+    return codes, scales_out, tscale_out, y
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, codes: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                           tscale_out: torch.Tensor | None = None, y: torch.Tensor | None = None, scales_in=None,
+                           tscale_in=None):
+    """nvfp4_quantize without a workspace (the library's fixed scratch): the
+    caller passes every output it wants (None skips it; nothing is allocated
+    here).  Returns (codes, scales_out, tscale_out, y)."""
+    B, R, Cc = _brc(x)
+    dev = x.device
+    n = B * R * Cc
+    scales_in = _opt(scales_in, "scales_in", dev, torch.uint8, n // 16)
+    tscale_in = _opt(tscale_in, "tscale_in", dev, torch.float32, B)
+    codes = _opt(codes, "codes", dev, torch.uint8, n // 2)
+    scales_out = _opt(scales_out, "scales_out", dev, torch.uint8, n // 16)
+    tscale_out = _opt(tscale_out, "tscale_out", dev, torch.float32, B)
+    y = _opt(y, "y", dev, torch.bfloat16, n)
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_quantize_noalloc(_p(x), _dt(x), B, R, Cc, _p(scales_in), _p(tscale_in), _p(codes),
+                                            _p(scales_out), _p(tscale_out), _p(y), _stream(dev)),
+               "nvfp4_quantize_noalloc")
     return codes, scales_out, tscale_out, y
 
 

@@ -7,6 +7,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "qad_internal.h"
 
@@ -16,6 +17,35 @@ namespace {
 
 // bound of the kernels' device-side waits, in microseconds (default 20 ms)
 std::atomic<int64_t> g_wait_us{20000};
+
+// Scratch of nvfp4_quantize_noalloc: the tensor records of the dynamic
+// quantizer, in a fixed device array (every GPU the library runs on holds its
+// own copy until the process ends).  Host code never uses the array's name
+// as an address: its device address is taken per device with
+// hipGetSymbolAddress, on the first call on that device with the device
+// current, and kept.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// the current device's address of `scratch`, or nullptr on failure
+void* static_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 } // namespace
 
@@ -75,11 +105,14 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
 }
 
 // fp8: per-tensor E4M3 (no block scales; frozen iff tscale_in is given;
-// codes one byte per element, 8-byte aligned); otherwise NVFP4
+// codes one byte per element, 8-byte aligned); otherwise NVFP4.
+// static_ws: dynamic scales take their records from the library's fixed
+// scratch (nvfp4_quantize_noalloc) instead of the caller's workspace, once
+// every other argument has been checked.
 qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
                            const uint8_t* scales_in, const float* tscale_in, uint8_t* codes,
                            uint8_t* scales_out, float* tscale_out, void* y, void* workspace,
-                           size_t ws_bytes, qad_stream_t stream, bool fp8 = false)
+                           size_t ws_bytes, qad_stream_t stream, bool fp8 = false, bool static_ws = false)
 {
     if (!valid_dtype(xt)) return QAD_ERR_DTYPE;
     const int64_t n = tensor_elems(B, R, C);
@@ -109,6 +142,12 @@ qad_status_t quantize_impl(const void* x, qad_dtype_t xt, int64_t B, int64_t R, 
         (codes && ranges_overlap(x, xbytes, codes, fp8 ? (size_t)n : (size_t)n / 2)) ||
         (scales_out && ranges_overlap(x, xbytes, scales_out, (size_t)n / 16)))
         return QAD_ERR_INVALID_ARG;
+    if (!frozen && static_ws) {
+        if (qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C) > kStaticScratchBytes) return QAD_ERR_WORKSPACE;
+        workspace = static_scratch();
+        if (!workspace) return QAD_ERR_HIP;
+        ws_bytes = kStaticScratchBytes;
+    }
     if (!frozen) {
         if (!workspace || ws_bytes < qad_workspace_bytes(QAD_OP_QUANTIZE, B, R, C)) return QAD_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return QAD_ERR_ALIGNMENT;
@@ -207,6 +246,14 @@ qad_status_t nvfp4_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R,
 {
     return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, codes, scales_out, tscale_out, y, workspace,
                          ws_bytes, stream);
+}
+
+qad_status_t nvfp4_quantize_noalloc(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,
+                                    const uint8_t* scales_in, const float* tscale_in, uint8_t* codes,
+                                    uint8_t* scales_out, float* tscale_out, void* y, qad_stream_t stream)
+{
+    return quantize_impl(x, xt, B, R, C, scales_in, tscale_in, codes, scales_out, tscale_out, y, nullptr, 0, stream,
+                         false, true);
 }
 
 qad_status_t nvfp4_qdq_fwd(const void* x, qad_dtype_t xt, int64_t B, int64_t R, int64_t C,

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
