@@ -272,6 +272,51 @@ void orc_nvfp4_qdq_bwd_clipped(const void* grad_y, int gdtype, const void* x, in
 }
 
 /* ------------------------------------------------------------------------
+ * Frozen-scale weight step.  [Lightning] section "量化尺度处理策略": with
+ * frozen (MSE-calibrated) scales the scales stay fixed and only the weights
+ * are updated; section "训练配置": a constant learning rate and gradient
+ * clipping at norm 1.0.  The pages name no optimizer; the reading taken is
+ * plain SGD whose step is the learning rate times the clipping coefficient
+ * the caller derived from the global gradient norm (min(1, max_norm/norm)),
+ * applied to the gradient that reaches the weight through the quantizer, i.e.
+ * the clipped straight-through one above:
+ *   a  = fl32(lr * clip_coef)
+ *   w' = w                              where |w| > 6 * s_eff (saturated:
+ *                                       no gradient reaches the weight)
+ *   w' = round_w(fma32(-a, g, w))       elsewhere
+ * fma32 is one binary32 rounding (to nearest even); round_w is the identity
+ * for binary32 weights and a second rounding to bf16 (nearest even) for bf16
+ * weights.  The weight is the forward's input (it is what the quantizer
+ * coded), so the test |w| <= 6 * s_eff is exact as in the clipped backward.
+ * Optional n_clipped: number of weights left unchanged by the clip.
+ * ---------------------------------------------------------------------- */
+void orc_nvfp4_frozen_sgd_step(const void* w, int wdtype, const void* grad, int gdtype, int64_t nblocks,
+                               const uint8_t* scales, float s_g, float lr, float clip_coef, void* w_out,
+                               int64_t* n_clipped)
+{
+    const float a = lr * clip_coef;   /* binary32 product (built with -ffp-contract=off) */
+    int64_t clipped = 0;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const float s_eff = orc_e4m3_decode(scales[b]) * s_g;
+        const double lim = 6.0 * (double)s_eff;
+        for (int j = 0; j < 16; ++j) {
+            const int64_t i = b * 16 + j;
+            const float wv = load_x(w, wdtype, i);
+            if (!(fabs((double)wv) <= lim)) {
+                ++clipped;
+                if (wdtype == 1) ((uint16_t*)w_out)[i] = ((const uint16_t*)w)[i];
+                else ((float*)w_out)[i] = ((const float*)w)[i];
+                continue;
+            }
+            const float r = fmaf(-a, load_x(grad, gdtype, i), wv);
+            if (wdtype == 1) ((uint16_t*)w_out)[i] = orc_bf16_from_f32(r);
+            else ((float*)w_out)[i] = r;
+        }
+    }
+    if (n_clipped) *n_clipped = clipped;
+}
+
+/* ------------------------------------------------------------------------
  * FP8 (E4M3) per-tensor simulated quantization.  [Qwen] section "3. QAD"
  * (the table of quantized components: attention projections FP8 W8A8, KV
  * cache FP8) and [Nano] "NVFP4-Format und warum es wichtig ist?" (FP8 KV

@@ -106,6 +106,15 @@ void orc_nvfp4_qdq_bwd_clipped(const void* grad_y, int gdtype, const void* x, in
                                int64_t nblocks, const uint8_t* scales, float s_g,
                                void* grad_x, int64_t* n_clipped);
 
+/* ---- frozen-scale SGD weight step --------------------------------------
+ * w' = w where |w| > 6 dec(scales[b]) s_g, else round_w(fmaf(-fl32(lr *
+ * clip_coef), g, w)); w and w_out (may alias) of dtype wdtype, grad of
+ * gdtype (0 = float32, 1 = bf16 bits).  Optional n_clipped: weights the clip
+ * left unchanged. */
+void orc_nvfp4_frozen_sgd_step(const void* w, int wdtype, const void* grad, int gdtype, int64_t nblocks,
+                               const uint8_t* scales, float s_g, float lr, float clip_coef, void* w_out,
+                               int64_t* n_clipped);
+
 /* ---- FP8 (E4M3) per-tensor QDQ ---------------------------------------------
  * x: n elements of dtype.  tscale_in NULL: dynamic s = amax/448 (1 for an
  * all-zero tensor); else s = *tscale_in (> 0).  Optional codes[n] (E4M3 with

@@ -63,6 +63,7 @@ def _load():
             "orc_mse_calibrate_blocks": (None, [vp, i64, f32, i32, f32, f32, vp, vp, vp, vp]),
             "orc_fp8_quantize": (None, [vp, i32, i64, vp, vp, vp, vp]),
             "orc_nvfp4_qdq_bwd_clipped": (None, [vp, i32, vp, i32, i64, vp, f32, vp, vp]),
+            "orc_nvfp4_frozen_sgd_step": (None, [vp, i32, vp, i32, i64, vp, f32, f32, f32, vp, vp]),
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
             "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
             "orc_kl_topp_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, f64, vp, vp, vp, vp, vp]),
@@ -251,6 +252,25 @@ def nvfp4_qdq_bwd_clipped(grad_y: np.ndarray, x: np.ndarray, scales: np.ndarray,
     return out, int(nc[0])
 
 
+def nvfp4_frozen_sgd_step(w: np.ndarray, grad: np.ndarray, scales: np.ndarray, tscale: float, lr: float,
+                          clip_coef: float):
+    """Frozen-scale SGD step of one weight tensor (w.size % 16 == 0): w where
+    |w| > 6 * dec(scale) * tscale, else round_w(fma32(-fl32(lr * clip_coef),
+    g, w)).  w and grad are float32 or raw-bf16 uint16 arrays of the same
+    size; scales holds one E4M3 code per 16 consecutive elements.  Returns
+    (w' like w, number of weights the clip left unchanged)."""
+    w = np.ascontiguousarray(w)
+    g = np.ascontiguousarray(grad)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    if g.size != w.size or w.size % 16 or sc.size != w.size // 16:
+        raise ValueError("w, grad and scales sizes do not match")
+    out = np.empty_like(w)
+    nc = np.zeros(1, np.int64)
+    _load().orc_nvfp4_frozen_sgd_step(_ptr(w), _dtype_code(w), _ptr(g), _dtype_code(g), w.size // 16, _ptr(sc),
+                                      float(tscale), float(lr), float(clip_coef), _ptr(out), _ptr(nc))
+    return out, int(nc[0])
+
+
 def w4a4_linear_fwd(x: np.ndarray, w: np.ndarray, w_scales: np.ndarray | None = None,
                     w_tscale: float | None = None):
     """W4A4 fake-quant linear: y = QDQ(x) QDQ(w)^T in binary64 (numpy matmul of
@@ -350,5 +370,5 @@ __all__ = [
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
     "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd", "nvfp4_qdq_bwd_clipped",
-    "kl_topp_fwd_bwd",
+    "kl_topp_fwd_bwd", "nvfp4_frozen_sgd_step",
 ]
