@@ -323,6 +323,32 @@ def time_clipped_ste(wl, iters=10):
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes}
 
 
+def time_sgd_step(wl, iters=10):
+    """Frozen-scale SGD step on the MoE weight batch, the clipped
+    straight-through gradient fused in (scales: the forward's, taken once
+    before timing): reads w and its gradient (2 B each per element) and the
+    block scales (1/16 B), writes the stepped weights (2 B) out of place, so
+    every timed call does the same work."""
+    import torch
+    q = wl.q
+    w, g, wo = wl.w2, wl.g2, wl.gx2
+    _, scales, ts, _ = q.nvfp4_quantize(w, codes=False, y=False, ws=wl.ws2)
+    for _ in range(2):
+        q.nvfp4_frozen_sgd_step(w, g, scales, ts, 5e-6, 1.0, w_out=wo)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        q.nvfp4_frozen_sgd_step(w, g, scales, ts, 5e-6, 1.0, w_out=wo)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 6 * w.numel() + w.numel() // 16
+    return {"shape": list(w.shape), "lr": 5e-6, "clip_coef": 1.0, "ms": round(ms, 4),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+
+
 def time_linear(wl, dev, iters=10):
     """W4A4 fake-quant linear of one MoE expert's projection: 8192 tokens of the
     activation workload (x [8192, 4096]) times expert 0 of the MoE weights
@@ -440,7 +466,8 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), "kl_topp_fwd_bwd": time_topp(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
-                         "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl)}
+                         "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl),
+                         "nvfp4_frozen_sgd_step_moe": time_sgd_step(wl)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)

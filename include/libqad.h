@@ -215,6 +215,35 @@ qad_status_t nvfp4_qdq_bwd_clipped(const void* grad_y, qad_dtype_t gt, const voi
                                    int64_t B, int64_t R, int64_t C, const uint8_t* scales,
                                    const float* tscale, void* grad_x, qad_stream_t stream);
 
+/* Frozen-scale SGD weight step, the clipped straight-through gradient fused
+ * into the update ([Lightning] "量化尺度处理策略": with frozen scales the
+ * scales stay fixed and only the weights are updated; "训练配置": a constant
+ * learning rate and gradient clipping at norm 1.0).  The pages name no
+ * optimizer; this is plain SGD, and the clipping coefficient
+ * (min(1, max_norm / global gradient norm)) is the caller's, since it needs
+ * every parameter's gradient.  With a = fl32(lr * clip_coef), element by
+ * element:
+ *   w_out = w                          where |w| > 6 * s_eff (the quantizer
+ *                                      saturates: no gradient reaches w),
+ *   w_out = round(fma32(-a, g, w))     elsewhere (one binary32 rounding, then
+ *                                      nearest-even bf16 for bf16 weights),
+ * with s_eff = fl(dec(s_b) * s_g) and the exact comparison of
+ * nvfp4_qdq_bwd_clipped.  The weight is the forward's input, so one pass
+ * reads w, g and the scales and writes w_out.
+ *   w          : device, dtype wt, [B][R][C], 16-byte aligned, finite
+ *   grad       : device, dtype gt, [B][R][C], 16-byte aligned (gradient of the
+ *                loss wrt the QDQ output)
+ *   scales     : device u8 [B][R][C/16] frozen E4M3 block scale codes (0..126)
+ *   tscale     : device float[B] frozen tensor scales (positive, finite)
+ *   lr, clip_coef : finite (QAD_ERR_INVALID_ARG otherwise)
+ *   w_out      : device, dtype wt, [B][R][C], 16-byte aligned; w_out == w is
+ *                allowed (in place); any other overlap with an input is not
+ * C % 16 == 0.  Other scale codes or tensor scales give unspecified results. */
+qad_status_t nvfp4_frozen_sgd_step(const void* w, qad_dtype_t wt, const void* grad, qad_dtype_t gt,
+                                   int64_t B, int64_t R, int64_t C, const uint8_t* scales,
+                                   const float* tscale, float lr, float clip_coef, void* w_out,
+                                   qad_stream_t stream);
+
 /* MSE calibration of the frozen block scales ([Lightning] "量化尺度处理策略":
  * the MSE scale search runs once, before training, because it is too costly
  * per step).  For each block the candidates are amax_b * k_i / 6 with k_i the

@@ -35,6 +35,8 @@ SIGNATURES = {
     "nvfp4_qdq_fwd": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_qdq_bwd": (_int, [_vp, _vp, _int, _i64, _vp]),
     "nvfp4_qdq_bwd_clipped": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_frozen_sgd_step": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, C.c_float, C.c_float, _vp,
+                                     _vp]),
     "nvfp4_mse_calibrate": (_int, [_vp, _int, _i64, _i64, _i64, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "qad_kl_fwd_bwd": (_int, [_vp, _vp, _int, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
     "qad_w4a4_linear_fwd": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -285,6 +287,28 @@ def nvfp4_qdq_bwd_clipped(grad_y: torch.Tensor, x: torch.Tensor, scales: torch.T
         _check(lib().nvfp4_qdq_bwd_clipped(_p(grad_y), _dt(grad_y), _p(x), _dt(x), B, R, Cc, _p(scales), _p(tscale),
                                            _p(grad_x), _stream(x.device)), "nvfp4_qdq_bwd_clipped")
     return grad_x
+
+
+def nvfp4_frozen_sgd_step(w: torch.Tensor, grad: torch.Tensor, scales: torch.Tensor, tscale: torch.Tensor,
+                          lr: float, clip_coef: float = 1.0, w_out: torch.Tensor | None = None) -> torch.Tensor:
+    """Frozen-scale SGD step through the clipped straight-through gradient:
+    w where |w| > 6 * s_eff, else round(fma32(-fl32(lr * clip_coef), grad, w)).
+    w and grad share the shape [R, C] or [B, R, C]; scales [.., C/16] u8,
+    tscale [B] float32.  w_out=w updates in place; None allocates."""
+    B, R, Cc = _brc(w, "w")
+    _gpu(grad, "grad", w.device, _FLOAT)
+    if tuple(grad.shape) != tuple(w.shape):
+        raise ValueError("grad and w shapes differ")
+    _gpu(scales, "scales (uint8, one code per 16 elements)", w.device, torch.uint8, B * R * (Cc // 16))
+    _gpu(tscale, "tscale (float32, one scale per tensor)", w.device, torch.float32, B)
+    w_out = _opt(w_out, "w_out", w.device, w.dtype, w.numel())
+    if w_out is None:
+        w_out = torch.empty_like(w)
+    with torch.cuda.device(w.device):
+        _check(lib().nvfp4_frozen_sgd_step(_p(w), _dt(w), _p(grad), _dt(grad), B, R, Cc, _p(scales), _p(tscale),
+                                           float(lr), float(clip_coef), _p(w_out), _stream(w.device)),
+               "nvfp4_frozen_sgd_step")
+    return w_out
 
 
 def nvfp4_mse_calibrate(w: torch.Tensor, n_candidates: int = 64, k_min: float = 0.5, k_max: float = 1.0,

@@ -315,6 +315,41 @@ qad_status_t nvfp4_qdq_bwd_clipped(const void* grad_y, qad_dtype_t gt, const voi
     return hip_status(qad::launch_qdq_bwd_clipped(a, hs(stream)));
 }
 
+qad_status_t nvfp4_frozen_sgd_step(const void* w, qad_dtype_t wt, const void* grad, qad_dtype_t gt,
+                                   int64_t B, int64_t R, int64_t C, const uint8_t* scales,
+                                   const float* tscale, float lr, float clip_coef, void* w_out,
+                                   qad_stream_t stream)
+{
+    if (!valid_dtype(wt) || !valid_dtype(gt)) return QAD_ERR_DTYPE;
+    const int64_t n = tensor_elems(B, R, C);
+    if (n < 0 || C % 16 != 0) return QAD_ERR_SHAPE;
+    if (!isfinite(lr) || !isfinite(clip_coef)) return QAD_ERR_INVALID_ARG;
+    if (n == 0) return QAD_OK;
+    if (B > (int64_t)INT32_MAX / qad::clip_chunks(R * C)) return QAD_ERR_SHAPE;
+    if (!w || !grad || !scales || !tscale || !w_out) return QAD_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(grad, 16) || !aligned(w_out, 16) || !aligned(tscale, 4))
+        return QAD_ERR_ALIGNMENT;
+    const size_t wbytes = (size_t)n * esize(wt);
+    if ((w_out != w && ranges_overlap(w, wbytes, w_out, wbytes)) ||
+        ranges_overlap(grad, (size_t)n * esize(gt), w_out, wbytes) ||
+        ranges_overlap(scales, (size_t)n / 16, w_out, wbytes) ||
+        ranges_overlap(tscale, (size_t)B * 4, w_out, wbytes))
+        return QAD_ERR_INVALID_ARG;
+    qad::SgdArgs a;
+    a.w = w;
+    a.wbf16 = wt == QAD_BF16;
+    a.grad = grad;
+    a.gbf16 = gt == QAD_BF16;
+    a.B = B;
+    a.elems = R * C;
+    a.scales = scales;
+    a.tscale = tscale;
+    a.lr = lr;
+    a.clip_coef = clip_coef;
+    a.w_out = w_out;
+    return hip_status(qad::launch_sgd_step(a, hs(stream)));
+}
+
 qad_status_t nvfp4_mse_calibrate(const void* w, qad_dtype_t wt, int64_t B, int64_t R, int64_t C,
                                  int32_t n_candidates, float k_min, float k_max, uint8_t* scales_out,
                                  float* tscale_out, void* workspace, size_t ws_bytes, qad_stream_t stream)

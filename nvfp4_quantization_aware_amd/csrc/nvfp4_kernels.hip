@@ -552,6 +552,63 @@ __global__ __launch_bounds__(kQThreads) void clip_ste_kernel(ClipArgs a, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// Frozen-scale SGD weight step ([Lightning] "量化尺度处理策略": frozen scales
+// stay fixed and only the weights move; "训练配置": a constant learning rate
+// and clipping of the gradient norm, whose coefficient the caller computed).
+// The gradient reaches the weight through the clipped straight-through
+// estimator, so a weight the quantizer saturates (|w| > 6 * s_eff, the same
+// exact test as above) keeps its value, and every other weight becomes
+// fma(-a, g, w) rounded to the weight's dtype, a = lr * clip_coef in
+// binary32.  One pass over w and g: the weight is both the quantizer's input
+// (for the clip) and the value updated.  Launch shape of the clipped backward.
+// ---------------------------------------------------------------------------
+template <bool WBF16, bool GBF16>
+__global__ __launch_bounds__(kQThreads) void sgd_step_kernel(SgdArgs a, int64_t P)
+{
+    const int64_t b = blockIdx.x / P;
+    const int64_t u0 = (blockIdx.x - b * P) * ((int64_t)kQThreads * kClipUnits);
+    const int64_t upt = a.elems >> 3;
+    const float s_g = a.tscale[b];
+    const float step = a.lr * a.clip_coef;
+    const void* w = (const char*)a.w + b * a.elems * (WBF16 ? 2 : 4);
+    const void* gr = (const char*)a.grad + b * a.elems * (GBF16 ? 2 : 4);
+    void* wo = (char*)a.w_out + b * a.elems * (WBF16 ? 2 : 4);
+    const uint8_t* sc = a.scales + b * (a.elems >> 4);
+    Raw<WBF16> wr[kClipUnits];
+    Raw<GBF16> g[kClipUnits];
+    uint32_t code[kClipUnits];
+#pragma unroll
+    for (int k = 0; k < kClipUnits; ++k) {
+        const int64_t u = u0 + k * kQThreads + threadIdx.x;
+        const bool valid = u < upt;
+        wr[k] = load_raw<WBF16>(w, u, valid);
+        g[k] = load_raw<GBF16>(gr, u, valid);
+        code[k] = valid ? sc[u >> 1] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kClipUnits; ++k) {
+        const int64_t u = u0 + k * kQThreads + threadIdx.x;
+        if (u >= upt) continue;
+        float e[8], gv[8], r[8];
+        unpack<WBF16>(wr[k], e);
+        unpack<GBF16>(g[k], gv);
+        const float s = e4m3_decode(code[k] & 127u) * s_g;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool keep = __builtin_fmaf(-6.0f, s, __builtin_fabsf(e[i])) <= 0.0f;
+            r[i] = keep ? __builtin_fmaf(-step, gv[i], e[i]) : e[i];
+        }
+        if constexpr (WBF16) {
+            stnt(wo, u, v4u{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                            pack_bf16x2(r[6], r[7])});
+        } else {
+            stnt(wo, 2 * u, v4u{as_u(r[0]), as_u(r[1]), as_u(r[2]), as_u(r[3])});
+            stnt(wo, 2 * u + 1, v4u{as_u(r[4]), as_u(r[5]), as_u(r[6]), as_u(r[7])});
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // MSE calibration of the frozen block scales ([Lightning] "量化尺度处理策略").
 // One lane per 16-element block.  The candidates amax_b * k_i / 6 rounded to
 // E4M3 are non-decreasing in i and, for grids no coarser than k_min/16 per
@@ -814,6 +871,21 @@ hipError_t launch_qdq_bwd_clipped(const ClipArgs& a, hipStream_t stream)
         if (a.xbf16) CK(false, true); else CK(false, false);
     }
 #undef CK
+    return hipGetLastError();
+}
+
+hipError_t launch_sgd_step(const SgdArgs& a, hipStream_t stream)
+{
+    if (a.B <= 0 || a.elems <= 0) return hipSuccess;
+    const int64_t P = clip_chunks(a.elems);
+    const dim3 grid((unsigned)(a.B * P)), block(kQThreads);
+#define SK(W, G) hipLaunchKernelGGL((sgd_step_kernel<W, G>), grid, block, 0, stream, a, P)
+    if (a.wbf16) {
+        if (a.gbf16) SK(true, true); else SK(true, false);
+    } else {
+        if (a.gbf16) SK(false, true); else SK(false, false);
+    }
+#undef SK
     return hipGetLastError();
 }
 

@@ -71,6 +71,22 @@ struct ClipArgs {
 int64_t clip_chunks(int64_t elems);
 hipError_t launch_qdq_bwd_clipped(const ClipArgs& a, hipStream_t stream);
 
+struct SgdArgs {
+    const void* w;             // weights before the step (the forward's input)
+    bool wbf16;
+    const void* grad;          // gradient wrt the QDQ output
+    bool gbf16;
+    int64_t B;
+    int64_t elems;             // R * C per tensor, multiple of 16
+    const uint8_t* scales;     // [B][elems/16] frozen block scale codes
+    const float* tscale;       // [B] frozen tensor scales
+    float lr;
+    float clip_coef;
+    void* w_out;               // dtype of w; may be w
+};
+// frozen-scale SGD step: launch shape of the clipped backward
+hipError_t launch_sgd_step(const SgdArgs& a, hipStream_t stream);
+
 struct MseArgs {
     const void* w;
     bool bf16;

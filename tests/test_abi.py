@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -220,6 +220,33 @@ def test_qdq_bwd_clipped_rejects(L):
     assert f(*a(R=0)) == OK                          # empty: nothing launched
 
 
+def test_frozen_sgd_step_rejects(L):
+    f = L.nvfp4_frozen_sgd_step
+    Q = 1 << 24   # far-apart fake addresses: w, grad, scales, tscale, w_out
+
+    def a(w=P, wt=1, g=P + Q, gt=1, B=2, R=4, C=32, sc=P + 2 * Q, ts=P + 3 * Q, lr=0.5, cc=1.0, wo=P + 4 * Q):
+        return w, wt, g, gt, B, R, C, sc, ts, lr, cc, wo, None
+
+    assert f(*a(wt=7)) == DTYPE
+    assert f(*a(gt=7)) == DTYPE
+    assert f(*a(C=24)) == SHAPE                      # C % 16
+    assert f(*a(B=-1)) == SHAPE
+    assert f(*a(B=1 << 31, R=1, C=16)) == SHAPE      # grid beyond 2^31 workgroups
+    assert f(*a(lr=float("nan"))) == INVALID
+    assert f(*a(cc=float("inf"))) == INVALID
+    assert f(*a(g=None)) == INVALID
+    assert f(*a(sc=None)) == INVALID
+    assert f(*a(ts=None)) == INVALID
+    assert f(*a(wo=None)) == INVALID
+    assert f(*a(w=P_ODD)) == ALIGN
+    assert f(*a(wo=P_ODD + 4 * Q)) == ALIGN
+    assert f(*a(ts=P + 3 * Q + 2)) == ALIGN
+    assert f(*a(wo=P + 64)) == INVALID               # partial overlap with w
+    assert f(*a(wo=P + Q)) == INVALID                # w_out over grad
+    assert f(*a(wo=P + 2 * Q)) == INVALID            # w_out over the scales
+    assert f(*a(R=0)) == OK                          # empty: nothing launched
+
+
 def test_amax_rejects(L):
     ws = 1 << 16
     assert L.nvfp4_amax(P, 1, 1, 4, 12, P * 2, P * 4, ws, None) == SHAPE   # 24-byte rows
@@ -359,6 +386,7 @@ def test_binding_rejects_host_tensors():
         lambda: q.nvfp4_qdq_fwd(x),
         lambda: q.nvfp4_qdq_bwd(x),
         lambda: q.nvfp4_qdq_bwd_clipped(x, x, torch.zeros(8, dtype=torch.uint8), torch.ones(1)),
+        lambda: q.nvfp4_frozen_sgd_step(x, x, torch.zeros(8, dtype=torch.uint8), torch.ones(1), 0.1),
         lambda: q.nvfp4_mse_calibrate(x),
         lambda: q.fp8_quantize(x),
         lambda: q.qad_kl_fwd_bwd(t, t),
