@@ -11,6 +11,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -381,6 +382,18 @@ static float block_sq_error(const float* xb, float s_eff)
     return err;
 }
 
+/* the n_cand values of k (any n_cand >= 1; the caller frees them) */
+static float* cand_grid(int n_cand, float k_min, float k_max)
+{
+    float* k = (float*)malloc(sizeof(float) * (size_t)(n_cand > 0 ? n_cand : 1));
+    if (!k) {
+        fprintf(stderr, "oracle: no memory for %d MSE candidates\n", n_cand);
+        abort();
+    }
+    orc_mse_kgrid(n_cand, k_min, k_max, k);
+    return k;
+}
+
 static uint8_t calibrate_one_block(const float* xb, float s_g, int n_cand,
                                    const float* k, float* best_err,
                                    uint8_t* cand_codes, float* cand_err)
@@ -407,9 +420,7 @@ void orc_mse_calibrate_blocks(const float* blocks, int64_t nblocks, float s_g,
                               uint8_t* scales, float* err_out,
                               uint8_t* cand_codes, float* cand_err)
 {
-    float k[4096];
-    if (n_cand > 4096) n_cand = 4096;
-    orc_mse_kgrid(n_cand, k_min, k_max, k);
+    float* k = cand_grid(n_cand, k_min, k_max);
     for (int64_t b = 0; b < nblocks; ++b) {
         float e;
         uint8_t sb = calibrate_one_block(blocks + b * 16, s_g, n_cand, k, &e,
@@ -418,6 +429,7 @@ void orc_mse_calibrate_blocks(const float* blocks, int64_t nblocks, float s_g,
         if (scales) scales[b] = sb;
         if (err_out) err_out[b] = e;
     }
+    free(k);
 }
 
 void orc_mse_calibrate(const void* x, int dtype, int64_t R, int64_t C,
@@ -427,14 +439,13 @@ void orc_mse_calibrate(const void* x, int dtype, int64_t R, int64_t C,
     const int64_t n = R * C, nb = n / 16;
     float s_g = orc_tensor_scale(orc_amax(x, dtype, n));
     if (tscale) *tscale = s_g;
-    float k[4096];
-    if (n_cand > 4096) n_cand = 4096;
-    orc_mse_kgrid(n_cand, k_min, k_max, k);
+    float* k = cand_grid(n_cand, k_min, k_max);
     float xb[16];
     for (int64_t b = 0; b < nb; ++b) {
         for (int j = 0; j < 16; ++j) xb[j] = load_x(x, dtype, b * 16 + j);
         scales[b] = calibrate_one_block(xb, s_g, n_cand, k, NULL, NULL, NULL);
     }
+    free(k);
 }
 
 /* ------------------------------------------------------------------------
@@ -495,6 +506,49 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
         total += kl;
     }
     return rows > 0 ? total / (double)rows : 0.0;
+}
+
+/* ------------------------------------------------------------------------
+ * The same KL loss and gradient evaluated in binary32 (expf, logf, expm1f),
+ * row by row in the order above.  TIMING VARIANT ONLY: it gives a CPU rate
+ * in the arithmetic width the GPU kernels use; no parity test compares
+ * against it (the binary64 function above is the reference).  Its test holds
+ * it to the binary64 result within binary32 accuracy.
+ * ---------------------------------------------------------------------- */
+float orc_kl_fwd_bwd_f32(const void* teacher, const void* student, int dtype,
+                         int64_t rows, int64_t V, float T, float grad_scale,
+                         float* row_kl, float* grad)
+{
+    double total = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t o = r * V;
+        float mt = -INFINITY, ms = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            float t = load_x(teacher, dtype, o + v) / T;
+            float s = load_x(student, dtype, o + v) / T;
+            if (t > mt) mt = t;
+            if (s > ms) ms = s;
+        }
+        float zt = 0.0f, zs = 0.0f;
+        for (int64_t v = 0; v < V; ++v) {
+            zt += expf(load_x(teacher, dtype, o + v) / T - mt);
+            zs += expf(load_x(student, dtype, o + v) / T - ms);
+        }
+        const float delta = (mt - ms) + logf(zt / zs);
+        float kl = 0.0f;
+        for (int64_t v = 0; v < V; ++v) {
+            float t = load_x(teacher, dtype, o + v) / T;
+            float s = load_x(student, dtype, o + v) / T;
+            float d = (t - s) - delta;
+            float p = expf(t - mt) / zt;
+            float em = expm1f(-d);
+            kl += p * (em + d);
+            if (grad) grad[o + v] = p * em * grad_scale / T;
+        }
+        if (row_kl) row_kl[r] = kl;
+        total += kl;
+    }
+    return rows > 0 ? (float)(total / (double)rows) : 0.0f;
 }
 
 /* ------------------------------------------------------------------------

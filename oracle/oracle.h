@@ -130,6 +130,11 @@ double orc_kl_fwd_bwd(const void* teacher, const void* student, int dtype,
                       int64_t rows, int64_t V, double T, double grad_scale,
                       double* row_kl, double* grad);
 
+/* ---- binary32 KL (timing variant, not a parity reference) --------------- */
+float orc_kl_fwd_bwd_f32(const void* teacher, const void* student, int dtype,
+                         int64_t rows, int64_t V, float T, float grad_scale,
+                         float* row_kl, float* grad);
+
 /* ---- teacher-top-k KL -----------------------------------------------------
  * As orc_kl_fwd_bwd restricted to S = { v : t_v >= k-th largest teacher logit
  * of the row } (ties kept), both distributions renormalised over S; gradient
@@ -147,6 +152,22 @@ double orc_kl_topp_fwd_bwd(const void* teacher, const void* student, int dtype,
                            int64_t rows, int64_t V, double top_p, double T, double grad_scale,
                            double* row_kl, double* grad, int64_t* row_count, double* row_tau,
                            double* row_mass);
+
+/* ---- all-cores harness (oracle_omp.c; benchmark CPU baseline only) -------
+ * The functions above, run with OpenMP over tensors, rows or row ranges;
+ * results equal the single-threaded calls bit for bit. */
+int    orc_omp_threads(void);
+void   orc_omp_quantize_batch(const void* x, int dtype, int64_t B, int64_t R, int64_t C,
+                              uint8_t* codes, uint8_t* scales, float* tscale, uint16_t* y);
+void   orc_omp_quantize_tensor(const void* x, int dtype, int64_t R, int64_t C, const uint8_t* scales_in,
+                               const float* tscale_in, uint8_t* codes, uint8_t* scales, float* tscale,
+                               uint16_t* y);
+void   orc_omp_mse_calibrate(const void* x, int dtype, int64_t R, int64_t C, int n_cand, float k_min,
+                             float k_max, uint8_t* scales, float* tscale);
+double orc_omp_kl_fwd_bwd(const void* teacher, const void* student, int dtype, int64_t rows, int64_t V,
+                          double T, double grad_scale, double* row_kl, double* grad);
+float  orc_omp_kl_fwd_bwd_f32(const void* teacher, const void* student, int dtype, int64_t rows, int64_t V,
+                              float T, float grad_scale, float* row_kl, float* grad);
 
 #ifdef __cplusplus
 }

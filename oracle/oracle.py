@@ -15,6 +15,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRC_OMP = os.path.join(_HERE, "oracle_omp.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD_DIR, "liboracle.so")
 _lock = threading.Lock()
@@ -24,12 +25,13 @@ F32, BF16 = 0, 1
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (strict IEEE binary32/binary64, no fusion)."""
+    """Compile oracle.c with gcc (strict IEEE binary32/binary64, no fusion),
+    with the OpenMP harness oracle_omp.c beside it."""
     os.makedirs(_BUILD_DIR, exist_ok=True)
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-               "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+               "-fPIC", "-shared", "-Wall", "-fopenmp", "-o", tmp, _SRC, _SRC_OMP, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -67,6 +69,13 @@ def _load():
             "orc_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
             "orc_kl_topk_fwd_bwd": (f64, [vp, vp, i32, i64, i64, i64, f64, f64, vp, vp, vp]),
             "orc_kl_topp_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, f64, vp, vp, vp, vp, vp]),
+            "orc_kl_fwd_bwd_f32": (f32, [vp, vp, i32, i64, i64, f32, f32, vp, vp]),
+            "orc_omp_threads": (i32, []),
+            "orc_omp_quantize_batch": (None, [vp, i32, i64, i64, i64, vp, vp, vp, vp]),
+            "orc_omp_quantize_tensor": (None, [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]),
+            "orc_omp_mse_calibrate": (None, [vp, i32, i64, i64, i32, f32, f32, vp, vp]),
+            "orc_omp_kl_fwd_bwd": (f64, [vp, vp, i32, i64, i64, f64, f64, vp, vp]),
+            "orc_omp_kl_fwd_bwd_f32": (f32, [vp, vp, i32, i64, i64, f32, f32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -365,10 +374,93 @@ def kl_topp_fwd_bwd(teacher: np.ndarray, student: np.ndarray, top_p: float, T: f
     return float(loss), row, g, cnt, tau, mass
 
 
+# ---- binary32 KL (timing variant) and the all-cores harness ----------------
+def kl_fwd_bwd_f32(teacher: np.ndarray, student: np.ndarray, T: float = 1.0, grad_scale: float | None = None):
+    """The KL loss and gradient in binary32 (a CPU timing variant, not a
+    parity reference).  Returns (mean loss, row losses f32, grad f32)."""
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    rows, V = t.shape
+    gs = 1.0 / rows if grad_scale is None else grad_scale
+    row = np.empty(rows, np.float32)
+    grad = np.empty((rows, V), np.float32)
+    loss = _load().orc_kl_fwd_bwd_f32(_ptr(t), _ptr(s), _dtype_code(t), rows, V, float(T), float(gs), _ptr(row), _ptr(grad))
+    return float(loss), row, grad
+
+
+def omp_threads() -> int:
+    return int(_load().orc_omp_threads())
+
+
+def omp_quantize_batch(x: np.ndarray):
+    """orc_nvfp4_quantize of every tensor of x [B, R, C] on all cores.
+    Returns (codes, scales, tscale [B], y bits)."""
+    x = np.ascontiguousarray(x)
+    B, R, C = x.shape
+    codes = np.empty((B, R, C // 2), np.uint8)
+    scales = np.empty((B, R, C // 16), np.uint8)
+    ts = np.empty(B, np.float32)
+    y = np.empty((B, R, C), np.uint16)
+    _load().orc_omp_quantize_batch(_ptr(x), _dtype_code(x), B, R, C, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(y))
+    return codes, scales, ts, y
+
+
+def omp_quantize_tensor(x: np.ndarray, scales_in: np.ndarray | None = None, tscale_in: float | None = None):
+    """nvfp4_quantize of one [R, C] tensor on all cores (row ranges)."""
+    x = np.ascontiguousarray(x)
+    R, C = x.shape
+    codes = np.empty((R, C // 2), np.uint8)
+    scales = np.empty((R, C // 16), np.uint8)
+    ts = np.empty(1, np.float32)
+    y = np.empty((R, C), np.uint16)
+    si = None if scales_in is None else np.ascontiguousarray(scales_in, dtype=np.uint8)
+    ti = None if tscale_in is None else np.array([tscale_in], np.float32)
+    _load().orc_omp_quantize_tensor(_ptr(x), _dtype_code(x), R, C, _ptr(si), _ptr(ti), _ptr(codes), _ptr(scales),
+                                    _ptr(ts), _ptr(y))
+    return codes, scales, float(ts[0]), y
+
+
+def omp_mse_calibrate(x: np.ndarray, n_cand: int = 64, k_min: float = 0.5, k_max: float = 1.0):
+    """mse_calibrate of one [R, C] tensor on all cores.  Returns (scales, tscale)."""
+    x = np.ascontiguousarray(x)
+    R, C = x.shape
+    scales = np.empty((R, C // 16), np.uint8)
+    ts = np.empty(1, np.float32)
+    _load().orc_omp_mse_calibrate(_ptr(x), _dtype_code(x), R, C, int(n_cand), float(k_min), float(k_max),
+                                  _ptr(scales), _ptr(ts))
+    return scales, float(ts[0])
+
+
+def omp_kl_fwd_bwd(teacher: np.ndarray, student: np.ndarray, T: float = 1.0, grad_scale: float | None = None):
+    """kl_fwd_bwd on all cores, one row per call.  Returns (mean, rows, grad)."""
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    rows, V = t.shape
+    gs = 1.0 / rows if grad_scale is None else grad_scale
+    row = np.empty(rows, np.float64)
+    grad = np.empty((rows, V), np.float64)
+    loss = _load().orc_omp_kl_fwd_bwd(_ptr(t), _ptr(s), _dtype_code(t), rows, V, float(T), float(gs), _ptr(row), _ptr(grad))
+    return float(loss), row, grad
+
+
+def omp_kl_fwd_bwd_f32(teacher: np.ndarray, student: np.ndarray, T: float = 1.0, grad_scale: float | None = None):
+    """kl_fwd_bwd_f32 on all cores, one row per call.  Returns (mean, rows, grad)."""
+    t = np.ascontiguousarray(teacher)
+    s = np.ascontiguousarray(student)
+    rows, V = t.shape
+    gs = 1.0 / rows if grad_scale is None else grad_scale
+    row = np.empty(rows, np.float32)
+    grad = np.empty((rows, V), np.float32)
+    loss = _load().orc_omp_kl_fwd_bwd_f32(_ptr(t), _ptr(s), _dtype_code(t), rows, V, float(T), float(gs), _ptr(row),
+                                          _ptr(grad))
+    return float(loss), row, grad
+
+
 __all__ = [
     "build", "F32", "BF16", "e2m1_encode", "e2m1_decode", "e4m3_encode", "e4m3_decode",
     "e4m3_decode_table", "bf16_from_f32", "f32_from_bf16", "amax", "tensor_scale",
     "nvfp4_quantize", "nvfp4_quantize_blocks", "mse_kgrid", "mse_calibrate", "mse_calibrate_blocks", "kl_fwd_bwd",
     "kl_topk_fwd_bwd", "fp8_quantize", "w4a4_linear_fwd", "w4a4_linear_bwd", "nvfp4_qdq_bwd_clipped",
-    "kl_topp_fwd_bwd", "nvfp4_frozen_sgd_step",
+    "kl_topp_fwd_bwd", "nvfp4_frozen_sgd_step", "kl_fwd_bwd_f32", "omp_threads", "omp_quantize_batch",
+    "omp_quantize_tensor", "omp_mse_calibrate", "omp_kl_fwd_bwd", "omp_kl_fwd_bwd_f32",
 ]
