@@ -480,12 +480,15 @@ __device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_
 //                 (binary64 L, Y, P), written after pass 2 on rows that take
 //                 that form;
 //   [18 W]        1 when the row takes the term-wise form (the mean kernel
-//                 then adds the shares up and forms the row's loss).
+//                 then adds the shares up and forms the row's loss);
+//   [18 W + 1 + s] claim of segment s's state by a workgroup whose wait timed
+//                 out (it then computes and publishes that state itself).
 // ---------------------------------------------------------------------------
 constexpr int kStateWords = 6;
-__host__ __device__ inline int64_t rec_words(int W) { return (18 * (int64_t)W + 1 + 31) & ~(int64_t)31; }
+__host__ __device__ inline int64_t rec_words(int W) { return (19 * (int64_t)W + 1 + 31) & ~(int64_t)31; }
 __host__ __device__ inline int64_t share_word(int W, int seg) { return 12 * (int64_t)W + 6 * seg; }
 __host__ __device__ inline int64_t flag_word(int W) { return 18 * (int64_t)W; }
+__host__ __device__ inline int64_t claim_word(int W, int seg) { return 18 * (int64_t)W + 1 + seg; }
 
 __device__ __forceinline__ float state_word(const Stats& st, int j)
 {
@@ -622,18 +625,39 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
     uint32_t* rec = rec_base + row * rec_words(W);
     Stats row_st = my_seg;
     if (W > 1) {
-        if (!collect(reinterpret_cast<const uint64_t*>(rec), W, sh.seg_words, &sh.flag, a.wait_ticks)) {
-            // timed out: compute every segment's state here, with the same
-            // lane mapping and arithmetic as its own workgroup
+        uint64_t* rec64 = reinterpret_cast<uint64_t*>(rec);
+        if (!collect(rec64, W, sh.seg_words, &sh.flag, a.wait_ticks)) {
+            // timed out: every segment still unpublished is computed -- with
+            // the same lane mapping and arithmetic as its own workgroup -- and
+            // published by the one workgroup that claims it; then all states
+            // are collected.  Each segment is by then published or being
+            // computed by a running workgroup that needs nothing from anyone,
+            // so that wait ends; and however many workgroups time out, each
+            // segment is read at most once more.
+            __syncthreads();   // every lane has read collect's flag
             for (int s = 0; s < W; ++s) {
-                const int64_t o_u0 = s * kSegSpan;
-                const Stats ol = lane_state<BF16_IN, false, false, TOPK>(o_u0, units, c, tau, [&](int k, Unit<BF16_IN>& u) {
-                    u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
-                });
-                const Stats os = group_merge<kSegThreads>(ol, sh.part);
-                if (threadIdx.x < kStateWords) sh.seg_words[kStateWords * s + threadIdx.x] = as_u(state_word(os, threadIdx.x));
+                if (threadIdx.x == 0) {
+                    bool have = true;
+                    for (int q = 0; q < kStateWords; ++q)
+                        have = have && (__hip_atomic_load(rec64 + kStateWords * s + q, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT) >> 32) != 0;
+                    uint32_t expected = 0u;
+                    sh.flag = !have && __hip_atomic_compare_exchange_strong(rec + claim_word(W, s), &expected, 1u,
+                                                                           __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+                const bool mine = sh.flag != 0u;
+                __syncthreads();
+                if (mine) {
+                    const int64_t o_u0 = s * kSegSpan;
+                    const Stats ol = lane_state<BF16_IN, false, false, TOPK>(o_u0, units, c, tau, [&](int k, Unit<BF16_IN>& u) {
+                        u.load(a, row_unit0 + lane_unit(o_u0, k), lane_unit(o_u0, k) < units);
+                    });
+                    publish(rec64, s, group_merge<kSegThreads>(ol, sh.part));
+                }
             }
-            __syncthreads();
+            collect(rec64, W, sh.seg_words, &sh.flag, ~(uint64_t)0);
         }
         row_st = merge_segments(sh.seg_words, W);
     }

@@ -42,6 +42,12 @@ __device__ __forceinline__ uint32_t a_load(const uint32_t* p) { return __hip_ato
 __device__ __forceinline__ void a_store(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ uint32_t a_max(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ uint32_t a_add(uint32_t* p, uint32_t v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// compare-and-swap: true when *p was `expected` and now holds `desired`
+__device__ __forceinline__ bool a_cas(uint32_t* p, uint32_t expected, uint32_t desired)
+{
+    return __hip_atomic_compare_exchange_strong(p, &expected, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until the value returned by a preceding atomic has arrived, i.e. the
 // atomic has been performed, before any later memory operation is issued.
 __device__ __forceinline__ void completed(uint32_t v) { asm volatile("" ::"v"(v) : "memory"); }
@@ -131,7 +137,9 @@ __device__ __forceinline__ float fp8_scale_of(uint32_t amax_bits)
 // ---------------------------------------------------------------------------
 // Per-tensor record in the workspace, used by the amax publication.
 //   word 0: tensor amax (binary32 bits), word 1: completed sub-groups
-//   sub-group s (16 consecutive chunks): words 32+32s (max), 33+32s (arrivals)
+//   sub-group s (16 consecutive chunks): words 32+32s (max), 33+32s (arrivals),
+//     34+32s (maximum found by a fallback scan | 0x80000000), 35+32s (claim
+//     of that scan)
 //   broadcast slot of chunk j: word 32 + 32*nsub + 16*j (amax | 0x80000000)
 // Every field sits on its own 64- or 128-byte line so that no address sees
 // more than ~16 atomics or one poller.  Records are zeroed before each launch.
@@ -328,14 +336,73 @@ __device__ __forceinline__ void code_chunk(const QuantizeArgs& a, const Raw<BF16
     }
 }
 
-// tensor amax by a full scan of tensor b by one workgroup (the bounded wait's
-// fallback; exact, so its result equals the published one)
+// Tensor amax after a timed-out wait (exact, so it equals the published one),
+// reading only what has not been published.  A sub-group whose arrivals are
+// complete contributes its published maximum.  Each unfinished sub-group is
+// scanned (its 16 chunks of input) by the one workgroup that claims it.  A
+// workgroup claims one sub-group at a time, looking first at its own
+// (`first`) and then onward, scans it and looks again, so that the scans of
+// many timed-out workgroups spread over the sub-groups; when none is left to
+// claim, wave 0 collects every sub-group's maximum, waiting where another
+// workgroup's scan is still running -- that scan needs nothing from anyone,
+// so the wait ends.  However many workgroups time out, each byte of the
+// tensor is read at most once more.  Returns the amax; *scanned tells whether
+// this workgroup scanned anything.  `sh` is three words of LDS.
 template <bool BF16>
-__device__ uint32_t scan_amax(const void* x, int64_t ubase, int64_t units, uint32_t* red)
+__device__ uint32_t fallback_amax(const Record& rec, const void* x, int64_t ubase, int64_t units, int first,
+                                  uint32_t* red, uint32_t* sh, bool* scanned)
 {
-    uint32_t m = 0;
-    for (int64_t u = threadIdx.x; u < units; u += kQThreads) m = umax(m, unit_absmax<BF16>(load_raw<BF16>(x, ubase + u, true)));
-    return group_max(m, red);
+    constexpr int64_t kSubUnits = 16 * Chunk<BF16>::UNITS;
+    const int t = threadIdx.x;
+    const int nsub = (int)rec.nsub, chunks = (int)rec.chunks;   // at most 64 and 1024 on this path
+    *scanned = false;
+    for (;;) {
+        if (t == 0) {
+            int claim = -1;
+            int sg = first;
+            for (int i = 0; i < nsub && claim < 0; ++i, sg = sg + 1 == nsub ? 0 : sg + 1) {
+                uint32_t* sw = rec.w + 32 + 32 * sg;
+                const uint32_t members = (uint32_t)(chunks - sg * 16 < 16 ? chunks - sg * 16 : 16);
+                if (a_load(sw + 3) != 0u || a_load(sw + 1) == members) continue;   // claimed, or complete
+                if (a_cas(sw + 3, 0u, 1u)) claim = sg;
+            }
+            sh[0] = (uint32_t)(claim + 1);
+        }
+        __syncthreads();
+        const int sg = (int)sh[0] - 1;
+        __syncthreads();
+        if (sg < 0) break;
+        *scanned = true;
+        const int64_t u0 = sg * kSubUnits;
+        const int n = (int)((u0 + kSubUnits < units ? u0 + kSubUnits : units) - u0);
+        uint32_t m = 0;
+        for (int u = t; u < n; u += kQThreads) m = umax(m, unit_absmax<BF16>(load_raw<BF16>(x, ubase + u0 + u, true)));
+        m = group_max(m, red);
+        if (t == 0) a_store(rec.w + 32 + 32 * sg + 2, m | 0x80000000u);
+    }
+    if (t < 64) {
+        uint32_t am = 0;
+        for (int sg = t; sg < nsub; sg += 64) {
+            uint32_t* sw = rec.w + 32 + 32 * sg;
+            const uint32_t members = (uint32_t)(chunks - sg * 16 < 16 ? chunks - sg * 16 : 16);
+            for (;;) {
+                if (a_load(sw + 1) == members) {
+                    am = umax(am, a_load(sw));
+                    break;
+                }
+                const uint32_t sc = a_load(sw + 2);
+                if (sc & 0x80000000u) {
+                    am = umax(am, sc & 0x7FFFFFFFu);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        am = wave_max_u32(am);
+        if (t == 0) sh[2] = am;
+    }
+    __syncthreads();
+    return sh[2];
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +427,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
     using CH = Chunk<BF16>;
     __shared__ ScaleTable tab;
     __shared__ uint32_t red[kQThreads / 64];
-    __shared__ uint32_t sh_bcast, sh_amax;
+    __shared__ uint32_t sh_bcast, sh_amax, sh_fb[3];
     const int64_t c = blockIdx.x;
     const int64_t b = c / P, j = c - b * P;
     const int64_t units = a.elems >> 3;
@@ -374,11 +441,6 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         const int64_t u = u0 + k * kQThreads + t;
         raw[k] = load_raw<BF16>(a.x, ubase + u, u < units);
     }
-    // each unit's largest magnitude (binary32 bits), from the packed data
-    uint32_t unit_max[CH::U];
-#pragma unroll
-    for (int k = 0; k < CH::U; ++k) unit_max[k] = unit_absmax<BF16>(raw[k]);
-
     float s_g;
     if constexpr (MODE == MODE_FROZEN) {
         s_g = a.tscale_in[b];
@@ -389,7 +451,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         const Record rec(ws, b, P);
         uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < CH::U; ++k) m = umax(m, unit_max[k]);
+        for (int k = 0; k < CH::U; ++k) m = umax(m, unit_absmax<BF16>(raw[k]));
         m = group_max(m, red);
         if (t == 0) sh_bcast = publish_max(rec, j, m) ? (a_load(rec.w) | 0x80000000u) : 0u;
         __syncthreads();
@@ -407,11 +469,28 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
         }
         __syncthreads();
         uint32_t am = sh_amax;
-        if (!(am & 0x80000000u)) am = scan_amax<BF16>(a.x, ubase, units, red); // timed out
+        if (!(am & 0x80000000u)) {
+            // timed out: the amax from what is published plus scans of the rest
+            bool scanned;
+            am = fallback_amax<BF16>(rec, a.x, ubase, units, (int)(j / 16), red, sh_fb, &scanned) | 0x80000000u;
+            if (scanned)   // a workgroup that scanned broadcasts, so that no chunk waits any longer
+                for (int64_t i = t; i < P; i += kQThreads) a_store(rec.slot(i), am);
+            // the chunk is read again rather than held across this rare path,
+            // which leaves the fallback the registers the chunk occupied
+#pragma unroll
+            for (int k = 0; k < CH::U; ++k) {
+                const int64_t u = u0 + k * kQThreads + t;
+                raw[k] = load_raw<BF16>(a.x, ubase + u, u < units);
+            }
+        }
         s_g = FP8 ? fp8_scale_of(am & 0x7FFFFFFFu) : tensor_scale_of(am & 0x7FFFFFFFu);
     }
     if (!FP8) build_table(tab, s_g);
     if (j == 0 && t == 0 && a.tscale_out) a.tscale_out[b] = s_g;
+    // each unit's largest magnitude (binary32 bits), from the packed data
+    uint32_t unit_max[CH::U];
+#pragma unroll
+    for (int k = 0; k < CH::U; ++k) unit_max[k] = unit_absmax<BF16>(raw[k]);
     __syncthreads();
     if (s_g >= kFastMinScale) code_chunk<BF16, MODE, true, FP8>(a, raw, unit_max, ubase, u0, units, tab, s_g);
     else code_chunk<BF16, MODE, false, FP8>(a, raw, unit_max, ubase, u0, units, tab, s_g);

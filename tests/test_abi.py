@@ -75,7 +75,7 @@ def test_workspace_sizes(L):
     for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20), (3, (1 << 20) + 8),
                           (3, 1 << 22)):
         W = -(-vocab // 16384)
-        rec = ((18 * W + 1 + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
+        rec = ((19 * W + 1 + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
         expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
         assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
     # top-k KL: the KL workspace, then one float per row (thresholds)

@@ -56,3 +56,34 @@ def test_wait_fallbacks_bit_identical(dev):
     for i, (a, b) in enumerate(zip(got, ref)):
         assert a.dtype == b.dtype and a.shape == b.shape, i
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (i, tuple(a.shape), a.dtype)
+
+
+def test_wait_fallbacks_many_subgroups_and_segments(dev):
+    # tensors of many 16-chunk sub-groups with a ragged last chunk (bf16 and
+    # fp32), and logit rows of 9 segments with a ragged last one: the
+    # cooperative fallbacks claim and scan sub-groups / segments from several
+    # workgroups at once; results must not change
+    w, _ = synth.moe_weights_bf16(experts=3, rows=1000, cols=4112, seed=9, with_grad=False)
+    t, s = synth.logits_bf16(tokens=16, vocab=131072 + 8, seed=10)
+    w, t, s = w.to(dev), t.to(dev), s.to(dev)
+
+    def run():
+        out = list(q.nvfp4_quantize(w)) + list(q.nvfp4_quantize(w.float()))
+        out += list(q.fp8_quantize(w))
+        out += list(q.qad_kl_fwd_bwd(t, s, row_loss=True))
+        out += list(q.qad_kl_topk_fwd_bwd(t, s, 4096, row_loss=True))
+        return [o for o in out if o is not None]
+
+    announce("fallback many sub-groups: normal path")
+    ref = run()
+    torch.cuda.synchronize()
+    prev = q.set_wait_limit_us(0)
+    try:
+        announce("fallback many sub-groups: every wait gives up at once")
+        got = run()
+        torch.cuda.synchronize()
+    finally:
+        q.set_wait_limit_us(prev)
+    assert len(got) == len(ref)
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (i, tuple(a.shape), a.dtype)
