@@ -15,8 +15,10 @@ in HBM, in the launch configuration the parity tests check:
           N(0,0.5^2), T = 1.
 `value` is the step's algorithmic HBM bytes (every input read once, every
 output written once) divided by the step time.  Per-part times come from HIP
-events recorded on the stream the kernels run on.  The CPU baseline times the
-CPU oracle, single-threaded, on a bounded sample of the same workload.
+events recorded on the stream the kernels run on.  The smallest configuration
+(one fp32 256 x 1024 tensor) is timed on its own, in microseconds.  The CPU
+baseline times the CPU oracle, single-threaded and on all host cores, on a
+bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -160,8 +162,11 @@ def _host_cpu():
 
 
 def cpu_baseline(fraction: float):
-    """The CPU oracle (single-threaded C) on `fraction` of one step: the same
-    share of every part, so its GB/s compares directly with the GPU step."""
+    """The CPU oracle on `fraction` of one step (the same share of every part,
+    so its GB/s compares directly with the GPU step): single-threaded, then
+    the same oracle functions with OpenMP over tensors / rows on every host
+    core (oracle/oracle_omp.c).  Also the KL in binary32 (the oracle's timing
+    variant), one core and all cores, on a sample of the KL rows."""
     import numpy as np
     import oracle
     from nvfp4_quantization_aware_amd import synth
@@ -171,12 +176,14 @@ def cpu_baseline(fraction: float):
     rows3 = max(16, round(32768 * fraction))
     rows4 = max(16, round(8192 * fraction))
     rows5 = max(2, round(8192 * fraction))
-    parts = {}
+    rows_f32 = max(2, rows5 // 8)
+    one, omp = {}, {}
 
-    def timed(name, fn, nbytes):
+    def timed(store, name, fn, nbytes):
         t0 = time.perf_counter()
-        fn()
-        parts[name] = (time.perf_counter() - t0, nbytes)
+        r = fn()
+        store[name] = (time.perf_counter() - t0, nbytes)
+        return r
 
     w, g = synth.moe_weights_bf16(experts, 2048, 4096, seed=2)
     w, g = bits(w), bits(g)
@@ -185,43 +192,150 @@ def cpu_baseline(fraction: float):
         for e in range(experts):
             oracle.nvfp4_quantize(w[e])
 
-    timed("moe_qdq_fwd", moe_fwd, 4 * w.size)
-    timed("moe_ste_bwd", lambda: np.copy(g), 4 * g.size)   # the oracle's STE is the identity
+    timed(one, "moe_qdq_fwd", moe_fwd, 4 * w.size)
+    timed(one, "moe_ste_bwd", lambda: np.copy(g), 4 * g.size)   # the oracle's STE is the identity
+    timed(omp, "moe_qdq_fwd", lambda: oracle.omp_quantize_batch(w), 4 * w.size)
+    timed(omp, "moe_ste_bwd", lambda: np.copy(g), 4 * g.size)
     del w, g
     x, g3 = synth.student_t_activations_bf16(rows3, 4096, seed=3)
     x, g3 = bits(x), bits(g3)
-    timed("act_qdq_fwd", lambda: oracle.nvfp4_quantize(x), 4 * x.size)
-    timed("act_ste_bwd", lambda: np.copy(g3), 4 * g3.size)
+    timed(one, "act_qdq_fwd", lambda: oracle.nvfp4_quantize(x), 4 * x.size)
+    timed(one, "act_ste_bwd", lambda: np.copy(g3), 4 * g3.size)
+    timed(omp, "act_qdq_fwd", lambda: oracle.omp_quantize_tensor(x), 4 * x.size)
+    timed(omp, "act_ste_bwd", lambda: np.copy(g3), 4 * g3.size)
     del x, g3
     w4 = bits(synth.gaussian_weight_bf16(rows4, 8192, seed=4))
-    cal = {}
-
-    def mse():
-        cal["s"] = oracle.mse_calibrate(w4)
-
-    timed("mse_calibrate", mse, 2 * w4.size + w4.size // 16)
-    timed("mse_frozen_qdq", lambda: oracle.nvfp4_quantize(w4, cal["s"][0], cal["s"][1]),
-          2 * w4.size + w4.size // 16 + 2 * w4.size)
+    b_cal, b_qdq = 2 * w4.size + w4.size // 16, 2 * w4.size + w4.size // 16 + 2 * w4.size
+    sc, ts = timed(one, "mse_calibrate", lambda: oracle.mse_calibrate(w4), b_cal)
+    timed(one, "mse_frozen_qdq", lambda: oracle.nvfp4_quantize(w4, sc, ts), b_qdq)
+    sc, ts = timed(omp, "mse_calibrate", lambda: oracle.omp_mse_calibrate(w4), b_cal)
+    timed(omp, "mse_frozen_qdq", lambda: oracle.omp_quantize_tensor(w4, sc, ts), b_qdq)
     del w4
     t5, s5 = synth.logits_bf16(rows5, 131072, seed=5)
     t5, s5 = bits(t5), bits(s5)
-    timed("kl_fwd_bwd", lambda: oracle.kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
-    secs = sum(t for t, _ in parts.values())
-    nbytes = sum(b for _, b in parts.values())
+    timed(one, "kl_fwd_bwd", lambda: oracle.kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
+    timed(omp, "kl_fwd_bwd", lambda: oracle.omp_kl_fwd_bwd(t5, s5, grad_scale=1.0 / 8192), 6 * t5.size)
+    kl32 = {}
+    timed(kl32, "one", lambda: oracle.kl_fwd_bwd_f32(t5[:rows_f32], s5[:rows_f32], grad_scale=1.0 / 8192), 0)
+    timed(kl32, "omp", lambda: oracle.omp_kl_fwd_bwd_f32(t5, s5, grad_scale=1.0 / 8192), 0)
+
+    def rate(store):
+        secs = sum(t for t, _ in store.values())
+        return secs, sum(b for _, b in store.values()) / secs / 1e9
+
+    secs1, gbs1 = rate(one)
+    secs_n, gbs_n = rate(omp)
+    cores = oracle.omp_threads()
     return {
-        "value": round(nbytes / secs / 1e9, 4),
+        "value": round(gbs1, 4),
         "unit": "GB/s",
         "cores": 1,
         "host": _host_cpu(),
         "kind": "oracle",
-        "seconds": round(secs, 2),
-        "part_seconds": {k: round(v[0], 3) for k, v in parts.items()},
-        "kl_tokens_per_s": round(rows5 / parts["kl_fwd_bwd"][0], 2),
+        "seconds": round(secs1, 2),
+        "part_seconds": {k: round(v[0], 3) for k, v in one.items()},
+        "kl_tokens_per_s": round(rows5 / one["kl_fwd_bwd"][0], 2),
+        "all_cores": {"value": round(gbs_n, 4), "unit": "GB/s", "cores": cores, "kind": "oracle (OpenMP)",
+                      "seconds": round(secs_n, 2), "part_seconds": {k: round(v[0], 3) for k, v in omp.items()},
+                      "kl_tokens_per_s": round(rows5 / omp["kl_fwd_bwd"][0], 2)},
+        "kl_binary32": {"tokens_per_s_1_core": round(rows_f32 / kl32["one"][0], 2),
+                        "tokens_per_s_all_cores": round(rows5 / kl32["omp"][0], 2), "cores": cores,
+                        "rows": {"1_core": rows_f32, "all_cores": rows5}},
         "sample": ("1/%d of one step, every part in proportion: %d of 128 experts QDQ + STE copy, %d of "
                    "32768 activation rows QDQ + STE copy, %d of 8192 rows MSE calibration + frozen QDQ, "
-                   "%d of 8192 KL rows fwd+bwd (binary64); same generators and seeds as the GPU workload"
-                   % (round(1 / fraction), experts, rows3, rows4, rows5)),
+                   "%d of 8192 KL rows fwd+bwd (binary64); same generators and seeds as the GPU workload; "
+                   "binary32 KL on %d rows (1 core) and %d rows (all cores)"
+                   % (round(1 / fraction), experts, rows3, rows4, rows5, rows_f32, rows5)),
     }
+
+
+def time_c1(dev, iters=200):
+    """The smallest configuration: dynamic NVFP4 quantization of one fp32
+    256 x 1024 tensor (N(0,1), 0.1% outliers x50) emitting packed codes,
+    block scales, the tensor scale and bf16 values.  1.7 MB of traffic takes
+    about 0.2 us at peak bandwidth, so the call is bound by launch latency:
+    reported in microseconds (median of single timed calls, and the mean of
+    back-to-back calls) and GB/s, outside the step's value."""
+    import torch
+    import nvfp4_quantization_aware_amd as q
+    from nvfp4_quantization_aware_amd import synth
+    x = synth.outlier_tensor_f32(256, 1024, seed=1, device=dev).unsqueeze(0)
+    n = x.numel()
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    ws = q.workspace(q.QAD_OP_QUANTIZE, 1, 256, 1024, dev)
+    f = lambda: q.nvfp4_quantize(x, codes=codes, scales_out=scales, tscale_out=ts, y=y, ws=ws)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    singles = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        singles.append(e0.elapsed_time(e1) * 1e3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    mean_us = e0.elapsed_time(e1) * 1e3 / iters
+    med_us = sorted(singles)[len(singles) // 2]
+    nbytes = 4 * n + n // 2 + n // 16 + 4 + 2 * n
+    return {"shape": [256, 1024], "dtype": "f32", "bytes": nbytes, "us_median_single": round(med_us, 2),
+            "us_mean_back_to_back": round(mean_us, 2), "GB/s": round(nbytes / (med_us * 1e-6) / 1e9, 1),
+            "bound": "launch latency"}
+
+
+def time_wait0(wl, iters=5):
+    """The one-pass kernels with every device-side wait giving up at once
+    (qad_set_wait_limit_us(0)): what the exact fallbacks cost when other work
+    keeps workgroups from being resident together.  The MoE QDQ forward and
+    the KL forward + backward of the step, next to their normal times."""
+    import torch
+    q = wl.q
+    calls = {"moe_qdq_fwd": lambda: q.nvfp4_qdq_fwd(wl.w2, y=wl.y2, ws=wl.ws2),
+             "kl_fwd_bwd": lambda: q.qad_kl_fwd_bwd(wl.t5, wl.s5, loss_out=wl.l5, grad=wl.gr5, ws=wl.ws5)}
+    out = {}
+    for name, f in calls.items():
+        res = {}
+        for label, limit in (("normal_ms", None), ("wait0_ms", 0)):
+            prev = q.set_wait_limit_us(limit) if limit is not None else None
+            try:
+                f()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(iters):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+            finally:
+                if prev is not None:
+                    q.set_wait_limit_us(prev)
+            res[label] = round(e0.elapsed_time(e1) / iters, 4)
+        res["ratio"] = round(res["wait0_ms"] / res["normal_ms"], 3)
+        out[name] = res
+    return out
+
+
+def act_accountings(parts):
+    """The activation path (forward QDQ + straight-through backward) under its
+    two byte accountings: each tensor read or written once (1 GiB), and with
+    the amax pass's second read of the 256 MiB input counted (1.25 GiB)."""
+    ms = parts["act_qdq_fwd"]["ms"] + parts["act_ste_bwd"]["ms"]
+    uniq = parts["act_qdq_fwd"]["bytes"] + parts["act_ste_bwd"]["bytes"]
+    reread = uniq + parts["act_qdq_fwd"]["bytes"] // 2
+    out = {"ms": round(ms, 4)}
+    for name, b in (("unique_1GiB", uniq), ("with_amax_reread_1.25GiB", reread)):
+        gbs = b / (ms * 1e-3) / 1e9
+        out[name] = {"bytes": b, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def time_topk(wl, dev, k=4096, iters=10):
@@ -460,6 +574,7 @@ def main():
         "nvfp4_qdq_GBps": round(qdq_bytes / (qdq_ms * 1e-3) / 1e9, 1),
         "kl_tokens_per_s": round(kl_tokens_s, 1),
         "parts": parts,
+        "act_fwd_bwd": act_accountings(parts),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
@@ -467,7 +582,9 @@ def main():
     }
     out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), "kl_topp_fwd_bwd": time_topp(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
                          "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl),
-                         "nvfp4_frozen_sgd_step_moe": time_sgd_step(wl)}
+                         "nvfp4_frozen_sgd_step_moe": time_sgd_step(wl),
+                         "c1_fp32_quantize_256x1024": time_c1(dev),
+                         "wait0_fallbacks": time_wait0(wl)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
