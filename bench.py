@@ -476,13 +476,14 @@ def time_linear(wl, dev, iters=10):
     N = w.shape[0]
     ws = q.workspace(q.QAD_OP_W4A4_LINEAR, M, N, K, dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty(q.nvfp4_packed_bytes(M, K), dtype=torch.uint8, device=dev)
+    wq = torch.empty(q.nvfp4_packed_bytes(N, K), dtype=torch.uint8, device=dev)
     gy = torch.empty((M, N), dtype=torch.bfloat16, device=dev).normal_(0, 1e-3)
-    gx, gw = torch.empty_like(xq), torch.empty_like(wq)
+    gx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    gw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     res = {"shape_MNK": [M, N, K], "peak_TFLOPs_bf16": 2500.0}
     for name, f, flops in (("fwd", lambda: q.qad_w4a4_linear_fwd(x, w, y=y, xq=xq, wq=wq, ws=ws), 2 * M * N * K),
-                           ("bwd", lambda: q.qad_w4a4_linear_bwd(gy, xq, wq, grad_x=gx, grad_w=gw, ws=ws),
+                           ("bwd", lambda: q.qad_w4a4_linear_bwd(gy, xq, wq, K, grad_x=gx, grad_w=gw),
                             4 * M * N * K)):
         for _ in range(2):
             f()

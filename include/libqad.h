@@ -285,6 +285,13 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
                           const float* tscale_in, uint8_t* codes, float* tscale_out, void* y,
                           void* workspace, size_t ws_bytes, qad_stream_t stream);
 
+/* Bytes of a packed NVFP4 tensor of R x C elements (C % 16 == 0), the
+ * W4A4 linear's saved operand form: the E2M1 codes (R*C/2 bytes, row-major,
+ * even element in the low nibble), then the E4M3 block scales (R*C/16 bytes,
+ * row-major) at byte R*C/2, then the fp32 tensor scale at the next multiple
+ * of 16 bytes.  0 for invalid sizes. */
+size_t qad_nvfp4_packed_bytes(int64_t R, int64_t C);
+
 /* W4A4 NVFP4 fake-quant linear layer ([Qwen] "3. QAD": the student is the
  * W4A4 NVFP4 model, weights and activations both NVFP4; [Lightning]
  * "QAD的工作原理": simulated quantization in every student forward).
@@ -293,36 +300,37 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  *             for w dynamic scales too, or the frozen ones given
  *             ([Lightning] "量化尺度处理策略": frozen-scale QAD keeps the
  *             MSE-calibrated weight scales fixed while the weights train);
- *             bf16 product of the bf16 QDQ values with fp32 accumulation
- *             (MFMA, hipBLASLt)
+ *             each output is the bf16 rounding of an fp32 sum of the bf16
+ *             QDQ values' products.  x and w are quantized once each into
+ *             packed NVFP4 operands (qad_nvfp4_packed_bytes); the product
+ *             reads those and rebuilds the bf16 QDQ values on chip (the
+ *             library's own MFMA kernel; no other library is called and the
+ *             call never synchronises).
  *   x, w    : device, dtype dt, row-major, 16-byte aligned; K > 0, K % 16 == 0
  *   w_scales_in, w_tscale_in : device u8 [N][K/16] and float[1], frozen
  *             scales of w (as from nvfp4_mse_calibrate), or both NULL
- *   y       : device bf16 [M][N]; xq, wq: device bf16 [M][K], [N][K]
- *             receive QDQ(x), QDQ(w) (kept for the backward); no output may
- *             overlap another or an input
- *   workspace : qad_workspace_bytes(QAD_OP_W4A4_LINEAR, M, N, K) bytes
- * M == 0 or N == 0: y is empty and the other operand's QDQ output (xq or wq)
- * is still written; pointers of empty buffers may be NULL.
- * The library keeps one hipBLASLt handle per device, created on first use;
- * hipBLASLt's scratch comes from the workspace.  The first call of a shape
- * on a device times up to 16 of hipBLASLt's candidate algorithms on the
- * call's own operands (one synchronisation of `stream`) and keeps the
- * fastest for every later call of that shape; under graph capture it takes
- * the heuristic's first candidate untimed.  Another process may choose
- * another algorithm: results then differ within the fp32 accumulation
- * bound, not bit for bit. */
+ *   y       : device bf16 [M][N]
+ *   xq, wq  : device, qad_nvfp4_packed_bytes(M, K) and (N, K) bytes, 16-byte
+ *             aligned: receive the packed NVFP4 forms of x and w (kept for the
+ *             backward); no output may overlap another or an input
+ *   workspace : qad_workspace_bytes(QAD_OP_W4A4_LINEAR, M, N, K) bytes (the
+ *             quantizer's records)
+ * M == 0 or N == 0: y is empty and the other operand's packed form (xq or
+ * wq) is still written; pointers of empty buffers may be NULL.  The fp32
+ * sums are formed in a fixed order, so results are reproducible bit for bit. */
 qad_status_t qad_w4a4_linear_fwd(const void* x, const void* w, qad_dtype_t dt, int64_t M, int64_t N, int64_t K,
                                  const uint8_t* w_scales_in, const float* w_tscale_in, void* y, void* xq, void* wq,
                                  void* workspace, size_t ws_bytes, qad_stream_t stream);
 
 /* Backward of qad_w4a4_linear_fwd with the straight-through estimator through
- * both quantizers: grad_x[M][K] = grad_y[M][N] * wq[N][K] and
- * grad_w[N][K] = grad_y^T * xq[M][K] (bf16, fp32 accumulation).
- *   grad_y : device bf16 [M][N]; xq, wq: the forward's QDQ outputs
+ * both quantizers: grad_x[M][K] = grad_y[M][N] * QDQ(w)[N][K] and
+ * grad_w[N][K] = grad_y^T * QDQ(x)[M][K] (bf16 of fp32 sums), QDQ(x), QDQ(w)
+ * rebuilt on chip from the forward's packed operands.
+ *   grad_y : device bf16 [M][N], 16-byte aligned; xq, wq: the forward's
+ *            packed operands
  *   grad_x, grad_w : device bf16 outputs, either may be NULL (not both,
  *                    unless both are empty)
- *   workspace : as for the forward
+ *   workspace, ws_bytes : unused (may be NULL / 0)
  * M == 0 or N == 0 writes zeros to the other gradient. */
 qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void* wq, int64_t M, int64_t N, int64_t K,
                                  void* grad_x, void* grad_w, void* workspace, size_t ws_bytes, qad_stream_t stream);

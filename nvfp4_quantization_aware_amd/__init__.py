@@ -7,7 +7,7 @@ the seeded synthetic input generators.  Build with
 """
 from ._lib import (QAD_BF16, QAD_F32, QAD_OP_AMAX, QAD_OP_KL, QAD_OP_KL_TOPK, QAD_OP_KL_TOPP, QAD_OP_W4A4_LINEAR,  # noqa: F401
                    QAD_OP_MSE_CALIBRATE, QAD_OP_QUANTIZE, QadError, fp8_quantize, lib, nvfp4_amax, nvfp4_frozen_sgd_step,
-                   nvfp4_mse_calibrate,
+                   nvfp4_mse_calibrate, nvfp4_packed_bytes, nvfp4_unpack,
                    nvfp4_qdq_bwd, nvfp4_qdq_bwd_clipped, nvfp4_qdq_fwd, nvfp4_quantize, nvfp4_quantize_noalloc,
                    qad_check_finite,
                    qad_kl_fwd_bwd, qad_kl_topk_fwd_bwd, qad_kl_topp_fwd_bwd, qad_w4a4_linear_bwd, qad_w4a4_linear_fwd,

@@ -29,6 +29,7 @@ SIGNATURES = {
     "qad_abi_version": (_int, []),
     "qad_set_wait_limit_us": (_i64, [_i64]),
     "qad_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
+    "qad_nvfp4_packed_bytes": (_sz, [_i64, _i64]),
     "nvfp4_amax": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_noalloc": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -384,22 +385,36 @@ def fp8_quantize(x: torch.Tensor, tscale_in: torch.Tensor | None = None, codes=T
     return cd, tscale_out, yy
 
 
+def nvfp4_packed_bytes(R: int, C: int) -> int:
+    """Bytes of a packed NVFP4 tensor (codes, block scales, tensor scale) of R x C."""
+    return int(lib().qad_nvfp4_packed_bytes(R, C))
+
+
+def nvfp4_unpack(packed: torch.Tensor, R: int, C: int):
+    """Views of a packed NVFP4 tensor: (codes u8 [R, C/2], scales u8 [R, C/16],
+    tensor scale f32 [1])."""
+    n = R * C
+    toff = (n // 2 + n // 16 + 15) // 16 * 16
+    return (packed[:n // 2].view(R, C // 2), packed[n // 2:n // 2 + n // 16].view(R, C // 16),
+            packed[toff:toff + 4].view(torch.float32))
+
+
 def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=None, ws: torch.Tensor | None = None,
                         w_scales_in: torch.Tensor | None = None, w_tscale_in: torch.Tensor | None = None):
     """y = QDQ(x) QDQ(w)^T (bf16) for x [M, K], w [N, K]; w's scales are
     dynamic, or the frozen w_scales_in (u8 [N, K/16]) / w_tscale_in (f32 [1]).
-    Returns (y, xq, wq)."""
+    Returns (y, xq, wq): xq, wq the packed NVFP4 forms of x and w (uint8,
+    nvfp4_packed_bytes each; nvfp4_unpack gives their parts)."""
     _gpu(x, "x", dtype=_FLOAT)
     _gpu(w, "w", x.device, x.dtype)
     if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
         raise ValueError("x [M, K] and w [N, K] of one dtype")
     (M, K), N = x.shape, w.shape[0]
     dev = x.device
+    bx, bw = nvfp4_packed_bytes(M, K), nvfp4_packed_bytes(N, K)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else _gpu(y, "y", dev, torch.bfloat16, M * N)
-    xq = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if xq is None else _gpu(xq, "xq", dev, torch.bfloat16,
-                                                                                        M * K)
-    wq = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if wq is None else _gpu(wq, "wq", dev, torch.bfloat16,
-                                                                                        N * K)
+    xq = torch.empty(bx, dtype=torch.uint8, device=dev) if xq is None else _gpu(xq, "xq", dev, torch.uint8, bx)
+    wq = torch.empty(bw, dtype=torch.uint8, device=dev) if wq is None else _gpu(wq, "wq", dev, torch.uint8, bw)
     ws = _ws(ws, dev)
     w_scales_in = _opt(w_scales_in, "w_scales_in", dev)
     w_tscale_in = _opt(w_tscale_in, "w_tscale_in", dev)
@@ -412,33 +427,29 @@ def qad_w4a4_linear_fwd(x: torch.Tensor, w: torch.Tensor, y=None, xq=None, wq=No
         raise ValueError("w_scales_in must be uint8 [N, K/16] and w_tscale_in float32 [1]")
     with torch.cuda.device(dev):
         _check(lib().qad_w4a4_linear_fwd(_p(x), _p(w), _dt(x), M, N, K, _p(w_scales_in), _p(w_tscale_in), _p(y), _p(xq),
-                                         _p(wq), _p(ws), ws.numel(), _stream(dev)), "qad_w4a4_linear_fwd")
+                                         _p(wq), _p(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+               "qad_w4a4_linear_fwd")
     return y, xq, wq
 
 
-def qad_w4a4_linear_bwd(grad_y: torch.Tensor, xq: torch.Tensor, wq: torch.Tensor, grad_x=True, grad_w=True,
-                        ws: torch.Tensor | None = None):
-    """Straight-through backward: returns (grad_x [M, K] or None, grad_w [N, K] or None)."""
+def qad_w4a4_linear_bwd(grad_y: torch.Tensor, xq: torch.Tensor, wq: torch.Tensor, K: int, grad_x=True, grad_w=True):
+    """Straight-through backward from the forward's packed operands xq, wq
+    (for x [M, K], w [N, K]): returns (grad_x [M, K] or None, grad_w [N, K]
+    or None)."""
     _gpu(grad_y, "grad_y", dtype=torch.bfloat16)
     dev = grad_y.device
-    _gpu(xq, "xq", dev, torch.bfloat16)
-    _gpu(wq, "wq", dev, torch.bfloat16)
-    if grad_y.dim() != 2 or xq.dim() != 2 or wq.dim() != 2:
-        raise ValueError("grad_y [M, N], xq [M, K] and wq [N, K]")
+    if grad_y.dim() != 2:
+        raise ValueError("grad_y [M, N]")
     M, N = grad_y.shape
-    K = xq.shape[1]
-    if xq.shape[0] != M or tuple(wq.shape) != (N, K):
-        raise ValueError("grad_y [M, N], xq [M, K] and wq [N, K]")
+    _gpu(xq, "xq", dev, torch.uint8, nvfp4_packed_bytes(M, K))
+    _gpu(wq, "wq", dev, torch.uint8, nvfp4_packed_bytes(N, K))
     gx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if grad_x is True else (
         _gpu(grad_x, "grad_x", dev, torch.bfloat16, M * K) if isinstance(grad_x, torch.Tensor) else None)
     gw = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if grad_w is True else (
         _gpu(grad_w, "grad_w", dev, torch.bfloat16, N * K) if isinstance(grad_w, torch.Tensor) else None)
-    ws = _ws(ws, dev)
-    if ws is None:
-        ws = workspace(QAD_OP_W4A4_LINEAR, M, N, K, dev)
     with torch.cuda.device(dev):
-        _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), _p(ws), ws.numel(),
-                                         _stream(dev)), "qad_w4a4_linear_bwd")
+        _check(lib().qad_w4a4_linear_bwd(_p(grad_y), _p(xq), _p(wq), M, N, K, _p(gx), _p(gw), None, 0, _stream(dev)),
+               "qad_w4a4_linear_bwd")
     return gx, gw
 
 

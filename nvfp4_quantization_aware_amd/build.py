@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libqad.so")
 SOURCES = ["libqad.hip", "nvfp4_kernels.hip", "kl_kernels.hip", "linear.hip"]
-LIBS = ["-lhipblaslt"]
+LIBS = []
 ARCH = "gfx950"
 
 

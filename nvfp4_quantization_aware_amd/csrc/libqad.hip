@@ -195,7 +195,7 @@ const char* qad_status_string(qad_status_t status)
     return "unknown qad_status_t";
 }
 
-int qad_abi_version(void) { return 1; }
+int qad_abi_version(void) { return 2; }
 
 int64_t qad_set_wait_limit_us(int64_t us)
 {

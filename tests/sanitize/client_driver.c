@@ -31,7 +31,7 @@ int main(void)
     char* ODD = P + 2;
     const qad_dtype_t BAD = (qad_dtype_t)7;
 
-    if (qad_abi_version() != 1) ++failures;
+    if (qad_abi_version() != 2) ++failures;
     for (int s = 0; s <= 8; ++s) if (!qad_status_string((qad_status_t)s)) ++failures;
     for (int op = 0; op <= 7; ++op) (void)qad_workspace_bytes((qad_op_t)op, 3, 17, 4096);
     if (qad_workspace_bytes(QAD_OP_QUANTIZE, -1, 4, 16) != 0) ++failures;

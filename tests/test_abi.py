@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -50,7 +50,7 @@ def test_exported_symbols_in_dynamic_table(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.qad_abi_version() == 1
+    assert L.qad_abi_version() == 2
     for s in range(8):
         assert L.qad_status_string(s).startswith(b"QAD_")
     assert L.qad_status_string(99) == b"unknown qad_status_t"
@@ -157,7 +157,7 @@ def test_fp8_quantize_rejects(L):
 def test_w4a4_linear_rejects(L):
     fw, bw = L.qad_w4a4_linear_fwd, L.qad_w4a4_linear_bwd
     ws = L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, 64, 32, 128)
-    assert ws >= 64 << 20 and ws % 256 == 0
+    assert ws > 0 and ws % 256 == 0            # the quantizer's records only
     a = lambda **kw: [kw.get("x", P), kw.get("w", P * 2), kw.get("dt", 1), kw.get("M", 64), kw.get("N", 32),
                       kw.get("K", 128), kw.get("wsc", None), kw.get("wts", None), kw.get("y", P * 3),
                       kw.get("xq", P * 4), kw.get("wq", P * 5), kw.get("ws", P * 6), kw.get("wsb", ws), None]
@@ -180,7 +180,7 @@ def test_w4a4_linear_rejects(L):
     assert bw(*b(K=8)) == SHAPE
     assert bw(*b(wq=None)) == INVALID                 # grad_x needs wq
     assert bw(*b(gx=P)) == INVALID                    # grad_x overlaps grad_y
-    assert bw(*b(wsb=16)) == WS
+    assert bw(*b(gw=P * 2)) == INVALID                # grad_w over xq
 
 
 def test_qdq_fwd_bwd_reject(L):
@@ -393,7 +393,7 @@ def test_binding_rejects_host_tensors():
         lambda: q.qad_kl_topk_fwd_bwd(t, t, 4),
         lambda: q.qad_kl_topp_fwd_bwd(t, t, 0.9),
         lambda: q.qad_w4a4_linear_fwd(x, x),
-        lambda: q.qad_w4a4_linear_bwd(x[:, :4].contiguous(), x, x),
+        lambda: q.qad_w4a4_linear_bwd(x[:, :4].contiguous(), x, x, 32),
         lambda: q.qad_check_finite(torch.zeros(3)),
     ]
     for i, f in enumerate(calls):
@@ -425,7 +425,7 @@ def test_plain_c_client(L, tmp_path):
     src.write_text(
         '#include <stdio.h>\n#include <string.h>\n#include "libqad.h"\n'
         "int main(void) {\n"
-        "  if (qad_abi_version() != 1) return 1;\n"
+        "  if (qad_abi_version() != 2) return 1;\n"
         '  if (strncmp(qad_status_string(QAD_ERR_SHAPE), "QAD_ERR_SHAPE", 13) != 0) return 2;\n'
         "  if (qad_workspace_bytes(QAD_OP_QUANTIZE, 1, 64, 64) % 256 != 0) return 3;\n"
         "  if (qad_set_wait_limit_us(-1) != 20000) return 4;\n"

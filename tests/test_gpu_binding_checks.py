@@ -45,9 +45,12 @@ def test_binding_rejects_bad_arguments(dev):
         (lambda: q.qad_kl_topk_fwd_bwd(t, s, 10, loss_out=torch.empty(1, dtype=bf, device=dev)), "loss_out must be"),
         (lambda: q.qad_kl_topp_fwd_bwd(t, s, 0.9, tau=torch.empty(9, device=dev)), "tau must hold"),
         (lambda: q.qad_w4a4_linear_fwd(t, s, y=torch.empty(4, 8, dtype=bf, device=dev)), "y must hold"),
-        (lambda: q.qad_w4a4_linear_bwd(torch.empty(8, 16, dtype=bf, device=dev), t, torch.empty(8, 1024, dtype=bf,
-                                                                                               device=dev)),
-         "grad_y \\[M, N\\]"),
+        (lambda: q.qad_w4a4_linear_bwd(torch.empty(16, dtype=bf, device=dev), torch.empty(16, dtype=torch.uint8,
+                                                                                            device=dev),
+                                       torch.empty(16, dtype=torch.uint8, device=dev), 16), "grad_y \\[M, N\\]"),
+        (lambda: q.qad_w4a4_linear_bwd(torch.empty(8, 16, dtype=bf, device=dev), torch.empty(5, dtype=torch.uint8,
+                                                                                               device=dev),
+                                       torch.empty(5, dtype=torch.uint8, device=dev), 32), "xq must hold"),
         (lambda: q.qad_check_finite(torch.zeros(3, dtype=bf, device=dev)), "values must be"),
     ]
     for i, (f, msg) in enumerate(bad):

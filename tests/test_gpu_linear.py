@@ -1,10 +1,16 @@
 """GPU parity of the W4A4 fake-quant linear layer (qad_w4a4_linear_fwd/_bwd).
 
-The quantized operands xq, wq must equal the oracle's NVFP4 QDQ outputs bit
-for bit (dynamic scales, or for w frozen MSE-calibrated scales).  The products are bf16 values of fp32-accumulated sums, compared with
-the binary64 oracle product within the bound that arithmetic allows: half a
-bf16 ulp of the result plus 2 K 2^-24 sum_k |a_k b_k| (fp32 rounding of up to
-K products and partial sums in any order).
+The packed operands xq, wq (E2M1 codes, E4M3 block scales, tensor scale) must
+equal the oracle's NVFP4 quantization of x and w bit for bit (dynamic
+scales, or for w frozen MSE-calibrated scales).  The products -- computed by
+the library's MFMA kernel from those packed operands -- are bf16 values of
+fp32-accumulated sums of the bf16 QDQ values' products, compared with the
+binary64 oracle product of the oracle's QDQ values within the bound that
+arithmetic allows: half a bf16 ulp of the result plus 2 K 2^-24 sum_k
+|a_k b_k| (fp32 rounding of up to K products and partial sums in any order).
+Shapes span several 128 x 128 x 64 tiles with ragged edges in every
+dimension, rows whose lengths break 16-byte alignment (bf16 grad_y with
+N % 8 != 0), and single elements.
 """
 import numpy as np
 import pytest
@@ -33,6 +39,18 @@ def assert_product_close(got_bits, ref, absprod, K, label):
     assert not bad.any(), (label, np.argwhere(bad)[:3], (np.abs(got - ref) - bound).max())
 
 
+def check_packed(orc, packed, xh, R, C, scales_in=None, tscale_in=None):
+    """The packed operand equals the oracle's quantization of xh, part by part."""
+    codes, scales, ts = q.nvfp4_unpack(packed, R, C)
+    if scales_in is None:
+        rc, rs, rt, _ = orc.nvfp4_quantize(xh)
+    else:
+        rc, rs, rt, _ = orc.nvfp4_quantize(xh, scales_in, tscale_in)
+    assert np.array_equal(host(codes), rc.reshape(R, C // 2))
+    assert np.array_equal(host(scales), rs.reshape(R, C // 16))
+    assert host(ts)[0].view(np.uint32) == np.float32(rt).view(np.uint32)
+
+
 def run_case(dev, orc, M, N, K, dtype, seed, frozen=False):
     g = torch.Generator().manual_seed(seed)
     x = (torch.randn((M, K), generator=g) * 2).to(dtype)
@@ -48,10 +66,11 @@ def run_case(dev, orc, M, N, K, dtype, seed, frozen=False):
                                           w_tscale_in=torch.tensor([ts], dtype=torch.float32, device=dev))
     else:
         y, xq, wq = q.qad_w4a4_linear_fwd(x.to(dev), w.to(dev))
-    gx, gw = q.qad_w4a4_linear_bwd(gy.to(dev), xq, wq)
+    gx, gw = q.qad_w4a4_linear_bwd(gy.to(dev), xq, wq, K)
     torch.cuda.synchronize()
+    check_packed(orc, xq, host(x), M, K)
+    check_packed(orc, wq, host(w), N, K, ws_in, wt_in)
     yr, xqr, wqr = orc.w4a4_linear_fwd(host(x), host(w), ws_in, wt_in)
-    assert np.array_equal(host(xq), xqr) and np.array_equal(host(wq), wqr)
     xf, wf, gf = f64(xqr), f64(wqr), f64(host(gy))
     assert_product_close(host(y), yr, np.abs(xf) @ np.abs(wf).T, K, "y")
     gxr, gwr = orc.w4a4_linear_bwd(host(gy), xqr, wqr)
@@ -60,7 +79,9 @@ def run_case(dev, orc, M, N, K, dtype, seed, frozen=False):
 
 
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 32, 128, torch.bfloat16), (37, 19, 48, torch.float32),
-                                         (256, 512, 1024, torch.bfloat16), (1, 1, 16, torch.bfloat16)])
+                                         (256, 512, 1024, torch.bfloat16), (1, 1, 16, torch.bfloat16),
+                                         (300, 260, 208, torch.bfloat16), (129, 131, 80, torch.float32),
+                                         (200, 136, 4112, torch.bfloat16)])
 def test_linear_small(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=M + N + K)
 
@@ -79,11 +100,12 @@ def test_linear_expert_shape_sampled(dev, orc):
     announce("qad_w4a4_linear_fwd 8192x2048x4096")
     y, xq, wq = q.qad_w4a4_linear_fwd(x, w)
     gy = (torch.randn((M, N), device=dev) * 1e-3).to(torch.bfloat16)
-    gx, gw = q.qad_w4a4_linear_bwd(gy, xq, wq)
+    gx, gw = q.qad_w4a4_linear_bwd(gy, xq, wq, K)
     torch.cuda.synchronize()
+    check_packed(orc, xq, host(x), M, K)
+    check_packed(orc, wq, host(w), N, K)
     xqr = orc.nvfp4_quantize(host(x))[3]
     wqr = orc.nvfp4_quantize(host(w))[3]
-    assert np.array_equal(host(xq), xqr.reshape(M, K)) and np.array_equal(host(wq), wqr.reshape(N, K))
     rows = [0, 1, 4097, 8191]
     xf, wf = f64(xqr.reshape(M, K)[rows]), f64(wqr.reshape(N, K))
     assert_product_close(host(y)[rows], xf @ wf.T, np.abs(xf) @ np.abs(wf).T, K, "y rows")
