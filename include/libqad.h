@@ -64,16 +64,15 @@
  *    qad_check_finite()); the other outputs are then unspecified.
  *  - Alignment: tensor pointers 16-byte aligned, packed codes 4-byte aligned;
  *    scale and scalar pointers have no requirement beyond their type.
- *  - Results are deterministic: the same inputs give bitwise-equal outputs
- *    (the W4A4 linear: within a process, once its GEMM plan for the shape
- *    is chosen; see qad_w4a4_linear_fwd).
+ *  - Results are deterministic: the same inputs give bitwise-equal outputs,
+ *    in every process (every sum has a fixed order).
  *  - Thread-safe.  The state kept across calls: per device and written
- *    once, the compute-unit count and the quantizer's occupancy (atomics)
- *    and for the W4A4 linear a hipBLASLt handle and its GEMM plans (under a
- *    mutex); process-wide, the wait bound of qad_set_wait_limit_us (an
- *    atomic).  Calls only enqueue kernels on `stream` (no
- *    memset, no allocation, no host synchronisation; qad_check_finite
- *    excepted), so a sequence of calls can be captured into a HIP graph.
+ *    once, the compute-unit count, the quantizer's occupancy and the
+ *    device address of nvfp4_quantize_noalloc's scratch (atomics);
+ *    process-wide, the wait bound of qad_set_wait_limit_us (an atomic).
+ *    Calls only enqueue kernels on `stream` (no memset, no allocation, no
+ *    host synchronisation; qad_check_finite excepted), so a sequence of
+ *    calls can be captured into a HIP graph.
  */
 #ifndef LIBQAD_H
 #define LIBQAD_H
@@ -289,7 +288,8 @@ qad_status_t fp8_quantize(const void* x, qad_dtype_t xt, int64_t B, int64_t R, i
  * W4A4 linear's saved operand form: the E2M1 codes (R*C/2 bytes, row-major,
  * even element in the low nibble), then the E4M3 block scales (R*C/16 bytes,
  * row-major) at byte R*C/2, then the fp32 tensor scale at the next multiple
- * of 16 bytes.  0 for invalid sizes. */
+ * of 16 bytes; the padding before and after the tensor scale is never
+ * written.  0 for invalid sizes. */
 size_t qad_nvfp4_packed_bytes(int64_t R, int64_t C);
 
 /* W4A4 NVFP4 fake-quant linear layer ([Qwen] "3. QAD": the student is the
@@ -347,8 +347,8 @@ qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void*
  *                      QAD_F32 for full-precision gradients), or NULL for
  *                      the forward only; must not overlap the inputs
  *   workspace        : qad_workspace_bytes(QAD_OP_KL, 1, tokens, vocab) bytes
- *                      (per-row exchange records; per-row losses when
- *                      row_loss is NULL) */
+ *                      (per-row exchange records, partial sums of the
+ *                      mean; per-row losses when row_loss is NULL) */
 qad_status_t qad_kl_fwd_bwd(const void* teacher, const void* student, qad_dtype_t lt,
                             int64_t tokens, int64_t vocab, float temperature, float grad_scale,
                             float* loss_out, float* row_loss, void* grad_student, qad_dtype_t gt,

@@ -98,7 +98,7 @@ def _stream(dev: torch.device):
     return torch.cuda.current_stream(dev).cuda_stream
 # Every library call runs with the tensors' device current (torch.cuda.device):
 # the library launches on the stream it is given, but keys its per-device
-# state (CU count, occupancy, the linear's hipBLASLt handle) by HIP's current
+# state (CU count, occupancy, the no-workspace scratch address) by HIP's current
 # device, and the two must agree.
 
 

@@ -817,17 +817,23 @@ __global__ __launch_bounds__(kRowThreads) void kl_row_kernel(KlArgs a, float c, 
     if (tid == 0) a.row_loss[row] = (float)termwise_kl(part.l, part.y, part.p);
 }
 
-// Mean of the per-row losses: fixed assignment of rows to lanes, binary64
-// accumulation, fixed reduction tree.  Rows the segment kernels marked for
-// the term-wise KL (rec non-null, W > 1) first get their loss from their
-// segments' shares, added in segment order (also written to row_loss).
-__global__ __launch_bounds__(1024) void kl_mean_kernel(float* row_loss, int64_t rows, float* loss_out,
-                                                       const uint32_t* rec, int W)
+// Mean of the per-row losses, in two kernels and a fixed order.  Rows the
+// segment kernels marked for the term-wise KL (rec non-null, W > 1) first
+// get their loss from their segments' shares, added in segment order (also
+// written to row_loss): one lane per row, kMeanRows rows per workgroup,
+// whose binary64 sum (fixed tree) goes to partial[workgroup].  One
+// workgroup then adds the partials: lane i takes partials i, i + 1024, ...
+// in order, then a fixed tree.
+constexpr int kMeanRows = 256;
+
+__global__ __launch_bounds__(kMeanRows) void kl_row_finish_kernel(float* row_loss, int64_t rows, const uint32_t* rec,
+                                                                  int W, double* partial)
 {
-    __shared__ double part[1024];
-    double acc = 0.0;
-    for (int64_t r = threadIdx.x; r < rows; r += 1024) {
-        float v = row_loss[r];
+    __shared__ double part[kMeanRows];
+    const int64_t r = (int64_t)blockIdx.x * kMeanRows + threadIdx.x;
+    double v = 0.0;
+    if (r < rows) {
+        float x = row_loss[r];
         if (rec) {
             const uint32_t* rr = rec + r * rec_words(W);
             if (rr[flag_word(W)]) {
@@ -838,12 +844,27 @@ __global__ __launch_bounds__(1024) void kl_mean_kernel(float* row_loss, int64_t 
                     y += share[1];
                     p += share[2];
                 }
-                v = (float)termwise_kl(l, y, p);
-                row_loss[r] = v;
+                x = (float)termwise_kl(l, y, p);
+                row_loss[r] = x;
             }
         }
-        acc += (double)v;
+        v = (double)x;
     }
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int w = kMeanRows / 2; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = part[0];
+}
+
+__global__ __launch_bounds__(1024) void kl_mean_kernel(const double* partial, int64_t groups, int64_t rows,
+                                                       float* loss_out)
+{
+    __shared__ double part[1024];
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < groups; i += 1024) acc += partial[i];
     part[threadIdx.x] = acc;
     __syncthreads();
     for (int w = 512; w > 0; w >>= 1) {
@@ -1593,12 +1614,22 @@ int segments(int64_t vocab)
 
 } // namespace
 
-size_t kl_workspace_bytes(int64_t tokens, int64_t vocab)
+namespace {
+inline size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
+// workspace layout: per-row losses, per-row records, the mean's partial sums
+size_t kl_recs_offset(int64_t tokens) { return r256((size_t)tokens * 4); }
+size_t kl_partial_offset(int64_t tokens, int64_t vocab)
 {
     const int W = segments(vocab);
-    const size_t rows = (size_t)tokens * 4;                         // per-row losses
     const size_t recs = W > 1 && W <= kMaxSegments ? (size_t)tokens * rec_words(W) * 4 : 0;
-    return ((rows + 255) & ~(size_t)255) + recs;
+    return kl_recs_offset(tokens) + r256(recs);
+}
+} // namespace
+
+size_t kl_workspace_bytes(int64_t tokens, int64_t vocab)
+{
+    const size_t groups = (size_t)((tokens + kMeanRows - 1) / kMeanRows);
+    return kl_partial_offset(tokens, vocab) + r256(groups * 8);
 }
 
 namespace {
@@ -1612,8 +1643,7 @@ hipError_t launch_rows(const KlArgs& a0, void* workspace, bool topk, hipStream_t
     const float gmul = a.grad_scale / a.temperature;
     const int W = segments(a.vocab);
     const int gmode = !a.grad ? 0 : a.grad_bf16 ? 1 : 2;
-    uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                (((size_t)a.tokens * 4 + 255) & ~(size_t)255));
+    uint32_t* rec = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kl_recs_offset(a.tokens));
     if (W > 1 && W <= kMaxSegments) {
         const int64_t n = a.tokens * rec_words(W);
         hipLaunchKernelGGL(zero_records_kernel, dim3((unsigned)min((n + 255) / 256, (int64_t)65536)), dim3(256), 0,
@@ -1658,12 +1688,15 @@ hipError_t launch_rows(const KlArgs& a0, void* workspace, bool topk, hipStream_t
 hipError_t launch_mean(const KlArgs& a, void* workspace, hipStream_t stream)
 {
     const int W = a.tokens > 0 && a.vocab > 0 ? segments(a.vocab) : 0;
+    char* ws = static_cast<char*>(workspace);
     const uint32_t* rec =
-        W > 1 && W <= kMaxSegments
-            ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(workspace) +
-                                                (((size_t)a.tokens * 4 + 255) & ~(size_t)255))
-            : nullptr;
-    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, a.row_loss, a.tokens, a.loss_out, rec, W);
+        W > 1 && W <= kMaxSegments ? reinterpret_cast<const uint32_t*>(ws + kl_recs_offset(a.tokens)) : nullptr;
+    const int64_t groups = (a.tokens + kMeanRows - 1) / kMeanRows;
+    double* partial = a.tokens > 0 ? reinterpret_cast<double*>(ws + kl_partial_offset(a.tokens, a.vocab)) : nullptr;
+    if (groups > 0)
+        hipLaunchKernelGGL(kl_row_finish_kernel, dim3((unsigned)groups), dim3(kMeanRows), 0, stream, a.row_loss,
+                           a.tokens, rec, W, partial);
+    hipLaunchKernelGGL(kl_mean_kernel, dim3(1), dim3(1024), 0, stream, partial, groups, a.tokens, a.loss_out);
     return hipGetLastError();
 }
 

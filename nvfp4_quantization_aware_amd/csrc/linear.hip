@@ -10,13 +10,15 @@
 // (dynamic per-tensor scales, blocks of 16 along K, or frozen weight scales)
 // into packed NVFP4 operands: E2M1 codes, E4M3 block scales and the tensor
 // scale, 9/16 of a byte per element.  The three products are one hand-written
-// MFMA GEMM: each workgroup stages 128 x 64 tiles of both operands into LDS,
-// rebuilding the QDQ values bf16(dec(code) * s_eff) there exactly as the
-// quantizer's own bf16 output is formed (FP4 decode, one binary32 product,
-// nearest-even bf16), then four waves multiply them with
-// v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  So the operands cross HBM
-// as 4-bit codes, never as bf16 QDQ copies.
+// MFMA GEMM: each workgroup owns a 256 x 256 (or 256 x 128) output tile and
+// stages 64-deep slices of both operands into LDS, rebuilding the QDQ values
+// bf16(dec(code) * s_eff) there exactly as the quantizer's own bf16 output is
+// formed (FP4 decode, one binary32 product, nearest-even bf16); eight waves
+// multiply them with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  So
+// the operands cross HBM as 4-bit codes, never as bf16 QDQ copies.
 #include "libqad.h"
+
+#include <type_traits>
 
 #include "qad_device.h"
 #include "qad_internal.h"
@@ -24,8 +26,9 @@
 namespace qad {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;   // workgroup tile
-constexpr int kThreads = 256;                    // four waves, 2 x 2 over the tile
+constexpr int kBM = 256, kBK = 64;              // workgroup tile: 256 x BN (BN 256 or 128), 64-deep steps
+constexpr int kThreads = 512;                    // eight waves, two per SIMD, 4 (M) x 2 (N) over the tile
+constexpr int kWM = 4;                           // waves along M; each owns 256 / kWM rows of the tile
 constexpr int kLds = kBK + 8;                    // LDS row stride in bf16 (144 B: conflict-free 16-B reads)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -51,65 +54,110 @@ struct Operand {
 struct GemmArgs {
     Operand a, b;
     uint16_t* c;            // bf16 [M][N]
-    int64_t M, N, K;        // K: contraction length (a multiple of 16)
+    int64_t M, N, K;        // K: contraction length
     int tiles_m, tiles_n;
 };
 
-// Staging registers of one thread for one 128 x 64 tile of an operand.
-//   *_K: row r = t / 2 of the tile, contraction [32 h, 32 h + 32), h = t % 2
-//   *_T: contraction rows [8 kb, 8 kb + 8), kb = t / 32, output [4 o, 4 o + 4), o = t % 32
-template <int KIND> struct Stage;
-template <> struct Stage<OP_BF16_K> { u32x4 v[4]; };
-template <> struct Stage<OP_FP4_K> { u32x2 code[2]; uint32_t sc; };
-template <> struct Stage<OP_BF16_T> { u32x2 v[8]; };
-template <> struct Stage<OP_FP4_T> { uint32_t code[4]; uint32_t sc[2]; };
+// A thread's share of one R x 64 tile of an operand (R output rows by 64
+// contraction values, kThreads threads).
+//   K forms: EPT consecutive contraction values of one output row: row
+//            t / TPR, contraction [EPT (t % TPR), +EPT); BLK NVFP4 blocks
+//   T forms: RPT contraction rows of 4 consecutive outputs: outputs
+//            [4 (t % OG), +4), contraction [RPT (t / OG), +RPT)
+template <int R> struct Share {
+    static constexpr int EPT = R * kBK / kThreads, TPR = kBK / EPT, BLK = EPT / 16;
+    static constexpr int OG = R / 4, RPT = kBK * OG / kThreads;
+};
+
+// Staging registers of that share.  Loaded values stay as loaded (no
+// arithmetic on them before the decode), so a thread never waits on its
+// prefetch before the step that decodes it.
+template <int KIND, int R> struct Stage;
+template <int R> struct Stage<OP_BF16_K, R> { u32x4 v[Share<R>::EPT / 8]; };
+template <int R> struct Stage<OP_FP4_K, R> { u32x2 code[Share<R>::BLK]; uint32_t sc[Share<R>::BLK]; uint32_t ok; };
+template <int R> struct Stage<OP_BF16_T, R> { u32x2 v[Share<R>::RPT]; };
+template <int R> struct Stage<OP_FP4_T, R> { uint32_t code[Share<R>::RPT]; uint32_t sc[Share<R>::RPT]; uint32_t ok; };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Global loads of the tile whose output rows start at row0 and contraction at
 // k0; what lies outside the operand reads as zeros (code 0 decodes to +0).
-template <int KIND>
-__device__ __forceinline__ void stage_load(Stage<KIND>& s, const Operand& op, int64_t row0, int64_t k0, int64_t K)
+template <int KIND, int R>
+__device__ __forceinline__ void stage_load(Stage<KIND, R>& s, const Operand& op, int64_t row0, int64_t k0, int64_t K)
 {
+    using S = Share<R>;
     const int t = threadIdx.x;
     if constexpr (KIND == OP_BF16_K || KIND == OP_FP4_K) {
-        const int64_t row = row0 + (t >> 1);
-        const int64_t kc = k0 + 32 * (t & 1);
+        const int64_t row = row0 + t / S::TPR;
+        const int64_t kc = k0 + S::EPT * (t % S::TPR);
         const bool rv = row < op.rows;
         if constexpr (KIND == OP_BF16_K) {
+            // the contraction here is the backward's N, of any length: a run
+            // of 8 is loaded as one vector only when 16-byte aligned and
+            // wholly inside the row, else element by element up to its end
             const uint16_t* p = static_cast<const uint16_t*>(op.data) + row * op.ld + kc;
-            const bool vec = (op.ld & 7) == 0;   // 16-byte aligned rows
+            const bool vec = (op.ld & 7) == 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool ok = rv && kc + 8 * q < K;   // K % 16 == 0: a run of 8 lies wholly inside or outside
-                if (ok && vec) {
+            for (int q = 0; q < S::EPT / 8; ++q) {
+                const int64_t k = kc + 8 * q;
+                if (rv && vec && k + 8 <= K) {
                     s.v[q] = ld16(p + 8 * q);
                 } else {
                     uint32_t w[4] = {0u, 0u, 0u, 0u};
-                    if (ok)
-                        for (int e = 0; e < 8; ++e) w[e >> 1] |= (uint32_t)p[8 * q + e] << (16 * (e & 1));
+                    if (rv)
+                        for (int e = 0; e < 8; ++e)
+                            if (k + e < K) w[e >> 1] |= (uint32_t)p[8 * q + e] << (16 * (e & 1));
                     s.v[q] = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
         } else {
-            const uint8_t* codes = static_cast<const uint8_t*>(op.data) + row * (op.ld >> 1) + (kc >> 1);
-            const uint8_t* sc = op.scales + row * (op.ld >> 4) + (kc >> 4);
-            s.sc = 0u;
+            // K % 16 == 0 here: whole blocks.  Every load is issued: a block
+            // outside the operand reads from an address clamped into it (the
+            // start of the row; the load may then run past the row or the
+            // codes, but stays inside the packed buffer, whose scales and
+            // tensor-scale line follow the codes), and bit b of `ok` tells
+            // the decode to zero block b.  When rows hold a whole number of
+            // the thread's runs (K % (16 BLK) == 0) the run's codes are 16-byte
+            // loads and its BLK scale bytes one load into sc[0] (bit 8 of
+            // ok); otherwise 8-byte code loads and single scale bytes.
+            const int64_t rc = rv ? row : op.rows - 1;
+            const int64_t kk = kc < K ? kc : 0;
+            const uint8_t* codes = static_cast<const uint8_t*>(op.data) + rc * (op.ld >> 1) + (kk >> 1);
+            const uint8_t* sc = op.scales + rc * (op.ld >> 4) + (kk >> 4);
+            uint32_t ok = 0u;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bool ok = rv && kc + 16 * b < K;   // rows of whole blocks: 8-byte aligned
-                s.code[b] = ok ? ld8(codes + 8 * b) : u32x2{0u, 0u};
-                s.sc |= (ok ? (uint32_t)sc[b] : 0u) << (8 * b);
+            for (int b = 0; b < S::BLK; ++b) ok |= (uint32_t)(rv && kc + 16 * b < K) << b;
+            if (S::BLK >= 2 && (op.ld % (16 * S::BLK)) == 0) {
+#pragma unroll
+                for (int h = 0; h < S::BLK / 2; ++h) {
+                    const u32x4 c = ld16(codes + 16 * h);
+                    s.code[2 * h] = u32x2{c[0], c[1]};
+                    s.code[2 * h + 1] = u32x2{c[2], c[3]};
+                }
+                if constexpr (S::BLK == 4)
+                    s.sc[0] = *reinterpret_cast<const uint32_t*>(sc);
+                else if constexpr (S::BLK == 2)
+                    s.sc[0] = *reinterpret_cast<const uint16_t*>(sc);
+#pragma unroll
+                for (int b = 1; b < S::BLK; ++b) s.sc[b] = 0u;
+                ok |= 0x100u;
+            } else {
+#pragma unroll
+                for (int b = 0; b < S::BLK; ++b) {
+                    s.code[b] = ld8(codes + 8 * b);
+                    s.sc[b] = sc[b];
+                }
             }
+            s.ok = ok;
         }
     } else {
-        const int64_t kr0 = k0 + 8 * (t >> 5);
-        const int64_t o = row0 + 4 * (t & 31);
+        const int64_t kr0 = k0 + S::RPT * (t / S::OG);
+        const int64_t o = row0 + 4 * (t % S::OG);
         if constexpr (KIND == OP_BF16_T) {
             const bool vec = (op.ld & 3) == 0 && o + 4 <= op.rows;   // 8-byte aligned, wholly inside
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < S::RPT; ++i) {
                 const int64_t kr = kr0 + i;
                 const uint16_t* p = static_cast<const uint16_t*>(op.data) + kr * op.ld + o;
                 if (kr < K && vec) {
@@ -123,23 +171,23 @@ __device__ __forceinline__ void stage_load(Stage<KIND>& s, const Operand& op, in
                 }
             }
         } else {
-            // four codes (2 bytes) and their block's scale per contraction row;
-            // the output extent is a multiple of 16, so a run of 4 lies wholly
-            // inside or outside
+            // four codes (2 bytes) and their block's scale per contraction
+            // row; the output extent is a multiple of 16, so a run of 4 lies
+            // wholly inside or outside (clamped addresses and a validity
+            // mask, as for the K form)
             const bool ov = o < op.rows;
-            s.code[0] = s.code[1] = s.code[2] = s.code[3] = 0u;
-            s.sc[0] = s.sc[1] = 0u;
+            const int64_t oc = ov ? o : op.rows - 4;
+            uint32_t ok = 0u;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < S::RPT; ++i) {
                 const int64_t kr = kr0 + i;
-                const bool ok = ov && kr < K;
-                const uint32_t c = ok ? *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(op.data) +
-                                                                           kr * (op.ld >> 1) + (o >> 1))
-                                      : 0u;
-                const uint32_t b = ok ? (uint32_t)op.scales[kr * (op.ld >> 4) + (o >> 4)] : 0u;
-                s.code[i >> 1] |= c << (16 * (i & 1));
-                s.sc[i >> 2] |= b << (8 * (i & 3));
+                const int64_t krc = kr < K ? kr : K - 1;
+                s.code[i] = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(op.data) +
+                                                               krc * (op.ld >> 1) + (oc >> 1));
+                s.sc[i] = op.scales[krc * (op.ld >> 4) + (oc >> 4)];
+                ok |= (uint32_t)(ov && kr < K) << i;
             }
+            s.ok = ok;
         }
     }
 }
@@ -156,65 +204,110 @@ __device__ __forceinline__ uint32_t qdq_pair(uint32_t codes, float s)
 
 __device__ __forceinline__ void lds_store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Registers -> LDS tile [128 output rows][64 contraction] (bf16, stride kLds)
-template <int KIND>
-__device__ __forceinline__ void stage_store(const Stage<KIND>& s, uint16_t* lds, float s_g)
+// Effective scale fl(dec(c) s_g) of block scale code c (0 <= c < 128), or 0
+// for a block outside the operand (whose codes are then zeroed too).  The
+// E4M3 value is 2^(e-7) (1 + m/8), or m 2^-9 for e = 0; both forms are
+// computed and one selected by a mask, without a branch.
+__device__ __forceinline__ float block_scale(uint32_t c, float s_g, bool ok)
 {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
+    const uint32_t sub = __builtin_bit_cast(uint32_t, (float)m * 0.001953125f);
+    const uint32_t sel = 0u - (uint32_t)(e != 0u);
+    const float dec = __builtin_bit_cast(float, (nrm & sel) | (sub & ~sel));
+    return ok ? dec * s_g : 0.0f;
+}
+
+// Decoded values of a transposed operand on their way into LDS: w[e][p] is
+// output row 4 og + e, contraction rows 2 p and 2 p + 1 of the thread's run.
+template <int R> struct TBuf { uint32_t w[4][Share<R>::RPT / 2]; };
+
+// Registers -> LDS tile [R output rows][64 contraction] (bf16, stride kLds),
+// in four parts (u = 0..3) so that the decode can be spread over the four
+// 16-deep MFMA slices of a step.  A part of a K operand is a quarter of the
+// thread's 8-value runs; one of a T operand decodes a quarter of its
+// contraction-row pairs, and the last part stores the transposed rows.
+template <int KIND, int R>
+__device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R>& tb, uint16_t* lds, float s_g, int u)
+{
+    using S = Share<R>;
     const int t = threadIdx.x;
     if constexpr (KIND == OP_BF16_K || KIND == OP_FP4_K) {
-        uint16_t* dst = lds + (t >> 1) * kLds + 32 * (t & 1);
-        if constexpr (KIND == OP_BF16_K) {
+        constexpr int RUNS = S::EPT / 8, UPP = (RUNS + 3) / 4;   // 8-value runs, per part
+        uint16_t* dst = lds + (t / S::TPR) * kLds + S::EPT * (t % S::TPR);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) lds_store16(dst + 8 * q, s.v[q]);
-        } else {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const float se = e4m3_decode((s.sc >> (8 * b)) & 127u) * s_g;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t c = s.code[b][h];
-                    lds_store16(dst + 16 * b + 8 * h,
-                                u32x4{qdq_pair<0>(c, se), qdq_pair<1>(c, se), qdq_pair<2>(c, se), qdq_pair<3>(c, se)});
-                }
+        for (int v = 0; v < UPP; ++v) {
+            const int r = u * UPP + v;   // run index
+            if (r >= RUNS) break;
+            if constexpr (KIND == OP_BF16_K) {
+                lds_store16(dst + 8 * r, s.v[r]);
+            } else {
+                // block r / 2: its scale byte from the one scale load or its own
+                const int b = r >> 1;
+                const bool ok = (s.ok >> b) & 1u;
+                const uint32_t sb = (s.ok & 0x100u) ? s.sc[0] >> (8 * b) : s.sc[b];
+                const float se = block_scale(sb & 127u, s_g, ok);
+                const uint32_t c = ok ? s.code[b][r & 1] : 0u;
+                lds_store16(dst + 8 * r,
+                            u32x4{qdq_pair<0>(c, se), qdq_pair<1>(c, se), qdq_pair<2>(c, se), qdq_pair<3>(c, se)});
             }
         }
     } else {
-        // transpose: output row 4 o + e receives contraction [8 kb, 8 kb + 8)
-        uint16_t* dst = lds + (4 * (t & 31)) * kLds + 8 * (t >> 5);
-        uint32_t w[4][4];   // [e][pair of contraction rows]
-        if constexpr (KIND == OP_BF16_T) {
+        constexpr int PAIRS = S::RPT / 2, PPP = (PAIRS + 3) / 4;   // contraction-row pairs, per part
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+        for (int v = 0; v < PPP; ++v) {
+            const int p = u * PPP + v;
+            if (p >= PAIRS) break;
+            if constexpr (KIND == OP_BF16_T) {
                 const u32x2 a = s.v[2 * p], b = s.v[2 * p + 1];
-                w[0][p] = (a[0] & 0xFFFFu) | (b[0] << 16);
-                w[1][p] = (a[0] >> 16) | (b[0] & 0xFFFF0000u);
-                w[2][p] = (a[1] & 0xFFFFu) | (b[1] << 16);
-                w[3][p] = (a[1] >> 16) | (b[1] & 0xFFFF0000u);
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float v[2][4];
+                tb.w[0][p] = (a[0] & 0xFFFFu) | (b[0] << 16);
+                tb.w[1][p] = (a[0] >> 16) | (b[0] & 0xFFFF0000u);
+                tb.w[2][p] = (a[1] & 0xFFFFu) | (b[1] << 16);
+                tb.w[3][p] = (a[1] >> 16) | (b[1] & 0xFFFF0000u);
+            } else {
+                float x[2][4];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const int i = 2 * p + r;
-                    const float se = e4m3_decode((s.sc[i >> 2] >> (8 * (i & 3))) & 127u) * s_g;
-                    const uint32_t c = s.code[i >> 1] >> (16 * (i & 1));
+                    const bool ok = (s.ok >> i) & 1u;
+                    const float se = block_scale(s.sc[i] & 127u, s_g, ok);
+                    const uint32_t c = ok ? s.code[i] : 0u;
                     float lo, hi;
                     fp4_decode_pair<0>(c, lo, hi);
-                    v[r][0] = lo * se;
-                    v[r][1] = hi * se;
+                    x[r][0] = lo * se;
+                    x[r][1] = hi * se;
                     fp4_decode_pair<1>(c, lo, hi);
-                    v[r][2] = lo * se;
-                    v[r][3] = hi * se;
+                    x[r][2] = lo * se;
+                    x[r][3] = hi * se;
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e][p] = pack_bf16x2(v[0][e], v[1][e]);
+                for (int e = 0; e < 4; ++e) tb.w[e][p] = pack_bf16x2(x[0][e], x[1][e]);
             }
         }
+        if (u == 3) {
+            // output row 4 og + e receives contraction [RPT cg, +RPT)
+            uint16_t* dst = lds + (4 * (t % S::OG)) * kLds + S::RPT * (t / S::OG);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lds_store16(dst + e * kLds, u32x4{w[e][0], w[e][1], w[e][2], w[e][3]});
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (S::RPT >= 8) {
+#pragma unroll
+                    for (int h = 0; h < S::RPT / 8; ++h)
+                        lds_store16(dst + e * kLds + 8 * h,
+                                    u32x4{tb.w[e][4 * h], tb.w[e][4 * h + 1], tb.w[e][4 * h + 2], tb.w[e][4 * h + 3]});
+                } else {
+                    *reinterpret_cast<u32x2*>(dst + e * kLds) = u32x2{tb.w[e][0], tb.w[e][1]};
+                }
+            }
+        }
     }
+}
+
+template <int KIND, int R>
+__device__ __forceinline__ void stage_store(const Stage<KIND, R>& s, uint16_t* lds, float s_g)
+{
+    TBuf<R> tb;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) stage_store_part<KIND, R>(s, tb, lds, s_g, u);
 }
 
 // tile index of workgroup `bid`: consecutive workgroups go to different XCDs
@@ -233,104 +326,127 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     tn = r / gm;
 }
 
-// Operand loads run this many 64-deep steps ahead of the MFMAs: NVFP4 stages
-// are 5 registers per operand, so three fit; bf16 stages are 16
-template <int KA, int KB> struct Depth {
-    static constexpr int value = (KA == OP_FP4_K || KA == OP_FP4_T) && (KB == OP_FP4_K || KB == OP_FP4_T) ? 3 : 1;
-};
-
-// One 64-deep step of the product: the registers of stage `st` are decoded
-// into LDS, the loads of stage st + Depth are issued into the same
-// registers, and the MFMAs consume the tile from LDS.
-template <int KA, int KB>
-__device__ __forceinline__ void gemm_step(const GemmArgs& g, Stage<KA>& ra, Stage<KB>& rb, int64_t st, int64_t steps,
-                                          int64_t m0, int64_t n0, float sa, float sb, uint16_t* lds_a,
-                                          uint16_t* lds_b, f32x16_t (&acc)[2][2])
+template <int KIND> __device__ __forceinline__ float tensor_scale(const Operand& op)
 {
-    const int t = threadIdx.x, l = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    __syncthreads();   // the previous step's fragments have been read
-    stage_store<KA>(ra, lds_a, sa);
-    stage_store<KB>(rb, lds_b, sb);
-    __syncthreads();
-    constexpr int D = Depth<KA, KB>::value;
-    if (st + D < steps) {
-        stage_load<KA>(ra, g.a, m0, (st + D) * kBK, g.K);
-        stage_load<KB>(rb, g.b, n0, (st + D) * kBK, g.K);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int kcol = ks * 16 + 8 * (l >> 5);
-        bf16x8_t fa[2], fb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            fa[i] = *reinterpret_cast<const bf16x8_t*>(lds_a + (wm * 64 + i * 32 + (l & 31)) * kLds + kcol);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            fb[j] = *reinterpret_cast<const bf16x8_t*>(lds_b + (wn * 64 + j * 32 + (l & 31)) * kLds + kcol);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+    return (KIND == OP_FP4_K || KIND == OP_FP4_T) ? *op.tscale : 0.0f;
 }
 
-// C[M][N] = sum_k A(m, k) B(n, k), bf16 out of fp32 accumulation.  One
-// 128 x 128 tile per workgroup; wave (wm, wn) owns the 64 x 64 quarter
-// (wm, wn) as 2 x 2 MFMA tiles of 32 x 32.  Operand loads run Depth 64-deep
-// steps ahead of the MFMAs, in a ring of register stages; each step decodes
-// one stage into LDS.
-template <int KA, int KB>
+// The fragments of one 16-deep slice ks for wave (wm, wn): A rows
+// [TI 32 wm + 32 i, +32), B rows [BN/2 wn + 32 j, +32); lane l holds row
+// l % 32, contraction [8 (l / 32), +8) of the slice (the MFMA operand layout)
+constexpr int kTI = kBM / kWM / 32;   // MFMA tiles of a wave along M
+template <int BN>
+__device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* lb, int ks, bf16x8_t (&fa)[kTI],
+                                           bf16x8_t (&fb)[BN / 64])
+{
+    const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave % kWM, wn = wave / kWM;
+    const int kcol = ks * 16 + 8 * (l >> 5);
+#pragma unroll
+    for (int i = 0; i < kTI; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(la + (wm * 32 * kTI + i * 32 + (l & 31)) * kLds + kcol);
+#pragma unroll
+    for (int j = 0; j < BN / 64; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + (wn * (BN / 2) + j * 32 + (l & 31)) * kLds + kcol);
+}
+
+// C[M][N] = sum_k A(m, k) B(n, k), bf16 out of fp32 accumulation in a fixed
+// order (k ascending in steps of 64, each step's four 16-deep MFMAs in
+// order).  One 256 x BN tile per workgroup of eight waves, two per SIMD;
+// wave (wm, wn) owns rows [64 wm, +64) and columns [BN/2 wn, +BN/2) as
+// 2 x BN/64 MFMA tiles of 32 x 32.  Two LDS buffers: while the waves
+// multiply the tiles of step s from one buffer (the fragments of each
+// 16-deep slice read while the previous slice's MFMAs run), each thread
+// decodes its registers of step s + 1 into the other, one quarter per slice,
+// and has the loads of step s + 2 in flight; one barrier per step separates
+// the phases.  Past the last step the loads repeat the last slice and the
+// decode fills the idle buffer, so the loop body has no branches.
+template <int KA, int KB, int BN>
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
 {
-    __shared__ __align__(16) uint16_t lds_a[kBM * kLds];
-    __shared__ __align__(16) uint16_t lds_b[kBN * kLds];
+    constexpr int TJ = BN / 64;
+    constexpr int kBufA = kBM * kLds, kBufB = BN * kLds;
+    __shared__ __align__(16) uint16_t lds[2 * (kBufA + kBufB)];
+
     int tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-    const int t = threadIdx.x, l = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const float sa = (KA == OP_FP4_K || KA == OP_FP4_T) ? *g.a.tscale : 0.0f;
-    const float sb = (KB == OP_FP4_K || KB == OP_FP4_T) ? *g.b.tscale : 0.0f;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
+    const float sa = tensor_scale<KA>(g.a), sb = tensor_scale<KB>(g.b);
+    const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave % kWM, wn = wave / kWM;
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[kTI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kTI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
 
     const int64_t steps = (g.K + kBK - 1) / kBK;
-    constexpr int D = Depth<KA, KB>::value;
-    Stage<KA> ra[D];
-    Stage<KB> rb[D];
+    const int64_t last = (steps - 1) * kBK;
+    Stage<KA, kBM> ra[2];
+    Stage<KB, BN> rb[2];
+    stage_load<KA, kBM>(ra[0], g.a, m0, 0, g.K);
+    stage_load<KB, BN>(rb[0], g.b, n0, 0, g.K);
+    stage_load<KA, kBM>(ra[1], g.a, m0, kBK < last ? kBK : last, g.K);
+    stage_load<KB, BN>(rb[1], g.b, n0, kBK < last ? kBK : last, g.K);
+    stage_store<KA, kBM>(ra[0], lds, sa);
+    stage_store<KB, BN>(rb[0], lds + kBufA, sb);
+    __syncthreads();
+
+    // step s: buffer s % 2 is multiplied, registers (s + 1) % 2 are decoded
+    // into buffer (s + 1) % 2, registers s % 2 receive the loads of step s + 2
+    auto step = [&](int64_t s, auto par) {
+        constexpr int P = decltype(par)::value;
+        const uint16_t* la = lds + P * (kBufA + kBufB);
+        const uint16_t* lb = la + kBufA;
+        uint16_t* wa = lds + (P ^ 1) * (kBufA + kBufB);
+        uint16_t* wb = wa + kBufA;
+        bf16x8_t fa[2][kTI], fb[2][TJ];
+        load_frags<BN>(la, lb, 0, fa[0], fb[0]);
+        const int64_t kn = (s + 2) * kBK < last ? (s + 2) * kBK : last;
+        stage_load<KA, kBM>(ra[P], g.a, m0, kn, g.K);
+        stage_load<KB, BN>(rb[P], g.b, n0, kn, g.K);
+        TBuf<kBM> ta;
+        TBuf<BN> tb;
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < steps) {
-            stage_load<KA>(ra[d], g.a, m0, d * kBK, g.K);
-            stage_load<KB>(rb[d], g.b, n0, d * kBK, g.K);
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            if (ks + 1 < kBK / 16) load_frags<BN>(la, lb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            stage_store_part<KA, kBM>(ra[P ^ 1], ta, wa, sa, ks);
+            stage_store_part<KB, BN>(rb[P ^ 1], tb, wb, sb, ks);
+#pragma unroll
+            for (int i = 0; i < kTI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
         }
-    for (int64_t st = 0; st < steps; st += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (st + d < steps) gemm_step<KA, KB>(g, ra[d], rb[d], st + d, steps, m0, n0, sa, sb, lds_a, lds_b, acc);
+        __syncthreads();
+    };
+    for (int64_t s = 0; s < steps; s += 2) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < steps) step(s + 1, std::integral_constant<int, 1>{});
     }
 
     // accumulator e of lane l in MFMA tile (i, j): row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kTI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 32 + (l & 31);
+        for (int j = 0; j < TJ; ++j) {
+            const int64_t col = n0 + wn * (BN / 2) + j * 32 + (l & 31);
             if (col >= g.N) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+                const int64_t row = m0 + wm * 32 * kTI + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
                 if (row < g.M) g.c[row * g.N + col] = (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
             }
         }
 }
 
+int64_t tile_count(int64_t rows, int64_t cols, int bn) { return ((rows + kBM - 1) / kBM) * ((cols + bn - 1) / bn); }
+
+// 256-wide tiles for the forward product (both operands NVFP4) when they
+// give every compute unit of the chip (256 on MI355X) a tile, else 128-wide
+// ones; the backward products (one bf16 operand, whose staging registers
+// leave no room for 256-wide accumulators) always take 128-wide tiles
 template <int KA, int KB>
 hipError_t launch_gemm(const Operand& a, const Operand& b, uint16_t* c, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream)
@@ -342,10 +458,19 @@ hipError_t launch_gemm(const Operand& a, const Operand& b, uint16_t* c, int64_t 
     g.M = M;
     g.N = N;
     g.K = K;
+    constexpr bool kCanWiden = KA == OP_FP4_K && KB == OP_FP4_K;
+    const bool wide = kCanWiden && tile_count(M, N, 256) >= 256;
+    const int bn = wide ? 256 : 128;
     g.tiles_m = (int)((M + kBM - 1) / kBM);
-    g.tiles_n = (int)((N + kBN - 1) / kBN);
-    const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
+    g.tiles_n = (int)((N + bn - 1) / bn);
+    const dim3 grid((unsigned)tile_count(M, N, bn));
+    if constexpr (kCanWiden) {
+        if (wide) {
+            hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 256>), grid, dim3(kThreads), 0, stream, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 128>), grid, dim3(kThreads), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -380,7 +505,7 @@ Operand bf16_operand(const void* data, int64_t ld, int64_t rows)
     return o;
 }
 
-int64_t tiles(int64_t rows, int64_t cols) { return ((rows + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN); }
+int64_t tiles(int64_t rows, int64_t cols) { return tile_count(rows, cols, 128); }
 
 bool dims_ok(int64_t M, int64_t N, int64_t K)
 {

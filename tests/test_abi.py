@@ -71,13 +71,15 @@ def test_workspace_sizes(L):
             assert L.qad_workspace_bytes(op, B, R, C_) == _record_bytes(B, R * C_)
     # KL: per-row losses, then one record per row when a row spans 2..64
     # segments of 16384 logits (6 tagged 64-bit state words and three binary64
-    # loss shares per segment, one flag word)
+    # loss shares per segment, one flag word), then one binary64 partial sum
+    # of the mean per 256 rows; each part starts on a 256-byte boundary
+    r256 = lambda n: -(-n // 256) * 256
     for tokens, vocab in ((8192, 131072), (100, 4096), (7, 16384), (7, 16392), (3, 1 << 20), (3, (1 << 20) + 8),
-                          (3, 1 << 22)):
+                          (3, 1 << 22), (0, 131072)):
         W = -(-vocab // 16384)
         rec = ((19 * W + 1 + 31) // 32 * 32) * 4 if 1 < W <= 64 else 0
-        expect = -(-(tokens * 4) // 256) * 256 + tokens * rec
-        assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == -(-expect // 256) * 256
+        expect = r256(tokens * 4) + r256(tokens * rec) + r256(-(-tokens // 256) * 8)
+        assert L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab) == expect
     # top-k KL: the KL workspace, then one float per row (thresholds)
     for tokens, vocab in ((8192, 131072), (3, 8), (1000, 248320), (3, 1 << 22)):
         kl = L.qad_workspace_bytes(q.QAD_OP_KL, 1, tokens, vocab)

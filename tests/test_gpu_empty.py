@@ -63,19 +63,29 @@ def test_empty_kl(dev, fn):
     assert out[1].numel() == 0 and out[2].shape == (0, 1024)
 
 
+def assert_packed_is_quantization(packed, x):
+    # the packed operand holds the codes, block scales and tensor scale that
+    # nvfp4_quantize gives for the same tensor
+    R, C = x.shape
+    codes, scales, ts = q.nvfp4_unpack(packed, R, C)
+    rc, rs, rt, _ = q.nvfp4_quantize(x, y=False)
+    assert torch.equal(codes.reshape(-1), rc.reshape(-1)) and torch.equal(scales.reshape(-1), rs.reshape(-1))
+    assert torch.equal(ts.reshape(-1), rt.reshape(-1))
+
+
 def test_empty_linear(dev):
     announce("empty W4A4 linear: M = 0 and N = 0")
     bf = torch.bfloat16
     w = torch.randn(32, 64, device=dev).to(bf)
     y, xq, wq = q.qad_w4a4_linear_fwd(torch.empty((0, 64), dtype=bf, device=dev), w)
-    gx, gw = q.qad_w4a4_linear_bwd(torch.empty((0, 32), dtype=bf, device=dev), xq, wq)
+    gx, gw = q.qad_w4a4_linear_bwd(torch.empty((0, 32), dtype=bf, device=dev), xq, wq, 64)
     x = torch.randn(16, 64, device=dev).to(bf)
     y2, xq2, wq2 = q.qad_w4a4_linear_fwd(x, torch.empty((0, 64), dtype=bf, device=dev))
-    gx2, gw2 = q.qad_w4a4_linear_bwd(torch.empty((16, 0), dtype=bf, device=dev), xq2, wq2)
+    gx2, gw2 = q.qad_w4a4_linear_bwd(torch.empty((16, 0), dtype=bf, device=dev), xq2, wq2, 64)
     torch.cuda.synchronize()
     assert y.shape == (0, 32) and gx.shape == (0, 64) and gw.shape == (32, 64)
     assert torch.count_nonzero(gw).item() == 0
-    assert torch.equal(wq, q.nvfp4_qdq_fwd(w))
+    assert_packed_is_quantization(wq, w)
     assert y2.shape == (16, 0) and gw2.shape == (0, 64) and gx2.shape == (16, 64)
     assert torch.count_nonzero(gx2).item() == 0
-    assert torch.equal(xq2, q.nvfp4_qdq_fwd(x))
+    assert_packed_is_quantization(xq2, x)
