@@ -73,9 +73,9 @@ template <int R> struct Share {
 // arithmetic on them before the decode), so a thread never waits on its
 // prefetch before the step that decodes it.
 template <int KIND, int R> struct Stage;
-template <int R> struct Stage<OP_BF16_K, R> { u32x4 v[Share<R>::EPT / 8]; };
+template <int R> struct Stage<OP_BF16_K, R> { u32x4 v[Share<R>::EPT / 8]; uint32_t ok; };
 template <int R> struct Stage<OP_FP4_K, R> { u32x2 code[Share<R>::BLK]; uint32_t sc[Share<R>::BLK]; uint32_t ok; };
-template <int R> struct Stage<OP_BF16_T, R> { u32x2 v[Share<R>::RPT]; };
+template <int R> struct Stage<OP_BF16_T, R> { u32x2 v[Share<R>::RPT]; uint32_t ok; };
 template <int R> struct Stage<OP_FP4_T, R> { uint32_t code[Share<R>::RPT]; uint32_t sc[Share<R>::RPT]; uint32_t ok; };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
@@ -83,21 +83,46 @@ __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<c
 
 // Global loads of the tile whose output rows start at row0 and contraction at
 // k0; what lies outside the operand reads as zeros (code 0 decodes to +0).
-template <int KIND, int R>
+// FAST (chosen per launch): every row of every operand is aligned for the
+// vector forms below -- NVFP4 rows hold whole 16-byte runs of codes (K % 32
+// == 0), bf16 rows whole 16-byte (K form) or 8-byte (T form) runs -- so each
+// load is one vector from a clamped address, with no branch around it (a
+// branch there makes the compiler wait for every load in flight at the loop
+// head); what lies outside the operand is zeroed when decoded.  Otherwise
+// the element-by-element forms.  FULL (FAST too): every tile lies wholly
+// inside both operands and K % 64 == 0, so nothing is clamped or masked (the
+// masks are constants the compiler folds away).
+template <int KIND, int R, bool FAST, bool FULL>
 __device__ __forceinline__ void stage_load(Stage<KIND, R>& s, const Operand& op, int64_t row0, int64_t k0, int64_t K)
 {
+    static_assert(FAST || !FULL, "FULL implies FAST");
     using S = Share<R>;
     const int t = threadIdx.x;
     if constexpr (KIND == OP_BF16_K || KIND == OP_FP4_K) {
         const int64_t row = row0 + t / S::TPR;
         const int64_t kc = k0 + S::EPT * (t % S::TPR);
-        const bool rv = row < op.rows;
-        if constexpr (KIND == OP_BF16_K) {
+        const bool rv = FULL || row < op.rows;
+        if constexpr (KIND == OP_BF16_K && FAST) {
+            // K (the backward's N) % 8 == 0: a run of 8 lies wholly inside or
+            // outside the row; bit q of ok marks the runs inside
+            const int64_t rc = rv ? row : op.rows - 1;
+            const uint16_t* p = static_cast<const uint16_t*>(op.data) + rc * op.ld;
+            uint32_t ok = 0u;
+#pragma unroll
+            for (int q = 0; q < S::EPT / 8; ++q) {
+                const int64_t k = kc + 8 * q;
+                const bool in = FULL || (rv && k < K);
+                s.v[q] = ld16(p + (in ? k : 0));
+                ok |= (uint32_t)in << q;
+            }
+            s.ok = ok;
+        } else if constexpr (KIND == OP_BF16_K) {
             // the contraction here is the backward's N, of any length: a run
             // of 8 is loaded as one vector only when 16-byte aligned and
             // wholly inside the row, else element by element up to its end
             const uint16_t* p = static_cast<const uint16_t*>(op.data) + row * op.ld + kc;
             const bool vec = (op.ld & 7) == 0;
+            s.ok = ~0u;
 #pragma unroll
             for (int q = 0; q < S::EPT / 8; ++q) {
                 const int64_t k = kc + 8 * q;
@@ -122,13 +147,13 @@ __device__ __forceinline__ void stage_load(Stage<KIND, R>& s, const Operand& op,
             // loads and its BLK scale bytes one load into sc[0] (bit 8 of
             // ok); otherwise 8-byte code loads and single scale bytes.
             const int64_t rc = rv ? row : op.rows - 1;
-            const int64_t kk = kc < K ? kc : 0;
+            const int64_t kk = FULL || kc < K ? kc : 0;
             const uint8_t* codes = static_cast<const uint8_t*>(op.data) + rc * (op.ld >> 1) + (kk >> 1);
             const uint8_t* sc = op.scales + rc * (op.ld >> 4) + (kk >> 4);
             uint32_t ok = 0u;
 #pragma unroll
-            for (int b = 0; b < S::BLK; ++b) ok |= (uint32_t)(rv && kc + 16 * b < K) << b;
-            if (S::BLK >= 2 && (op.ld % (16 * S::BLK)) == 0) {
+            for (int b = 0; b < S::BLK; ++b) ok |= (uint32_t)(FULL || (rv && kc + 16 * b < K)) << b;
+            if constexpr (S::BLK >= 2 && FAST) {
 #pragma unroll
                 for (int h = 0; h < S::BLK / 2; ++h) {
                     const u32x4 c = ld16(codes + 16 * h);
@@ -154,8 +179,23 @@ __device__ __forceinline__ void stage_load(Stage<KIND, R>& s, const Operand& op,
     } else {
         const int64_t kr0 = k0 + S::RPT * (t / S::OG);
         const int64_t o = row0 + 4 * (t % S::OG);
-        if constexpr (KIND == OP_BF16_T) {
+        if constexpr (KIND == OP_BF16_T && FAST) {
+            // the output extent (the backward's N) % 4 == 0: a run of 4 lies
+            // wholly inside or outside; bit i of ok marks the rows inside
+            const bool ov = FULL || o < op.rows;
+            const int64_t oc = ov ? o : 0;
+            uint32_t ok = 0u;
+#pragma unroll
+            for (int i = 0; i < S::RPT; ++i) {
+                const int64_t kr = kr0 + i;
+                const bool in = FULL || (ov && kr < K);
+                s.v[i] = ld8(static_cast<const uint16_t*>(op.data) + (in ? kr : 0) * op.ld + oc);
+                ok |= (uint32_t)in << i;
+            }
+            s.ok = ok;
+        } else if constexpr (KIND == OP_BF16_T) {
             const bool vec = (op.ld & 3) == 0 && o + 4 <= op.rows;   // 8-byte aligned, wholly inside
+            s.ok = ~0u;
 #pragma unroll
             for (int i = 0; i < S::RPT; ++i) {
                 const int64_t kr = kr0 + i;
@@ -175,17 +215,17 @@ __device__ __forceinline__ void stage_load(Stage<KIND, R>& s, const Operand& op,
             // row; the output extent is a multiple of 16, so a run of 4 lies
             // wholly inside or outside (clamped addresses and a validity
             // mask, as for the K form)
-            const bool ov = o < op.rows;
+            const bool ov = FULL || o < op.rows;
             const int64_t oc = ov ? o : op.rows - 4;
             uint32_t ok = 0u;
 #pragma unroll
             for (int i = 0; i < S::RPT; ++i) {
                 const int64_t kr = kr0 + i;
-                const int64_t krc = kr < K ? kr : K - 1;
+                const int64_t krc = FULL || kr < K ? kr : K - 1;
                 s.code[i] = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(op.data) +
                                                                krc * (op.ld >> 1) + (oc >> 1));
                 s.sc[i] = op.scales[krc * (op.ld >> 4) + (oc >> 4)];
-                ok |= (uint32_t)(ov && kr < K) << i;
+                ok |= (uint32_t)(FULL || (ov && kr < K)) << i;
             }
             s.ok = ok;
         }
@@ -240,7 +280,9 @@ __device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R
             const int r = u * UPP + v;   // run index
             if (r >= RUNS) break;
             if constexpr (KIND == OP_BF16_K) {
-                lds_store16(dst + 8 * r, s.v[r]);
+                const bool ok = (s.ok >> r) & 1u;
+                const u32x4 v = s.v[r];
+                lds_store16(dst + 8 * r, u32x4{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u});
             } else {
                 // block r / 2: its scale byte from the one scale load or its own
                 const int b = r >> 1;
@@ -259,7 +301,8 @@ __device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R
             const int p = u * PPP + v;
             if (p >= PAIRS) break;
             if constexpr (KIND == OP_BF16_T) {
-                const u32x2 a = s.v[2 * p], b = s.v[2 * p + 1];
+                const bool oka = (s.ok >> (2 * p)) & 1u, okb = (s.ok >> (2 * p + 1)) & 1u;
+                const u32x2 a = oka ? s.v[2 * p] : u32x2{0u, 0u}, b = okb ? s.v[2 * p + 1] : u32x2{0u, 0u};
                 tb.w[0][p] = (a[0] & 0xFFFFu) | (b[0] << 16);
                 tb.w[1][p] = (a[0] >> 16) | (b[0] & 0xFFFF0000u);
                 tb.w[2][p] = (a[1] & 0xFFFFu) | (b[1] << 16);
@@ -361,7 +404,7 @@ __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* l
 // and has the loads of step s + 2 in flight; one barrier per step separates
 // the phases.  Past the last step the loads repeat the last slice and the
 // decode fills the idle buffer, so the loop body has no branches.
-template <int KA, int KB, int BN>
+template <int KA, int KB, int BN, bool FAST, bool FULL>
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
 {
     constexpr int TJ = BN / 64;
@@ -385,10 +428,10 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
     const int64_t last = (steps - 1) * kBK;
     Stage<KA, kBM> ra[2];
     Stage<KB, BN> rb[2];
-    stage_load<KA, kBM>(ra[0], g.a, m0, 0, g.K);
-    stage_load<KB, BN>(rb[0], g.b, n0, 0, g.K);
-    stage_load<KA, kBM>(ra[1], g.a, m0, kBK < last ? kBK : last, g.K);
-    stage_load<KB, BN>(rb[1], g.b, n0, kBK < last ? kBK : last, g.K);
+    stage_load<KA, kBM, FAST, FULL>(ra[0], g.a, m0, 0, g.K);
+    stage_load<KB, BN, FAST, FULL>(rb[0], g.b, n0, 0, g.K);
+    stage_load<KA, kBM, FAST, FULL>(ra[1], g.a, m0, kBK < last ? kBK : last, g.K);
+    stage_load<KB, BN, FAST, FULL>(rb[1], g.b, n0, kBK < last ? kBK : last, g.K);
     stage_store<KA, kBM>(ra[0], lds, sa);
     stage_store<KB, BN>(rb[0], lds + kBufA, sb);
     __syncthreads();
@@ -404,8 +447,11 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
         bf16x8_t fa[2][kTI], fb[2][TJ];
         load_frags<BN>(la, lb, 0, fa[0], fb[0]);
         const int64_t kn = (s + 2) * kBK < last ? (s + 2) * kBK : last;
-        stage_load<KA, kBM>(ra[P], g.a, m0, kn, g.K);
-        stage_load<KB, BN>(rb[P], g.b, n0, kn, g.K);
+        stage_load<KA, kBM, FAST, FULL>(ra[P], g.a, m0, kn, g.K);
+        stage_load<KB, BN, FAST, FULL>(rb[P], g.b, n0, kn, g.K);
+        // keep the scheduler from sinking these loads towards their use in
+        // the next step (which would shorten the prefetch to nothing)
+        __builtin_amdgcn_sched_barrier(0);
         TBuf<kBM> ta;
         TBuf<BN> tb;
 #pragma unroll
@@ -464,13 +510,30 @@ hipError_t launch_gemm(const Operand& a, const Operand& b, uint16_t* c, int64_t 
     g.tiles_m = (int)((M + kBM - 1) / kBM);
     g.tiles_n = (int)((N + bn - 1) / bn);
     const dim3 grid((unsigned)tile_count(M, N, bn));
+    // the vector load forms: NVFP4 operands stored [rows][K] need K % 32 ==
+    // 0; a bf16 grad_y needs its row length N % 8 == 0 ([M][N] read along N)
+    // or N % 4 == 0 (read along M)
+    // (and with every tile inside: M % 256, N % BN, K % 64 all 0, no masks)
+    const bool fast = KA == OP_FP4_K ? (K % 32) == 0 : KA == OP_BF16_K ? (a.ld % 8) == 0 : (a.ld % 4) == 0;
+    const bool full = fast && M % kBM == 0 && N % bn == 0 && K % kBK == 0;
+    const dim3 block(kThreads);
     if constexpr (kCanWiden) {
         if (wide) {
-            hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 256>), grid, dim3(kThreads), 0, stream, g);
+            if (full)
+                hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 256, true, true>), grid, block, 0, stream, g);
+            else if (fast)
+                hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 256, true, false>), grid, block, 0, stream, g);
+            else
+                hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 256, false, false>), grid, block, 0, stream, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 128>), grid, dim3(kThreads), 0, stream, g);
+    if (full)
+        hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 128, true, true>), grid, block, 0, stream, g);
+    else if (fast)
+        hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 128, true, false>), grid, block, 0, stream, g);
+    else
+        hipLaunchKernelGGL((w4a4_gemm_kernel<KA, KB, 128, false, false>), grid, block, 0, stream, g);
     return hipGetLastError();
 }
 
