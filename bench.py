@@ -49,6 +49,28 @@ def parse():
     return ap.parse_args()
 
 
+class phase:
+    """Marks one part of the run as a named ROCTX range (torch.cuda.nvtx maps
+    to ROCTX on ROCm), the device synchronised before the range closes, so
+    that a kernel trace taken with rocprofv3 --marker-trace can assign every
+    dispatch to the part that issued it."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        import torch
+        torch.cuda.synchronize()
+        torch.cuda.nvtx.range_push(self.name)
+        return self
+
+    def __exit__(self, *exc):
+        import torch
+        torch.cuda.synchronize()
+        torch.cuda.nvtx.range_pop()
+        return False
+
+
 def ensure_built():
     from nvfp4_quantization_aware_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):
@@ -515,22 +537,23 @@ def main():
     wl = Workload(dev)
     torch.cuda.synchronize()
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
+    with phase("warmup"):
+        for _ in range(args.warmup):
+            wl.step()
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
     print("[bench] timing %d steps" % K, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for k in range(K):
-        wl.step(evs[k])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with phase("timed_steps"):
+        wall0 = time.perf_counter()
+        t_start.record()
+        for k in range(K):
+            wl.step(evs[k])
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / K
     part_ms = {}
@@ -581,11 +604,19 @@ def main():
                      "traffic": measured_traffic("kl_seg_bf16_kernel<1, false>") if dom == "kl_fwd_bwd" else None},
         "wall_s_timed": round(wall, 3),
     }
-    out["extensions"] = {"kl_topk_fwd_bwd": time_topk(wl, dev), "kl_topp_fwd_bwd": time_topp(wl, dev), **time_fp8(wl), "w4a4_linear": time_linear(wl, dev),
-                         "nvfp4_qdq_bwd_clipped_moe": time_clipped_ste(wl),
-                         "nvfp4_frozen_sgd_step_moe": time_sgd_step(wl),
-                         "c1_fp32_quantize_256x1024": time_c1(dev),
-                         "wait0_fallbacks": time_wait0(wl)}
+    ext = {}
+    for name, fn in (("kl_topk_fwd_bwd", lambda: time_topk(wl, dev)), ("kl_topp_fwd_bwd", lambda: time_topp(wl, dev)),
+                     ("fp8", lambda: time_fp8(wl)), ("w4a4_linear", lambda: time_linear(wl, dev)),
+                     ("nvfp4_qdq_bwd_clipped_moe", lambda: time_clipped_ste(wl)),
+                     ("nvfp4_frozen_sgd_step_moe", lambda: time_sgd_step(wl)),
+                     ("c1_fp32_quantize_256x1024", lambda: time_c1(dev)), ("wait0_fallbacks", lambda: time_wait0(wl))):
+        with phase(name):
+            r = fn()
+        if name == "fp8":
+            ext.update(r)
+        else:
+            ext[name] = r
+    out["extensions"] = ext
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_fraction)
