@@ -420,21 +420,22 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         // TOPK: dropped entries become -inf, whose weights 2^(-inf) are
         // exactly 0 once a kept entry has set the maxima; a unit of this lane
         // with no kept entry changes nothing and is skipped (which also
-        // keeps -inf - (-inf) out of the exponent)
+        // keeps -inf - (-inf) out of the exponent).  dx takes every entry of
+        // the units it sees, dropped ones too: it only has to bound the kept
+        // entries' s - t from above (for the choice of pass 2's form), and a
+        // maximum over more entries does, one select per entry cheaper.
         float d[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) d[i] = tv[i] - sv[i];
+        dx = maxnan(maxnan(maxnan(dx, -d[0]), maxnan(-d[1], -d[2])), maxnan(maxnan(-d[3], -d[4]), -d[5]));
+        dx = maxnan(dx, maxnan(-d[6], -d[7]));
         if constexpr (TOPK) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const bool kept = tv[i] >= tau;
                 tv[i] = kept ? tv[i] : -__builtin_inff();
                 sv[i] = kept ? sv[i] : -__builtin_inff();
-                dx = maxnan(dx, kept ? -d[i] : -__builtin_inff());
             }
-        } else {
-            dx = maxnan(maxnan(maxnan(dx, -d[0]), maxnan(-d[1], -d[2])), maxnan(maxnan(-d[3], -d[4]), -d[5]));
-            dx = maxnan(dx, maxnan(-d[6], -d[7]));
         }
         const float tmax = max8(tv);
         if (TOPK && tmax == -__builtin_inff()) continue;
