@@ -8,9 +8,11 @@ fp32-accumulated sums of the bf16 QDQ values' products, compared with the
 binary64 oracle product of the oracle's QDQ values within the bound that
 arithmetic allows: half a bf16 ulp of the result plus 2 K 2^-24 sum_k
 |a_k b_k| (fp32 rounding of up to K products and partial sums in any order).
-Shapes span several 128 x 128 x 64 tiles with ragged edges in every
-dimension, rows whose lengths break 16-byte alignment (bf16 grad_y with
-N % 8 != 0), and single elements.
+Shapes span several 256 x 256 (forward) and 256 x 128 (backward) tiles of
+64-deep steps with ragged edges in every dimension, each of the kernel's
+three load forms, rows whose lengths break 16-byte alignment (bf16 grad_y
+with N % 8 != 0), single elements, and one MoE expert's projection
+8192 x 2048 x 4096 compared in full.
 """
 import numpy as np
 import pytest
@@ -78,10 +80,15 @@ def run_case(dev, orc, M, N, K, dtype, seed, frozen=False):
     assert_product_close(host(gw), gwr, np.abs(gf).T @ np.abs(xf), M, "grad_w")
 
 
+# Each product takes one of three load forms, chosen per launch: whole tiles
+# (M % 256, N % tile, K % 64 all 0, e.g. 256 x 512 x 1024), aligned rows
+# (K % 32 == 0 for the NVFP4 operands, N % 8 or N % 4 for the bf16
+# gradient, e.g. 64 x 32 x 128), or element by element (e.g. 37 x 19 x 48,
+# 300 x 260 x 208 with K % 32 = 16).
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 32, 128, torch.bfloat16), (37, 19, 48, torch.float32),
                                          (256, 512, 1024, torch.bfloat16), (1, 1, 16, torch.bfloat16),
                                          (300, 260, 208, torch.bfloat16), (129, 131, 80, torch.float32),
-                                         (200, 136, 4112, torch.bfloat16)])
+                                         (200, 136, 4112, torch.bfloat16), (512, 768, 320, torch.bfloat16)])
 def test_linear_small(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=M + N + K)
 
@@ -91,8 +98,10 @@ def test_linear_frozen_weight_scales(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=7 * M + N, frozen=True)
 
 
-def test_linear_expert_shape_sampled(dev, orc):
-    # one MoE expert's projection: 8192 tokens x 4096 -> 2048 (the weight shape of the MoE workload)
+def test_linear_expert_shape_full(dev, orc):
+    # one MoE expert's projection: 8192 tokens x 4096 -> 2048 (the weight
+    # shape of the MoE workload), every element of y, grad_x and grad_w
+    # against the binary64 products of the oracle's QDQ values
     M, N, K = 8192, 2048, 4096
     announce("linear 8192x2048x4096 generate")
     x, _ = synth.student_t_activations_bf16(M, K, seed=3, device=dev)
@@ -104,13 +113,9 @@ def test_linear_expert_shape_sampled(dev, orc):
     torch.cuda.synchronize()
     check_packed(orc, xq, host(x), M, K)
     check_packed(orc, wq, host(w), N, K)
-    xqr = orc.nvfp4_quantize(host(x))[3]
-    wqr = orc.nvfp4_quantize(host(w))[3]
-    rows = [0, 1, 4097, 8191]
-    xf, wf = f64(xqr.reshape(M, K)[rows]), f64(wqr.reshape(N, K))
-    assert_product_close(host(y)[rows], xf @ wf.T, np.abs(xf) @ np.abs(wf).T, K, "y rows")
+    xf = f64(orc.nvfp4_quantize(host(x))[3].reshape(M, K))
+    wf = f64(orc.nvfp4_quantize(host(w))[3].reshape(N, K))
     gf = f64(host(gy))
-    cols = [0, 100, 4095]
-    assert_product_close(host(gx)[rows], gf[rows] @ wf, np.abs(gf[rows]) @ np.abs(wf), N, "grad_x rows")
-    xall = f64(xqr.reshape(M, K))
-    assert_product_close(host(gw)[:, cols], gf.T @ xall[:, cols], np.abs(gf).T @ np.abs(xall[:, cols]), M, "grad_w cols")
+    assert_product_close(host(y), xf @ wf.T, np.abs(xf) @ np.abs(wf).T, K, "y")
+    assert_product_close(host(gx), gf @ wf, np.abs(gf) @ np.abs(wf), N, "grad_x")
+    assert_product_close(host(gw), gf.T @ xf, np.abs(gf).T @ np.abs(xf), M, "grad_w")
