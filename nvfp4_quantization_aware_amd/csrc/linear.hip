@@ -355,15 +355,16 @@ __device__ __forceinline__ void stage_store(const Stage<KIND, R>& s, uint16_t* l
 
 // tile index of workgroup `bid`: consecutive workgroups go to different XCDs
 // (eight of them), so each XCD is given a contiguous run of tiles, ordered in
-// groups of 8 tile rows so that a run shares operand tiles in its XCD's L2
+// groups of GH tile rows so that a run shares operand tiles in its XCD's L2
+template <int GH>
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn)
 {
     const int total = tiles_m * tiles_n;
     int id = bid;
     if ((total & 7) == 0) id = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int per_group = 8 * tiles_n;
-    const int g = id / per_group, first = g * 8;
-    const int gm = tiles_m - first < 8 ? tiles_m - first : 8;
+    const int per_group = GH * tiles_n;
+    const int g = id / per_group, first = g * GH;
+    const int gm = tiles_m - first < GH ? tiles_m - first : GH;
     const int r = id - g * per_group;
     tm = first + r % gm;
     tn = r / gm;
@@ -411,8 +412,13 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
     constexpr int kBufA = kBM * kLds, kBufB = BN * kLds;
     __shared__ __align__(16) uint16_t lds[2 * (kBufA + kBufB)];
 
+    // a bf16 A operand (the backward's grad_y) moves 4x the bytes of an NVFP4
+    // one per tile row: fewer tile rows in flight keep its rows in L2 (4
+    // against 8 measured 10% faster for grad_x; the forward is the same at
+    // 2 to 16)
+    constexpr int GH = KA == OP_FP4_K ? 8 : 4;
     int tm, tn;
-    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    tile_of<GH>(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
     const float sa = tensor_scale<KA>(g.a), sb = tensor_scale<KB>(g.b);
     const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
