@@ -206,6 +206,10 @@ int64_t qad_set_wait_limit_us(int64_t us)
 
 size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
 {
+    // (B, R, C) of the W4A4 linear are (M, N, K): its operands are M x K and
+    // N x K, each checked by the quantizer's own size; every other op takes a
+    // batch of B tensors of R x C elements
+    if (op == QAD_OP_W4A4_LINEAR) return round256(qad::linear_workspace_bytes(B, R, C));
     if (tensor_elems(B, R, C) < 0) return 0;
     switch (op) {
     case QAD_OP_AMAX:
@@ -214,7 +218,7 @@ size_t qad_workspace_bytes(qad_op_t op, int64_t B, int64_t R, int64_t C)
     case QAD_OP_KL: return round256(qad::kl_workspace_bytes(R, C));
     case QAD_OP_KL_TOPK:
     case QAD_OP_KL_TOPP: return round256(qad::kl_topk_workspace_bytes(R, C));
-    case QAD_OP_W4A4_LINEAR: return round256(qad::linear_workspace_bytes(B, R, C));
+    case QAD_OP_W4A4_LINEAR: break;
     }
     return 0;
 }

@@ -607,6 +607,7 @@ qad_status_t quantize_packed(const void* src, qad_dtype_t dt, int64_t R, int64_t
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
+    if (!dims_ok(M, N, K) || K <= 0 || K % 16 != 0) return 0;   // the entry points' shape rule
     const size_t rx = qad_workspace_bytes(QAD_OP_QUANTIZE, 1, M, K);
     const size_t rw = qad_workspace_bytes(QAD_OP_QUANTIZE, 1, N, K);
     return round256(rx > rw ? rx : rw);

@@ -160,6 +160,12 @@ def test_w4a4_linear_rejects(L):
     fw, bw = L.qad_w4a4_linear_fwd, L.qad_w4a4_linear_bwd
     ws = L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, 64, 32, 128)
     assert ws > 0 and ws % 256 == 0            # the quantizer's records only
+    # (M, N, K) is no tensor: M N K may pass the tensor-size bound as long as
+    # each operand (M x K, N x K) is within it; the records of the larger one
+    for M, N, K in ((8200, 2048, 4096), (1 << 20, 4096, 8192), (64, 32, 128)):
+        big = max(L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 1, M, K), L.qad_workspace_bytes(q.QAD_OP_QUANTIZE, 1, N, K))
+        assert big > 0 and L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, M, N, K) == big
+    assert L.qad_workspace_bytes(q.QAD_OP_W4A4_LINEAR, -1, 32, 128) == 0
     a = lambda **kw: [kw.get("x", P), kw.get("w", P * 2), kw.get("dt", 1), kw.get("M", 64), kw.get("N", 32),
                       kw.get("K", 128), kw.get("wsc", None), kw.get("wts", None), kw.get("y", P * 3),
                       kw.get("xq", P * 4), kw.get("wq", P * 5), kw.get("ws", P * 6), kw.get("wsb", ws), None]

@@ -93,6 +93,14 @@ def test_linear_small(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=M + N + K)
 
 
+# 256-wide forward tiles (at least 256 of them) in the two load forms other
+# than whole tiles: a ragged last tile row (M = 8200, aligned rows) and rows
+# of K % 32 = 16 (element by element)
+@pytest.mark.parametrize("M,N,K", [(8200, 2048, 4096), (8192, 2048, 4112)])
+def test_linear_wide_tiles_ragged(dev, orc, M, N, K):
+    run_case(dev, orc, M, N, K, torch.bfloat16, seed=M + K)
+
+
 @pytest.mark.parametrize("M,N,K,dtype", [(64, 32, 128, torch.bfloat16), (40, 24, 256, torch.float32)])
 def test_linear_frozen_weight_scales(dev, orc, M, N, K, dtype):
     run_case(dev, orc, M, N, K, dtype, seed=7 * M + N, frozen=True)
