@@ -276,8 +276,9 @@ def time_c1(dev, iters=200):
     256 x 1024 tensor (N(0,1), 0.1% outliers x50) emitting packed codes,
     block scales, the tensor scale and bf16 values.  1.7 MB of traffic takes
     about 0.2 us at peak bandwidth, so the call is bound by launch latency:
-    reported in microseconds (median of single timed calls, and the mean of
-    back-to-back calls) and GB/s, outside the step's value."""
+    reported in microseconds (median of single timed calls, the mean of
+    back-to-back calls, and per call of a HIP graph of 20 calls replayed) and
+    GB/s, outside the step's value."""
     import torch
     import nvfp4_quantization_aware_amd as q
     from nvfp4_quantization_aware_amd import synth
@@ -308,10 +309,33 @@ def time_c1(dev, iters=200):
     torch.cuda.synchronize()
     mean_us = e0.elapsed_time(e1) * 1e3 / iters
     med_us = sorted(singles)[len(singles) // 2]
+    # the same calls captured once into a HIP graph and replayed: the GPU-side
+    # time per call without the host's launch overhead
+    per_graph = 20
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        f()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
     nbytes = 4 * n + n // 2 + n // 16 + 4 + 2 * n
     return {"shape": [256, 1024], "dtype": "f32", "bytes": nbytes, "us_median_single": round(med_us, 2),
-            "us_mean_back_to_back": round(mean_us, 2), "GB/s": round(nbytes / (med_us * 1e-6) / 1e9, 1),
-            "bound": "launch latency"}
+            "us_mean_back_to_back": round(mean_us, 2), "us_per_call_graph_replay": round(graph_us, 2),
+            "GB/s": round(nbytes / (med_us * 1e-6) / 1e9, 1),
+            "GB/s_graph_replay": round(nbytes / (graph_us * 1e-6) / 1e9, 1), "bound": "launch latency"}
 
 
 def time_wait0(wl, iters=5):
