@@ -29,7 +29,30 @@ namespace {
 constexpr int kBM = 256, kBK = 64;              // workgroup tile: 256 x BN (BN 256 or 128), 64-deep steps
 constexpr int kThreads = 512;                    // eight waves, two per SIMD, 4 (M) x 2 (N) over the tile
 constexpr int kWM = 4;                           // waves along M; each owns 256 / kWM rows of the tile
-constexpr int kLds = kBK + 8;                    // LDS row stride in bf16 (144 B: conflict-free 16-B reads)
+// LDS tile layouts, rows of 64 contraction values (bf16):
+//   padded (SWZ false): row stride 72 (144 B); the fragment reads (lanes
+//     0..31 on rows r0..r0+31 at one 16-byte chunk) and the row-major stores
+//     are conflict-free;
+//   swizzled (SWZ true, the kernels with a transposed operand): row stride
+//     64 (128 B), chunk c of row r stored at c ^ (r % 8) ^ (r / 8 % 8).  The
+//     fragment reads still see 8 consecutive rows on 8 distinct chunks, and
+//     the transposed stores (16 lanes on rows 4 i + e, i = 0..15) land on
+//     each chunk twice instead of 8 of them on one bank group (measured:
+//     bank conflicts were half of grad_x's LDS time and two thirds of
+//     grad_w's).  The forward keeps the padded layout, whose addresses cost
+//     fewer registers in its 256-wide kernel.
+template <bool SWZ> constexpr int lds_stride() { return SWZ ? kBK : kBK + 8; }
+
+template <bool SWZ>
+__device__ __forceinline__ int lds_pos(int row, int col)
+{
+    if constexpr (SWZ) {
+        const int sw = (row & 7) ^ ((row >> 3) & 7);
+        return row * kBK + ((((col >> 3) ^ sw) & 7) << 3) + (col & 7);
+    } else {
+        return row * (kBK + 8) + col;
+    }
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -262,27 +285,28 @@ __device__ __forceinline__ float block_scale(uint32_t c, float s_g, bool ok)
 // output row 4 og + e, contraction rows 2 p and 2 p + 1 of the thread's run.
 template <int R> struct TBuf { uint32_t w[4][Share<R>::RPT / 2]; };
 
-// Registers -> LDS tile [R output rows][64 contraction] (bf16, stride kLds),
+// Registers -> LDS tile [R output rows][64 contraction] (bf16, laid out by lds_pos),
 // in four parts (u = 0..3) so that the decode can be spread over the four
 // 16-deep MFMA slices of a step.  A part of a K operand is a quarter of the
 // thread's 8-value runs; one of a T operand decodes a quarter of its
 // contraction-row pairs, and the last part stores the transposed rows.
-template <int KIND, int R>
+template <int KIND, int R, bool SWZ>
 __device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R>& tb, uint16_t* lds, float s_g, int u)
 {
     using S = Share<R>;
     const int t = threadIdx.x;
     if constexpr (KIND == OP_BF16_K || KIND == OP_FP4_K) {
         constexpr int RUNS = S::EPT / 8, UPP = (RUNS + 3) / 4;   // 8-value runs, per part
-        uint16_t* dst = lds + (t / S::TPR) * kLds + S::EPT * (t % S::TPR);
+        const int drow = t / S::TPR, dcol = S::EPT * (t % S::TPR);
 #pragma unroll
         for (int v = 0; v < UPP; ++v) {
             const int r = u * UPP + v;   // run index
             if (r >= RUNS) break;
+            uint16_t* dst = lds + lds_pos<SWZ>(drow, dcol + 8 * r);
             if constexpr (KIND == OP_BF16_K) {
                 const bool ok = (s.ok >> r) & 1u;
                 const u32x4 v = s.v[r];
-                lds_store16(dst + 8 * r, u32x4{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u});
+                lds_store16(dst, u32x4{ok ? v[0] : 0u, ok ? v[1] : 0u, ok ? v[2] : 0u, ok ? v[3] : 0u});
             } else {
                 // block r / 2: its scale byte from the one scale load or its own
                 const int b = r >> 1;
@@ -290,8 +314,7 @@ __device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R
                 const uint32_t sb = (s.ok & 0x100u) ? s.sc[0] >> (8 * b) : s.sc[b];
                 const float se = block_scale(sb & 127u, s_g, ok);
                 const uint32_t c = ok ? s.code[b][r & 1] : 0u;
-                lds_store16(dst + 8 * r,
-                            u32x4{qdq_pair<0>(c, se), qdq_pair<1>(c, se), qdq_pair<2>(c, se), qdq_pair<3>(c, se)});
+                lds_store16(dst, u32x4{qdq_pair<0>(c, se), qdq_pair<1>(c, se), qdq_pair<2>(c, se), qdq_pair<3>(c, se)});
             }
         }
     } else {
@@ -329,28 +352,29 @@ __device__ __forceinline__ void stage_store_part(const Stage<KIND, R>& s, TBuf<R
         }
         if (u == 3) {
             // output row 4 og + e receives contraction [RPT cg, +RPT)
-            uint16_t* dst = lds + (4 * (t % S::OG)) * kLds + S::RPT * (t / S::OG);
+            const int row0 = 4 * (t % S::OG), col0 = S::RPT * (t / S::OG);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if constexpr (S::RPT >= 8) {
 #pragma unroll
                     for (int h = 0; h < S::RPT / 8; ++h)
-                        lds_store16(dst + e * kLds + 8 * h,
+                        lds_store16(lds + lds_pos<SWZ>(row0 + e, col0 + 8 * h),
                                     u32x4{tb.w[e][4 * h], tb.w[e][4 * h + 1], tb.w[e][4 * h + 2], tb.w[e][4 * h + 3]});
                 } else {
-                    *reinterpret_cast<u32x2*>(dst + e * kLds) = u32x2{tb.w[e][0], tb.w[e][1]};
+                    // 8 bytes: half a chunk (col0 % 8 is 0 or 4)
+                    *reinterpret_cast<u32x2*>(lds + lds_pos<SWZ>(row0 + e, col0)) = u32x2{tb.w[e][0], tb.w[e][1]};
                 }
             }
         }
     }
 }
 
-template <int KIND, int R>
+template <int KIND, int R, bool SWZ>
 __device__ __forceinline__ void stage_store(const Stage<KIND, R>& s, uint16_t* lds, float s_g)
 {
     TBuf<R> tb;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) stage_store_part<KIND, R>(s, tb, lds, s_g, u);
+    for (int u = 0; u < 4; ++u) stage_store_part<KIND, R, SWZ>(s, tb, lds, s_g, u);
 }
 
 // tile index of workgroup `bid`: consecutive workgroups go to different XCDs
@@ -379,7 +403,7 @@ template <int KIND> __device__ __forceinline__ float tensor_scale(const Operand&
 // [TI 32 wm + 32 i, +32), B rows [BN/2 wn + 32 j, +32); lane l holds row
 // l % 32, contraction [8 (l / 32), +8) of the slice (the MFMA operand layout)
 constexpr int kTI = kBM / kWM / 32;   // MFMA tiles of a wave along M
-template <int BN>
+template <int BN, bool SWZ>
 __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* lb, int ks, bf16x8_t (&fa)[kTI],
                                            bf16x8_t (&fb)[BN / 64])
 {
@@ -388,10 +412,10 @@ __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* l
     const int kcol = ks * 16 + 8 * (l >> 5);
 #pragma unroll
     for (int i = 0; i < kTI; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(la + (wm * 32 * kTI + i * 32 + (l & 31)) * kLds + kcol);
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(la + lds_pos<SWZ>(wm * 32 * kTI + i * 32 + (l & 31), kcol));
 #pragma unroll
     for (int j = 0; j < BN / 64; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + (wn * (BN / 2) + j * 32 + (l & 31)) * kLds + kcol);
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + lds_pos<SWZ>(wn * (BN / 2) + j * 32 + (l & 31), kcol));
 }
 
 // C[M][N] = sum_k A(m, k) B(n, k), bf16 out of fp32 accumulation in a fixed
@@ -409,7 +433,8 @@ template <int KA, int KB, int BN, bool FAST, bool FULL>
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
 {
     constexpr int TJ = BN / 64;
-    constexpr int kBufA = kBM * kLds, kBufB = BN * kLds;
+    constexpr bool SWZ = KA == OP_BF16_T || KA == OP_FP4_T || KB == OP_BF16_T || KB == OP_FP4_T;
+    constexpr int kBufA = kBM * lds_stride<SWZ>(), kBufB = BN * lds_stride<SWZ>();
     __shared__ __align__(16) uint16_t lds[2 * (kBufA + kBufB)];
 
     // a bf16 A operand (the backward's grad_y) moves 4x the bytes of an NVFP4
@@ -438,8 +463,8 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
     stage_load<KB, BN, FAST, FULL>(rb[0], g.b, n0, 0, g.K);
     stage_load<KA, kBM, FAST, FULL>(ra[1], g.a, m0, kBK < last ? kBK : last, g.K);
     stage_load<KB, BN, FAST, FULL>(rb[1], g.b, n0, kBK < last ? kBK : last, g.K);
-    stage_store<KA, kBM>(ra[0], lds, sa);
-    stage_store<KB, BN>(rb[0], lds + kBufA, sb);
+    stage_store<KA, kBM, SWZ>(ra[0], lds, sa);
+    stage_store<KB, BN, SWZ>(rb[0], lds + kBufA, sb);
     __syncthreads();
 
     // step s: buffer s % 2 is multiplied, registers (s + 1) % 2 are decoded
@@ -451,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
         uint16_t* wa = lds + (P ^ 1) * (kBufA + kBufB);
         uint16_t* wb = wa + kBufA;
         bf16x8_t fa[2][kTI], fb[2][TJ];
-        load_frags<BN>(la, lb, 0, fa[0], fb[0]);
+        load_frags<BN, SWZ>(la, lb, 0, fa[0], fb[0]);
         const int64_t kn = (s + 2) * kBK < last ? (s + 2) * kBK : last;
         stage_load<KA, kBM, FAST, FULL>(ra[P], g.a, m0, kn, g.K);
         stage_load<KB, BN, FAST, FULL>(rb[P], g.b, n0, kn, g.K);
@@ -462,9 +487,9 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
         TBuf<BN> tb;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            if (ks + 1 < kBK / 16) load_frags<BN>(la, lb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-            stage_store_part<KA, kBM>(ra[P ^ 1], ta, wa, sa, ks);
-            stage_store_part<KB, BN>(rb[P ^ 1], tb, wb, sb, ks);
+            if (ks + 1 < kBK / 16) load_frags<BN, SWZ>(la, lb, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            stage_store_part<KA, kBM, SWZ>(ra[P ^ 1], ta, wa, sa, ks);
+            stage_store_part<KB, BN, SWZ>(rb[P ^ 1], tb, wb, sb, ks);
 #pragma unroll
             for (int i = 0; i < kTI; ++i)
 #pragma unroll
