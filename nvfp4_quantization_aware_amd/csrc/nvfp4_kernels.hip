@@ -435,12 +435,20 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantizeArgs a, int
     const int64_t u0 = j * CH::UNITS;
     const int t = threadIdx.x;
 
+    // One pass: the chunk's loads are issued at the highest wave priority, so
+    // that the arbiter serves a wave that is starting its loads before the
+    // resident waves that are coding a chunk; that gets more bytes in flight
+    // while other workgroups wait on their tensor's maximum (the 128-expert
+    // batch: 0.815 -> 0.770 ms; the other modes, the amax pass and the copy
+    // measured no better or worse with it).
+    if constexpr (MODE == MODE_ONEPASS) __builtin_amdgcn_s_setprio(3);
     Raw<BF16> raw[CH::U];
 #pragma unroll
     for (int k = 0; k < CH::U; ++k) {
         const int64_t u = u0 + k * kQThreads + t;
         raw[k] = load_raw<BF16>(a.x, ubase + u, u < units);
     }
+    if constexpr (MODE == MODE_ONEPASS) __builtin_amdgcn_s_setprio(0);
     float s_g;
     if constexpr (MODE == MODE_FROZEN) {
         s_g = a.tscale_in[b];
