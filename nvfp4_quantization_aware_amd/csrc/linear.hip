@@ -418,6 +418,10 @@ __device__ __forceinline__ void load_frags(const uint16_t* la, const uint16_t* l
         fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + lds_pos<SWZ>(wn * (BN / 2) + j * 32 + (l & 31), kcol));
 }
 
+// An NVFP4 A operand stored [K][rows] is the weight of grad_x computed as
+// grad_x^T = wq^T grad_y^T; that product's C is written transposed.
+template <int KA> constexpr bool kTransposedOut = KA == OP_FP4_T;
+
 // C[M][N] = sum_k A(m, k) B(n, k), bf16 out of fp32 accumulation in a fixed
 // order (k ascending in steps of 64, each step's four 16-deep MFMAs in
 // order).  One 256 x BN tile per workgroup of eight waves, two per SIMD;
@@ -437,11 +441,11 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
     constexpr int kBufA = kBM * lds_stride<SWZ>(), kBufB = BN * lds_stride<SWZ>();
     __shared__ __align__(16) uint16_t lds[2 * (kBufA + kBufB)];
 
-    // a bf16 A operand (the backward's grad_y) moves 4x the bytes of an NVFP4
+    // a bf16 A operand (grad_y^T for grad_w) moves 4x the bytes of an NVFP4
     // one per tile row: fewer tile rows in flight keep its rows in L2 (4
-    // against 8 measured 10% faster for grad_x; the forward is the same at
-    // 2 to 16)
-    constexpr int GH = KA == OP_FP4_K ? 8 : 4;
+    // against 8 measured 10% faster for grad_y as A); with an NVFP4 A the
+    // products are the same at 2 to 16 within 3%
+    constexpr int GH = KA == OP_FP4_K || KA == OP_FP4_T ? 8 : 4;
     int tm, tn;
     tile_of<GH>(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
@@ -510,10 +514,24 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g)
         for (int j = 0; j < TJ; ++j) {
             const int64_t col = n0 + wn * (BN / 2) + j * 32 + (l & 31);
             if (col >= g.N) continue;
+            if constexpr (kTransposedOut<KA>) {
+                // C stored transposed (element (row, col) at col * M + row; M
+                // % 16 == 0): accumulators 4q .. 4q + 3 are four consecutive
+                // rows, so one 8-byte store each
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 32 * kTI + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
-                if (row < g.M) g.c[row * g.N + col] = (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t row = m0 + wm * 32 * kTI + i * 32 + 8 * q + 4 * (l >> 5);
+                    if (row < g.M)
+                        *reinterpret_cast<u32x2*>(g.c + col * g.M + row) =
+                            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = m0 + wm * 32 * kTI + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+                    if (row < g.M) g.c[row * g.N + col] = (uint16_t)(pack_bf16x2(acc[i][j][e], 0.0f) & 0xFFFFu);
+                }
             }
         }
 }
@@ -545,7 +563,10 @@ hipError_t launch_gemm(const Operand& a, const Operand& b, uint16_t* c, int64_t 
     // 0; a bf16 grad_y needs its row length N % 8 == 0 ([M][N] read along N)
     // or N % 4 == 0 (read along M)
     // (and with every tile inside: M % 256, N % BN, K % 64 all 0, no masks)
-    const bool fast = KA == OP_FP4_K ? (K % 32) == 0 : KA == OP_BF16_K ? (a.ld % 8) == 0 : (a.ld % 4) == 0;
+    const bool fast = KA == OP_FP4_K   ? (K % 32) == 0
+                      : KA == OP_FP4_T ? (b.ld % 8) == 0   // B is grad_y read along N
+                      : KA == OP_BF16_K ? (a.ld % 8) == 0
+                                        : (a.ld % 4) == 0;
     const bool full = fast && M % kBM == 0 && N % bn == 0 && K % kBK == 0;
     const dim3 block(kThreads);
     if constexpr (kCanWiden) {
@@ -715,9 +736,15 @@ qad_status_t qad_w4a4_linear_bwd(const void* grad_y, const void* xq, const void*
         (grad_w && overlap(grad_w, gwb, xq, qad_nvfp4_packed_bytes(M, K))))
         return QAD_ERR_INVALID_ARG;
     if (grad_x) {
-        // grad_x[M][K] = sum_n grad_y[m][n] wq(n, k): A = grad_y rows, B = wq stored [N][K]
-        const hipError_t e = launch_gemm<OP_BF16_K, OP_FP4_T>(bf16_operand(grad_y, N, M), packed_operand(wq, N, K, K),
-                                                              static_cast<uint16_t*>(grad_x), M, K, N, s);
+        // grad_x[M][K] = sum_n grad_y[m][n] wq(n, k), computed as its transpose
+        // [K][M]: A = wq stored [N][K] (output rows k), B = grad_y rows, C
+        // written transposed into grad_x.  The bf16 grad_y is then the
+        // 128-wide operand, read K / 256 times instead of K / 128 times (the
+        // other way round: grad_y as A, 32 KiB per step and tile; 298 -> 223
+        // us on 8192 x 2048 x 4096); grad_w measured slower transposed
+        // (212 -> 228 us), so it keeps grad_y^T as its A operand.
+        const hipError_t e = launch_gemm<OP_FP4_T, OP_BF16_K>(packed_operand(wq, N, K, K), bf16_operand(grad_y, N, M),
+                                                              static_cast<uint16_t*>(grad_x), K, M, N, s);
         if (e != hipSuccess) return QAD_ERR_HIP;
     }
     if (grad_w) {
