@@ -354,11 +354,12 @@ struct Unit {
     }
 };
 
-// Gradients of one unit (masked by the teacher threshold when TOPK) written
-// to `unit` of the gradient; LOSS adds the unit's term-wise KL to acc.
+// Gradients of one unit (masked by the teacher threshold when TOPK) as the
+// words unit_grad stores: bf16 in lo (GRAD 1), or binary32 in lo and hi
+// (GRAD 2); LOSS adds the unit's term-wise KL to acc.
 template <int GRAD, bool TOPK, int FORM>
-__device__ __forceinline__ void unit_grad(const float (&tv)[8], const float (&sv)[8], float c, float tau,
-                                          const RowConst& k, const KlArgs& a, int64_t unit, LossAcc& acc)
+__device__ __forceinline__ void unit_grad_words(const float (&tv)[8], const float (&sv)[8], float c, float tau,
+                                                const RowConst& k, LossAcc& acc, v4u& lo, v4u& hi)
 {
     float g[8];
     LossAcc ua{0.0f, 0.0f, 0.0f};
@@ -377,12 +378,32 @@ __device__ __forceinline__ void unit_grad(const float (&tv)[8], const float (&sv
         acc.p += ua.p;
     }
     if constexpr (GRAD == 1) {
-        stnt(a.grad, unit, v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                               pack_bf16x2(g[6], g[7])});
+        lo = v4u{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
     } else if constexpr (GRAD == 2) {
-        stnt(a.grad, 2 * unit, v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])});
-        stnt(a.grad, 2 * unit + 1, v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])});
+        lo = v4u{as_u(g[0]), as_u(g[1]), as_u(g[2]), as_u(g[3])};
+        hi = v4u{as_u(g[4]), as_u(g[5]), as_u(g[6]), as_u(g[7])};
     }
+}
+
+// the words of unit_grad_words written to `unit` of the gradient
+template <int GRAD>
+__device__ __forceinline__ void store_grad_unit(const KlArgs& a, int64_t unit, v4u lo, v4u hi)
+{
+    if constexpr (GRAD == 1) {
+        stnt(a.grad, unit, lo);
+    } else if constexpr (GRAD == 2) {
+        stnt(a.grad, 2 * unit, lo);
+        stnt(a.grad, 2 * unit + 1, hi);
+    }
+}
+
+template <int GRAD, bool TOPK, int FORM>
+__device__ __forceinline__ void unit_grad(const float (&tv)[8], const float (&sv)[8], float c, float tau,
+                                          const RowConst& k, const KlArgs& a, int64_t unit, LossAcc& acc)
+{
+    v4u lo{0u, 0u, 0u, 0u}, hi{0u, 0u, 0u, 0u};
+    unit_grad_words<GRAD, TOPK, FORM>(tv, sv, c, tau, k, acc, lo, hi);
+    store_grad_unit<GRAD>(a, unit, lo, hi);
 }
 
 // Opaque to the optimiser: values derived from v before this point cannot be
@@ -404,7 +425,8 @@ __device__ __forceinline__ int64_t lane_unit(int64_t seg_u0, int k) { return seg
 // and a valid one takes the same operations), so all give bit-identical
 // states.
 template <bool BF16, bool UNROLL, bool FULL, bool TOPK, class Get>
-__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, float tau, Get get)
+__device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float c, float tau, Get get,
+                                            uint32_t* kept_units = nullptr)
 {
     constexpr int kUnroll = UNROLL ? kSegUnits : 1;
     float mt = -__builtin_inff(), ms = -__builtin_inff();
@@ -439,6 +461,7 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
         }
         const float tmax = max8(tv);
         if (TOPK && tmax == -__builtin_inff()) continue;
+        if (TOPK && kept_units) *kept_units |= 1u << k;   // unit k holds a kept entry
         // c > 0: the max of the scaled logits is the scaled max
         const float nmt = maxnan(mt, tmax * c);
         const float nms = maxnan(ms, max8(sv) * c);
@@ -465,9 +488,11 @@ __device__ __forceinline__ Stats lane_state(int64_t seg_u0, int64_t units, float
 
 // every lane's state over a segment held in registers
 template <bool BF16, bool FULL, bool TOPK, class Regs>
-__device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c, float tau)
+__device__ __forceinline__ Stats lane_state_regs(Regs& m, int64_t seg_u0, int64_t units, float c, float tau,
+                                                 uint32_t* kept_units)
 {
-    return lane_state<BF16, true, FULL, TOPK>(seg_u0, units, c, tau, [&](int k, Unit<BF16>& u) { u = m[k]; });
+    return lane_state<BF16, true, FULL, TOPK>(seg_u0, units, c, tau, [&](int k, Unit<BF16>& u) { u = m[k]; },
+                                              kept_units);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,9 +602,9 @@ __device__ __forceinline__ void seg_load(SegRegs<BF16_IN>& m, const KlArgs& a, i
 // pass 1: the segment's state, identical in every lane
 template <bool BF16_IN, bool FULL, bool TOPK>
 __device__ __forceinline__ Stats seg_pass1(SegRegs<BF16_IN>& m, int64_t seg_u0, int64_t units, float c, float tau,
-                                           Stats* part)
+                                           Stats* part, uint32_t* kept_units)
 {
-    const Stats lane_st = lane_state_regs<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau);
+    const Stats lane_st = lane_state_regs<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau, kept_units);
     const Stats st = group_merge<kSegThreads>(lane_st, part);
 #pragma unroll
     for (int k = 0; k < kSegUnits; ++k)
@@ -598,10 +623,101 @@ struct SegShared {
 
 // pass 2 over the units held in registers: the gradient, and in FORM_LOSS the
 // lane's share of the term-wise KL
+// Teacher-masked pass 2 on bf16 logits: most units of a top-k row hold no
+// kept entry (k = 4096 of 131072: about 22% of 8-entry units hold one), and
+// their gradient is all zeros.  A wave packs its units that hold a kept entry
+// into LDS (up to kCompactUnits), its lanes take the packed units in turn, so
+// the exponentials run for a few rounds of 64 units instead of all 8 per
+// lane, and each result goes back through LDS to the unit's own lane, which
+// stores its 8 units as the plain loop does (one coalesced 16-byte store per
+// unit and lane; scattered stores from the packed order fragment the
+// gradient's lines).  Each unit's arithmetic is unit_grad's, so the bits are
+// those of the plain loop.  A wave with more such units than fit takes the
+// plain loop.  Returns false then.
+constexpr int kCompactUnits = 192;   // per wave: three rounds of 64
+struct CompactUnits {
+    v4u t[kSegThreads / 64][kCompactUnits];   // teacher words, then the gradient's low words
+    v4u s[kSegThreads / 64][kCompactUnits];   // student words, then (binary32) its high words
+};
+
+// one buffer per kernel, whichever instances of the pass use it
+__device__ __forceinline__ CompactUnits& compact_units()
+{
+    __shared__ CompactUnits cu;
+    return cu;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int GRAD, bool FULL, int FORM>
+__device__ __forceinline__ bool seg_pass2_compact(SegRegs<true>& m, const KlArgs& a, int64_t row_unit0,
+                                                  int64_t seg_u0, int64_t units, float c, float tau, const RowConst& k,
+                                                  uint32_t kept_units)
+{
+    CompactUnits& cu = compact_units();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t n = (uint32_t)__builtin_popcount(kept_units);
+    uint32_t incl = n;   // inclusive prefix sum over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+    if (total > (uint32_t)kCompactUnits) return false;   // the same in every lane of the wave
+    const uint32_t first = incl - n;
+    uint32_t pos = first;
+#pragma unroll
+    for (int j = 0; j < kSegUnits; ++j) {
+        if ((kept_units >> j) & 1u) {   // only valid units are marked
+            cu.t[wave][pos] = m[j].t[0];
+            cu.s[wave][pos] = m[j].s[0];
+            ++pos;
+        }
+    }
+    wave_lds_sync();
+    LossAcc acc{0.0f, 0.0f, 0.0f};
+    for (uint32_t r = (uint32_t)lane; r < total; r += 64) {
+        Unit<true> u;
+        u.t[0] = cu.t[wave][r];
+        u.s[0] = cu.s[wave][r];
+        float tv[8], sv[8];
+        u.values(tv, sv);
+        v4u lo{0u, 0u, 0u, 0u}, hi{0u, 0u, 0u, 0u};
+        unit_grad_words<GRAD, true, FORM>(tv, sv, c, tau, k, acc, lo, hi);
+        cu.t[wave][r] = lo;   // each slot is read and rewritten by one lane only
+        if constexpr (GRAD == 2) cu.s[wave][r] = hi;
+    }
+    wave_lds_sync();
+    pos = first;
+#pragma unroll
+    for (int j = 0; j < kSegUnits; ++j) {
+        if (!FULL && lane_unit(seg_u0, j) >= units) continue;
+        v4u lo{0u, 0u, 0u, 0u}, hi{0u, 0u, 0u, 0u};
+        if ((kept_units >> j) & 1u) {
+            lo = cu.t[wave][pos];
+            if constexpr (GRAD == 2) hi = cu.s[wave][pos];
+            ++pos;
+        }
+        store_grad_unit<GRAD>(a, row_unit0 + lane_unit(seg_u0, j), lo, hi);
+    }
+    return true;
+}
+
 template <bool BF16_IN, int GRAD, bool FULL, bool TOPK, int FORM>
 __device__ __forceinline__ LossAcc seg_pass2(SegRegs<BF16_IN>& m, const KlArgs& a, int64_t row_unit0, int64_t seg_u0,
-                                             int64_t units, float c, float tau, const RowConst& k)
+                                             int64_t units, float c, float tau, const RowConst& k,
+                                             uint32_t kept_units)
 {
+    if constexpr (TOPK && BF16_IN && GRAD != 0 && FORM != FORM_LOSS) {
+        if (seg_pass2_compact<GRAD, FULL, FORM>(m, a, row_unit0, seg_u0, units, c, tau, k, kept_units))
+            return LossAcc{0.0f, 0.0f, 0.0f};
+    }
     LossAcc acc{0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < kSegUnits; ++j) {
@@ -618,7 +734,7 @@ __device__ __forceinline__ LossAcc seg_pass2(SegRegs<BF16_IN>& m, const KlArgs& 
 template <bool BF16_IN, int GRAD, bool FULL, bool TOPK>
 __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a, int W, int64_t row, int seg,
                                            const Stats& my_seg, float c, float tau, float gmul,
-                                           uint32_t* rec_base, SegShared& sh)
+                                           uint32_t* rec_base, SegShared& sh, uint32_t kept_units)
 {
     const int64_t units = a.vocab >> 3;
     const int64_t row_unit0 = row * units;
@@ -668,12 +784,15 @@ __device__ __forceinline__ void seg_finish(SegRegs<BF16_IN>& m, const KlArgs& a,
     if (k.form != FORM_LOSS) {
         if (seg == 0 && threadIdx.x == 0) a.row_loss[row] = k.loss;
         if constexpr (GRAD != 0) {
-            if (k.form == FORM_PLAIN) seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_PLAIN>(m, a, row_unit0, seg_u0, units, c, tau, k);
-            else seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_SELECT>(m, a, row_unit0, seg_u0, units, c, tau, k);
+            if (k.form == FORM_PLAIN)
+                seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_PLAIN>(m, a, row_unit0, seg_u0, units, c, tau, k, kept_units);
+            else
+                seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_SELECT>(m, a, row_unit0, seg_u0, units, c, tau, k, kept_units);
         }
         return;
     }
-    const LossAcc acc = seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_LOSS>(m, a, row_unit0, seg_u0, units, c, tau, k);
+    const LossAcc acc = seg_pass2<BF16_IN, GRAD, FULL, TOPK, FORM_LOSS>(m, a, row_unit0, seg_u0, units, c, tau, k,
+                                                                        kept_units);
     const LossSum part = group_sum<kSegThreads>(acc, sh.lpart);
     if (threadIdx.x == 0) {
         if (W == 1) {
@@ -705,7 +824,8 @@ __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, in
     const float tau = TOPK ? a.tau[row] : 0.0f;
     SegRegs<BF16_IN> m;
     seg_load<BF16_IN, FULL>(m, a, row * units, seg_u0, units);
-    const Stats st = seg_pass1<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau, sh.part);
+    uint32_t kept_units = 0u;   // TOPK: bit k set when the lane's unit k holds a kept entry
+    const Stats st = seg_pass1<BF16_IN, FULL, TOPK>(m, seg_u0, units, c, tau, sh.part, &kept_units);
     if (W > 1) publish(rec_of(rec_base, row, W), seg, st);
     // From here on (the row's statistics, pass 2, the gradient stores) the
     // waves run at a raised priority: a workgroup that has its segment's
@@ -714,7 +834,7 @@ __device__ __forceinline__ void seg_body(const KlArgs& a, int W, int64_t row, in
     // 131072 bf16: 1.123 -> 1.105 ms; raising pass 1 instead, or the loads,
     // measured slower or no better).
     __builtin_amdgcn_s_setprio(2);
-    seg_finish<BF16_IN, GRAD, FULL, TOPK>(m, a, W, row, seg, st, c, tau, gmul, rec_base, sh);
+    seg_finish<BF16_IN, GRAD, FULL, TOPK>(m, a, W, row, seg, st, c, tau, gmul, rec_base, sh, kept_units);
 }
 
 // One workgroup per segment: load, pass 1, publish, wait, pass 2.  Segments
