@@ -66,6 +66,13 @@ def run_and_check(dev, orc, t, s, k, T, g_dt, label, grad_scale=None):
     (4, 131072, 4096, 1.0, torch.bfloat16, torch.bfloat16),
     (3, 24584, 300, 1.0, torch.float32, torch.bfloat16),
     (2, (1 << 20) + 8, 4096, 1.0, torch.bfloat16, torch.bfloat16),  # past 64 record segments: one workgroup per row
+    # k / V ~ 5.5%: about 36% of 8-entry units hold a kept entry, ~184 of a
+    # wave's 512, so some waves pack theirs for pass 2 and some (over 192)
+    # take the plain loop, in the same workgroups; bf16 and fp32 gradients,
+    # and a ragged last segment
+    (6, 65536, 3600, 1.0, torch.bfloat16, torch.bfloat16),
+    (4, 65536, 3600, 1.0, torch.bfloat16, torch.float32),
+    (5, 40008, 2300, 0.7, torch.bfloat16, torch.bfloat16),
 ])
 def test_topk_small(dev, orc, tokens, vocab, k, T, in_dt, g_dt):
     t, s = synth.logits_bf16(tokens=tokens, vocab=vocab, seed=tokens * 11 + vocab + k)
