@@ -268,16 +268,15 @@ __device__ __forceinline__ uint32_t qdq_pair(uint32_t codes, float s)
 __device__ __forceinline__ void lds_store16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Effective scale fl(dec(c) s_g) of block scale code c (0 <= c < 128), or 0
-// for a block outside the operand (whose codes are then zeroed too).  The
-// E4M3 value is 2^(e-7) (1 + m/8), or m 2^-9 for e = 0; both forms are
-// computed and one selected by a mask, without a branch.
+// for a block outside the operand (whose codes are then zeroed too).
+// The E4M3 value by gfx950's FP8 conversion (exact on every non-NaN code,
+// checked on every code against the format's definition), one instruction where
+// the bit arithmetic took about eight; code 0x7F, outside the scale codes the
+// library writes or accepts, keeps the integer decode's 480 so that the
+// product always agrees with the quantizer's own dequantization.
 __device__ __forceinline__ float block_scale(uint32_t c, float s_g, bool ok)
 {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
-    const uint32_t sub = __builtin_bit_cast(uint32_t, (float)m * 0.001953125f);
-    const uint32_t sel = 0u - (uint32_t)(e != 0u);
-    const float dec = __builtin_bit_cast(float, (nrm & sel) | (sub & ~sel));
+    const float dec = c == 0x7Fu ? 480.0f : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false)[0];
     return ok ? dec * s_g : 0.0f;
 }
 
